@@ -1,0 +1,147 @@
+"""Plain fp64 CPU oracle for the Comba mixer. TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module. The library's device path never calls it.
+
+What is computed (Comba: Improving Bilinear RNNs with Closed-loop Control;
+PaperWeekly write-up, section "Comba架构：基于闭环控制理论"; arXiv abstract):
+the state transition is scalar-plus-low-rank, the feedback vector is the key,
+and the same key feedback corrects first the value and then the output. The
+write-up's printed recurrence was lost from the page text, so the oracle
+takes the plainest form consistent with those three facts:
+
+    S_t = S_{t-1} (alpha_t I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+        = alpha_t S_{t-1} + beta_t (v_t - S_{t-1} k_t) k_t^T
+    o_t = S_t (q_t - d k_t)
+
+S_t has one row per value channel (V x K). alpha_t, beta_t are scalars per
+(token, head) and d is one scalar per head. No query scale is applied.
+
+Tensor layouts (row-major): q, k [B, T, H, K]; v [B, T, H, V];
+alpha, beta [B, T, H]; d [H]; state [N, H, V, K]. With ``cu_seqlens``
+(int [N + 1], B == 1) sequence n owns tokens cu_seqlens[n] .. cu_seqlens[n+1]-1
+and starts from its own initial state; otherwise N == B.
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import numpy as np
+
+
+def _segments(B: int, T: int, cu_seqlens):
+    """Yield (n, b, t0, t1) for every sequence."""
+    if cu_seqlens is None:
+        for b in range(B):
+            yield b, b, 0, T
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        for n in range(len(cu) - 1):
+            yield n, 0, int(cu[n]), int(cu[n + 1])
+
+
+def comba_forward(q, k, v, alpha, beta, d, s0=None, cu_seqlens=None
+                  ) -> Tuple[np.ndarray, np.ndarray]:
+    """Token-by-token recurrence in fp64 (the definition above, rank-1 form).
+
+    Returns (o [B, T, H, V], final_state [N, H, V, K]), both float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    d = np.asarray(d, dtype=np.float64)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    s_final = np.zeros((N, H, V, K), dtype=np.float64)
+    for n, b, t0, t1 in _segments(B, T, cu_seqlens):
+        S = np.zeros((H, V, K)) if s0 is None else np.array(s0[n], dtype=np.float64)
+        for t in range(t0, t1):
+            kk = k[b, t]                                   # [H, K]
+            u = v[b, t] - np.einsum("hvk,hk->hv", S, kk)   # value corrected by key feedback
+            S = alpha[b, t][:, None, None] * S + beta[b, t][:, None, None] * u[:, :, None] * kk[:, None, :]
+            qt = q[b, t] - d[:, None] * kk                 # output corrected by the same feedback
+            o[b, t] = np.einsum("hvk,hk->hv", S, qt)
+        s_final[n] = S
+    return o, s_final
+
+
+def comba_forward_chunked(q, k, v, alpha, beta, d, s0=None, cu_seqlens=None,
+                          chunk: int = 64, return_intermediates: bool = False):
+    """Chunk-wise form in fp64: recurrent across chunks, parallel inside one.
+
+    The write-up (section "硬件高效的分块并行计算") evaluates Comba chunk by
+    chunk through intermediates W and U, with a single matrix inverse per
+    chunk. Written out for one chunk of n tokens with incoming state
+    h = S^T (K x V), g = log alpha, G the inclusive and Gx the exclusive
+    within-chunk cumulative sums of g:
+
+        A[s, r] = beta_s exp(Gx_s - G_r) (k_s . k_r)   for r < s, else 0
+        Tinv    = (I + A)^-1                           (unit lower triangular)
+        W       = Tinv diag(beta * exp(Gx)) K          U = Tinv diag(beta) V
+        Ubar    = U - W h                  (row s equals beta_s (v_s - S_{s-1} k_s))
+        O       = diag(exp(G)) (Q - dK) h + [((Q - dK) K^T) * M] Ubar,
+                  M[t, s] = exp(G_t - G_s) for s <= t, else 0
+        h'      = exp(G_n) h + K^T diag(exp(G_n - G)) Ubar
+
+    Equal to :func:`comba_forward` up to rounding. With
+    ``return_intermediates`` it also returns, per (sequence, head), a list of
+    dicts holding the per-chunk Tinv, W, U, Ubar and incoming h.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    d = np.asarray(d, dtype=np.float64)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    o = np.zeros((B, T, H, V), dtype=np.float64)
+    s_final = np.zeros((N, H, V, K), dtype=np.float64)
+    inter = {}
+    for n, b, t0, t1 in _segments(B, T, cu_seqlens):
+        for hh in range(H):
+            h = np.zeros((K, V)) if s0 is None else np.array(s0[n, hh], dtype=np.float64).T
+            recs = []
+            for c0 in range(t0, t1, chunk):
+                c1 = min(c0 + chunk, t1)
+                Q, Kc, Vc = q[b, c0:c1, hh], k[b, c0:c1, hh], v[b, c0:c1, hh]
+                bet = beta[b, c0:c1, hh]
+                g = np.log(alpha[b, c0:c1, hh])
+                G = np.cumsum(g)
+                Gx = G - g
+                nrow = c1 - c0
+                low = np.tril(np.ones((nrow, nrow), dtype=bool), -1)
+                A = np.where(low, bet[:, None] * np.exp(Gx[:, None] - G[None, :]) * (Kc @ Kc.T), 0.0)
+                Tinv = np.linalg.solve(np.eye(nrow) + A, np.eye(nrow))
+                W = Tinv @ ((bet * np.exp(Gx))[:, None] * Kc)
+                U = Tinv @ (bet[:, None] * Vc)
+                Ubar = U - W @ h
+                Qt = Q - d[hh] * Kc
+                M = np.where(np.tril(np.ones((nrow, nrow), dtype=bool)),
+                             np.exp(np.minimum(G[:, None] - G[None, :], 0.0)), 0.0)
+                o[b, c0:c1, hh] = np.exp(G)[:, None] * (Qt @ h) + ((Qt @ Kc.T) * M) @ Ubar
+                if return_intermediates:
+                    recs.append(dict(Tinv=Tinv, W=W, U=U, Ubar=Ubar, h=h.copy()))
+                h = np.exp(G[-1]) * h + Kc.T @ (np.exp(G[-1] - G)[:, None] * Ubar)
+            s_final[n, hh] = h.T
+            if return_intermediates:
+                inter[(n, hh)] = recs
+    if return_intermediates:
+        return o, s_final, inter
+    return o, s_final
+
+
+def rel_l2(x, ref) -> float:
+    """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((x - ref).ravel())
+    if not np.isfinite(num):
+        return float("inf")
+    return float(num / den) if den > 0 else float(num)

@@ -1,0 +1,333 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle.
+
+Each check is an independent route to the same number: a hand-derived
+example, an explicit-matrix brute force, an adjoint (backward) algorithm,
+closed forms of special cases, an autograd gradient step on the delta loss,
+and invariants (linearity, row slicing, packing, resumption, a norm bound).
+Every pin runs against both oracle implementations (numpy and C).
+"""
+import os
+
+import numpy as np
+import pytest
+import yaml
+
+import oracle
+from oracle import comba_forward, comba_forward_chunked, rel_l2
+from bilinear_rnn_amd.inputs import WORKLOADS, make_inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+IMPLS = ["numpy", "c"]
+
+
+def run(impl, q, k, v, alpha, beta, d, s0=None, cu=None):
+    if impl == "numpy":
+        return comba_forward(q, k, v, alpha, beta, d, s0, cu)
+    return oracle.comba_forward_c(q, k, v, alpha, beta, d, s0, cu, nthreads=4, rows_per_task=7)
+
+
+def small_case(seed, B=2, T=37, H=3, K=8, V=5, s0=True, alpha_lo=0.6):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, V))
+    alpha = rng.uniform(alpha_lo, 1.0, (B, T, H))
+    beta = rng.uniform(0.0, 1.0, (B, T, H))
+    d = rng.uniform(-1.0, 1.0, (H,))
+    S0 = rng.standard_normal((B, H, V, K)) * 0.3 if s0 else None
+    return q, k, v, alpha, beta, d, S0
+
+
+# --- hand-derived worked examples -------------------------------------------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+@pytest.mark.parametrize("case", ["scalar_two_steps", "matrix_two_steps"])
+def test_hand_derived_examples(impl, case):
+    with open(os.path.join(GOLDEN, "hand_derived.yaml")) as f:
+        g = yaml.safe_load(f)[case]
+    arr = {key: np.array(g[key], dtype=np.float64)
+           for key in ("q", "k", "v", "alpha", "beta", "d", "s0", "expect_o", "expect_state")}
+    o, sf = run(impl, arr["q"], arr["k"], arr["v"], arr["alpha"], arr["beta"], arr["d"], arr["s0"])
+    np.testing.assert_array_equal(o, arr["expect_o"])
+    np.testing.assert_array_equal(sf, arr["expect_state"])
+
+
+# --- explicit-matrix brute force ----------------------------------------------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_explicit_transition_matrices(impl):
+    """S_t = S_{t-1} A_t + beta_t v_t k_t^T with the K x K matrix
+    A_t = alpha_t I - beta_t k_t k_t^T formed explicitly (scalar-plus-low-rank)."""
+    q, k, v, alpha, beta, d, S0 = small_case(1, B=1, T=16, H=2, K=8, V=5)
+    o, sf = run(impl, q, k, v, alpha, beta, d, S0)
+    for h in range(2):
+        S = S0[0, h].copy()
+        for t in range(16):
+            kt = k[0, t, h][:, None]
+            A = alpha[0, t, h] * np.eye(8) - beta[0, t, h] * (kt @ kt.T)
+            S = S @ A + beta[0, t, h] * (v[0, t, h][:, None] @ kt.T)
+            ref = S @ (q[0, t, h] - d[h] * k[0, t, h])
+            np.testing.assert_allclose(o[0, t, h], ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(sf[0, h], S, rtol=1e-12, atol=1e-12)
+
+
+# --- adjoint brute force: an O(T^2 K) algorithm that never forms S_t ----------------
+
+def adjoint_outputs(q, k, v, alpha, beta, d, S0):
+    """o_t = S_0 y_0 + sum_{r<=t} beta_r (k_r . y_r) v_r, with y_t = q_t - d k_t and
+    y_{r-1} = A_r y_r, A_r = alpha_r I - beta_r k_r k_r^T (A_r is symmetric).
+    Unrolling S_t = S_0 A_1..A_t + sum_r beta_r v_r k_r^T A_{r+1}..A_t gives it."""
+    T, K = q.shape
+    V = v.shape[1]
+    o = np.zeros((T, V))
+    for t in range(T):
+        y = q[t] - d * k[t]
+        acc = np.zeros(V)
+        for r in range(t, -1, -1):
+            acc += beta[r] * (k[r] @ y) * v[r]
+            y = alpha[r] * y - beta[r] * k[r] * (k[r] @ y)
+        o[t] = acc + S0 @ y
+    # final state applied to the identity: columns of S_T
+    Y = np.eye(K)
+    acc = np.zeros((V, K))
+    for r in range(T - 1, -1, -1):
+        acc += beta[r] * np.outer(v[r], k[r] @ Y)
+        Y = alpha[r] * Y - beta[r] * np.outer(k[r], k[r] @ Y)
+    return o, acc + S0 @ Y
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_adjoint_brute_force_tiny_workload(impl):
+    w = WORKLOADS["tiny_fp32"]
+    inp = make_inputs(w, s0_std=0.02)
+    o, sf = run(impl, inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, inp.s0)
+    f = lambda x: np.asarray(x, dtype=np.float64)
+    for h in range(w.H):
+        oa, sa = adjoint_outputs(f(inp.q[0, :, h]), f(inp.k[0, :, h]), f(inp.v[0, :, h]),
+                                 f(inp.alpha[0, :, h]), f(inp.beta[0, :, h]), float(inp.d[h]),
+                                 f(inp.s0[0, h]))
+        assert rel_l2(o[0, :, h], oa) < 1e-13
+        assert rel_l2(sf[0, h], sa) < 1e-13
+
+
+# --- closed forms of special cases -----------------------------------------------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_beta_zero_closed_form(impl):
+    """beta == 0 freezes the write and erase paths: S_t = (prod alpha) S_0, and
+    o_t = (prod_{s<=t} alpha_s) S_0 (q_t - d k_t). With alpha == 1 and d == 0
+    this is the literal 'alpha=1, beta=0, d=0' reduction, o_t = S_0 q_t."""
+    q, k, v, alpha, beta, d, S0 = small_case(2)
+    beta[:] = 0.0
+    o, sf = run(impl, q, k, v, alpha, beta, d, S0)
+    P = np.cumprod(alpha, axis=1)                          # [B, T, H]
+    ref = np.einsum("bth,bhvk,bthk->bthv", P, S0, q - d[None, None, :, None] * k)
+    assert rel_l2(o, ref) < 1e-14
+    assert rel_l2(sf, P[:, -1][:, :, None, None] * S0) < 1e-14
+    alpha[:] = 1.0
+    o, _ = run(impl, q, k, v, alpha, beta, np.zeros_like(d), S0)
+    assert rel_l2(o, np.einsum("bhvk,bthk->bthv", S0, q)) < 1e-14
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_orthonormal_keys_closed_form(impl):
+    """Orthonormal keys and S_0 = 0 make the erase term vanish
+    (S_{t-1} k_t = 0), so O = [(M_g * Q K^T) diag(beta) - d diag(beta)] V with
+    M_g[t, s] = prod_{s < i <= t} alpha_i for s <= t. With alpha = beta = 1 and
+    d = 0 it is causal linear attention, O = tril(Q K^T) V (the
+    S_t = S_{t-1} + k_t v_t, O_t = q_t S_t form on the GLA/KDA page)."""
+    rng = np.random.default_rng(3)
+    T, K, V, H = 12, 16, 6, 2
+    Qm, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    k = np.stack([Qm[:T].copy(), Qm[rng.permutation(K)[:T]].copy()], axis=1)[None]   # [1,T,H,K]
+    q = rng.standard_normal((1, T, H, K))
+    v = rng.standard_normal((1, T, H, V))
+    alpha = rng.uniform(0.5, 1.0, (1, T, H))
+    beta = rng.uniform(0.1, 1.0, (1, T, H))
+    d = np.array([0.3, -0.7])
+    o, _ = run(impl, q, k, v, alpha, beta, d)
+    for h in range(H):
+        la = np.log(alpha[0, :, h])
+        G = np.cumsum(la)
+        Mg = np.tril(np.exp(G[:, None] - G[None, :]))
+        QK = q[0, :, h] @ k[0, :, h].T
+        ref = (Mg * QK) @ (beta[0, :, h][:, None] * v[0, :, h]) - d[h] * beta[0, :, h][:, None] * v[0, :, h]
+        assert rel_l2(o[0, :, h], ref) < 1e-13
+    ones = np.ones_like(alpha)
+    o, _ = run(impl, q, k, v, ones, ones, np.zeros(H))
+    for h in range(H):
+        ref = np.tril(q[0, :, h] @ k[0, :, h].T) @ v[0, :, h]
+        assert rel_l2(o[0, :, h], ref) < 1e-13
+
+
+# --- the erase term as one SGD step on the delta loss (autograd) -----------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_decay_then_sgd_step_on_delta_loss(impl):
+    """The delta rule is a gradient step on L(S) = 1/2 ||S k - v||^2
+    (write-up, section on the Delta learning rule). With the scalar decay kept
+    outside the low-rank term: S_t = alpha_t S_{t-1} - beta_t grad L(S_{t-1}).
+    The gradient comes from torch.autograd, not from the oracle's algebra."""
+    torch = pytest.importorskip("torch")
+    q, k, v, alpha, beta, d, S0 = small_case(4, B=1, T=20, H=2, K=6, V=4)
+    o, sf = run(impl, q, k, v, alpha, beta, d, S0)
+    for h in range(2):
+        S = torch.tensor(S0[0, h], dtype=torch.float64)
+        for t in range(20):
+            Sv = S.clone().requires_grad_(True)
+            kt = torch.tensor(k[0, t, h], dtype=torch.float64)
+            vt = torch.tensor(v[0, t, h], dtype=torch.float64)
+            loss = 0.5 * torch.sum((Sv @ kt - vt) ** 2)
+            (grad,) = torch.autograd.grad(loss, Sv)
+            S = float(alpha[0, t, h]) * S - float(beta[0, t, h]) * grad
+            ref = S @ torch.tensor(q[0, t, h] - d[h] * k[0, t, h], dtype=torch.float64)
+            np.testing.assert_allclose(o[0, t, h], ref.numpy(), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sf[0, h], S.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def gated_delta_loop(q, k, v, alpha, beta, d):
+    """Negative control: the IPLR transition alpha (I - beta k k^T) of
+    Gated-DeltaNet, where the decay also scales the erase term."""
+    T, K = q.shape
+    S = np.zeros((v.shape[1], K))
+    o = np.zeros((T, v.shape[1]))
+    for t in range(T):
+        S = alpha[t] * (S - beta[t] * np.outer(S @ k[t], k[t])) + beta[t] * np.outer(v[t], k[t])
+        o[t] = S @ (q[t] - d * k[t])
+    return o
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_gated_delta_equal_only_without_decay(impl):
+    """At d = 0 the scalar-plus-low-rank and the IPLR transitions coincide when
+    alpha == 1 (DeltaNet) and differ measurably when alpha < 1 (the write-up
+    contrasts Comba's SPLR with Gated-DeltaNet's IPLR)."""
+    q, k, v, alpha, beta, d, _ = small_case(5, B=1, T=40, H=1, K=8, V=4, s0=False, alpha_lo=0.7)
+    z = np.zeros(1)
+    o1, _ = run(impl, q, k, v, np.ones_like(alpha), beta, z)
+    ref1 = gated_delta_loop(q[0, :, 0], k[0, :, 0], v[0, :, 0], np.ones(40), beta[0, :, 0], 0.0)
+    assert rel_l2(o1[0, :, 0], ref1) < 1e-13
+    o2, _ = run(impl, q, k, v, alpha, beta, z)
+    ref2 = gated_delta_loop(q[0, :, 0], k[0, :, 0], v[0, :, 0], alpha[0, :, 0], beta[0, :, 0], 0.0)
+    assert rel_l2(o2[0, :, 0], ref2) > 1e-3
+
+
+# --- invariants ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_state_norm_bound(impl):
+    """||S_t||_F <= rho_t ||S_{t-1}||_F + beta_t ||v_t|| ||k_t||, where
+    rho_t = max(alpha_t, |alpha_t - beta_t ||k_t||^2|) is the spectral norm of
+    the symmetric transition alpha_t I - beta_t k_t k_t^T. Checked per step by
+    resuming the oracle one token at a time."""
+    q, k, v, alpha, beta, d, S0 = small_case(6, B=1, T=30, H=2, K=8, V=5)
+    k = k * np.random.default_rng(7).uniform(0.5, 1.6, k.shape[:-1])[..., None]
+    beta = beta * 1.5
+    S = S0
+    for t in range(30):
+        sl = slice(t, t + 1)
+        _, S_new = run(impl, q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], d, S)
+        for h in range(2):
+            kn = np.linalg.norm(k[0, t, h])
+            rho = max(alpha[0, t, h], abs(alpha[0, t, h] - beta[0, t, h] * kn * kn))
+            bound = rho * np.linalg.norm(S[0, h]) + beta[0, t, h] * np.linalg.norm(v[0, t, h]) * kn
+            assert np.linalg.norm(S_new[0, h]) <= bound * (1 + 1e-12)
+        S = S_new
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_linear_in_state_and_values(impl):
+    q, k, v, alpha, beta, d, S0 = small_case(8)
+    rng = np.random.default_rng(9)
+    v2 = rng.standard_normal(v.shape)
+    S2 = rng.standard_normal(S0.shape)
+    o1, f1 = run(impl, q, k, v, alpha, beta, d, S0)
+    o2, f2 = run(impl, q, k, v2, alpha, beta, d, S2)
+    o3, f3 = run(impl, q, k, 2 * v - v2, alpha, beta, d, 2 * S0 - S2)
+    assert rel_l2(o3, 2 * o1 - o2) < 1e-13
+    assert rel_l2(f3, 2 * f1 - f2) < 1e-13
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_value_rows_are_independent(impl):
+    q, k, v, alpha, beta, d, S0 = small_case(10, V=7)
+    o, f = run(impl, q, k, v, alpha, beta, d, S0)
+    rows = [1, 4, 6]
+    os_, fs = run(impl, q, k, v[..., rows], alpha, beta, d, S0[:, :, rows])
+    np.testing.assert_allclose(os_, o[..., rows], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(fs, f[:, :, rows], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_packed_sequences_equal_separate_runs(impl):
+    q, k, v, alpha, beta, d, _ = small_case(11, B=1, T=50, s0=False)
+    lengths = [13, 0, 1, 36]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    S0 = np.random.default_rng(12).standard_normal((4, 3, 5, 8))
+    o, f = run(impl, q, k, v, alpha, beta, d, S0, cu)
+    for n in range(4):
+        sl = slice(cu[n], cu[n + 1])
+        if cu[n + 1] == cu[n]:
+            np.testing.assert_array_equal(f[n], S0[n])
+            continue
+        on, fn = run(impl, q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], d, S0[n:n + 1])
+        np.testing.assert_allclose(o[:, sl], on, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(f[n], fn[0], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_split_and_resume(impl):
+    q, k, v, alpha, beta, d, S0 = small_case(13, T=45)
+    o, f = run(impl, q, k, v, alpha, beta, d, S0)
+    a, b = slice(0, 19), slice(19, 45)
+    oa, fa = run(impl, q[:, a], k[:, a], v[:, a], alpha[:, a], beta[:, a], d, S0)
+    ob, fb = run(impl, q[:, b], k[:, b], v[:, b], alpha[:, b], beta[:, b], d, fa)
+    np.testing.assert_allclose(np.concatenate([oa, ob], axis=1), o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(fb, f, rtol=1e-12, atol=1e-13)
+
+
+# --- chunk-wise form --------------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 64])
+def test_chunked_form_equals_recurrence(chunk):
+    """The chunk-wise form (one unit-lower-triangular inverse per chunk,
+    intermediates W and U) reproduces the token recurrence, including partial
+    last chunks, a non-zero initial state, d != 0 and packed sequences."""
+    q, k, v, alpha, beta, d, S0 = small_case(14, B=2, T=150, H=2, K=16, V=12)
+    o, f = comba_forward(q, k, v, alpha, beta, d, S0)
+    oc, fc = comba_forward_chunked(q, k, v, alpha, beta, d, S0, chunk=chunk)
+    assert rel_l2(oc, o) < 1e-13
+    assert rel_l2(fc, f) < 1e-13
+    cu = np.array([0, 70, 71, 150], dtype=np.int32)
+    S0v = np.random.default_rng(15).standard_normal((3, 2, 12, 16)) * 0.1
+    o, f = comba_forward(q[:1], k[:1], v[:1], alpha[:1], beta[:1], d, S0v, cu)
+    oc, fc = comba_forward_chunked(q[:1], k[:1], v[:1], alpha[:1], beta[:1], d, S0v, cu, chunk=chunk)
+    assert rel_l2(oc, o) < 1e-13
+    assert rel_l2(fc, f) < 1e-13
+
+
+def test_chunk_intermediates_meaning():
+    """Row s of Ubar equals beta_s (v_s - S_{s-1} k_s), the value corrected by
+    the state feedback, with S_{s-1} taken from the token recurrence."""
+    q, k, v, alpha, beta, d, S0 = small_case(16, B=1, T=64, H=1, K=8, V=5)
+    _, _, inter = comba_forward_chunked(q, k, v, alpha, beta, d, S0, chunk=32,
+                                        return_intermediates=True)
+    S = S0[0, 0].copy()
+    ubar = []
+    for t in range(64):
+        kt = k[0, t, 0]
+        u = v[0, t, 0] - S @ kt
+        ubar.append(beta[0, t, 0] * u)
+        S = alpha[0, t, 0] * S + beta[0, t, 0] * np.outer(u, kt)
+    got = np.concatenate([r["Ubar"] for r in inter[(0, 0)]], axis=0)
+    assert rel_l2(got, np.array(ubar)) < 1e-13
+
+
+def test_c_and_numpy_oracles_agree_on_varlen_workload():
+    w = WORKLOADS["varlen"]
+    inp = make_inputs(w, num_seqs=5, H=2, lengths=np.array([16, 70, 1, 130, 64]))
+    o1, f1 = comba_forward(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, None, inp.cu_seqlens)
+    o2, f2 = oracle.comba_forward_c(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, None,
+                                    inp.cu_seqlens)
+    assert rel_l2(o2, o1) < 1e-14 and rel_l2(f2, f1) < 1e-14
