@@ -1,0 +1,11 @@
+"""Comba mixer hot path for AMD Instinct MI355X (gfx950).
+
+The chunk-wise parallel forward and the recurrent (decode) step of Comba,
+a bilinear RNN with a scalar-plus-low-rank state transition and output
+correction, as hand-written HIP kernels behind a C ABI (include/comba.h).
+This package is the thin Python binding over that library.
+"""
+from .api import (CombaError, chunk_fwd, lib, library_path, recurrent_step,  # noqa: F401
+                  varlen_order, workspace_size)
+
+__all__ = ["chunk_fwd", "recurrent_step", "varlen_order", "workspace_size", "CombaError"]

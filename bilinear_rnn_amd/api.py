@@ -1,0 +1,204 @@
+"""Thin ctypes binding of libcomba.so (the C ABI in include/comba.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+layout, outputs and the workspace are allocated with torch, and the call is
+enqueued on torch's current stream. Every step of the computation runs in
+the HIP kernels of libcomba.so; there is no fallback path. If the library is
+missing, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcomba.so")
+_lib = None
+
+COMBA_OK = 0
+COMBA_ERR_INVALID_ARG = -1
+COMBA_ERR_UNSUPPORTED = -2
+COMBA_ERR_WORKSPACE = -3
+COMBA_ERR_HIP = -4
+COMBA_BF16 = 0
+COMBA_FP32 = 1
+
+EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
+            "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_recurrent_step",
+            "comba_varlen_order")
+
+
+class CombaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcomba.so (built in-tree by ``python -m bilinear_rnn_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m bilinear_rnn_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+        i32, sz = ctypes.c_int32, ctypes.c_size_t
+        L.comba_abi_version.argtypes = []
+        L.comba_abi_version.restype = i32
+        L.comba_status_string.argtypes = [i32]
+        L.comba_status_string.restype = ctypes.c_char_p
+        L.comba_last_error.argtypes = []
+        L.comba_last_error.restype = ctypes.c_char_p
+        L.comba_chunk_fwd_workspace_size.argtypes = [i32] * 7
+        L.comba_chunk_fwd_workspace_size.restype = sz
+        L.comba_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
+                                      i32, i32, vp, fp, vp, sz, vp]
+        L.comba_chunk_fwd.restype = i32
+        L.comba_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
+                                           i32, i32, vp, fp, vp]
+        L.comba_recurrent_step.restype = i32
+        L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
+        L.comba_varlen_order.restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().comba_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().comba_last_error().decode()
+
+
+def _check(status: int):
+    if status != COMBA_OK:
+        raise CombaError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+_DT = {torch.bfloat16: COMBA_BF16, torch.float32: COMBA_FP32}
+
+
+def _require(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype):
+    if q.dtype not in _DT:
+        raise ValueError(f"q must be bfloat16 or float32 (got {q.dtype})")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [B, T, H, K] and v [B, T, H, V]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    _require(q, "q", q.dtype)
+    _require(k, "k", q.dtype, (B, T, H, K))
+    _require(v, "v", q.dtype, (B, T, H, V))
+    _require(alpha, "alpha", torch.float32, (B, T, H))
+    _require(beta, "beta", torch.float32, (B, T, H))
+    _require(d, "d", torch.float32, (H,))
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = B
+    if initial_state is not None:
+        _require(initial_state, "initial_state", torch.float32, (N, H, V, K))
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DT:
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    return B, T, H, K, V, N, out_dtype
+
+
+def workspace_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0,
+                   dtype: torch.dtype = torch.bfloat16) -> int:
+    return int(lib().comba_chunk_fwd_workspace_size(B, T, H, K, V, num_seqs, _DT[dtype]))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+              beta: torch.Tensor, d: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+              output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunk-wise forward through ``comba_chunk_fwd``. Returns (o, final_state)."""
+    B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    L = lib()
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
+    _require(out, "out", out_dtype, (B, T, H, V))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _require(final_state, "final_state", torch.float32, (N, H, V, K))
+    nws = int(L.comba_chunk_fwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0, _DT[q.dtype]))
+    if nws > 0 and (workspace is None or workspace.numel() < nws):
+        workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(L.comba_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d),
+                                 _ptr(initial_state), _ptr(cu_seqlens), N if cu_seqlens is not None else 0,
+                                 B, T, H, K, V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state),
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                 ctypes.c_void_p(stream)))
+    return out, final_state
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                   beta: torch.Tensor, d: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                   in_place: bool = False, output_final_state: bool = True,
+                   out: Optional[torch.Tensor] = None,
+                   final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Token-by-token recurrence through ``comba_recurrent_step`` (T == 1: decode).
+
+    With ``in_place`` the state is updated in ``initial_state`` itself."""
+    B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    L = lib()
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
+    _require(out, "out", out_dtype, (B, T, H, V))
+    if in_place:
+        if initial_state is None:
+            raise ValueError("in_place requires initial_state")
+        final_state = initial_state
+    elif final_state is None and output_final_state:
+        final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _require(final_state, "final_state", torch.float32, (N, H, V, K))
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(L.comba_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d),
+                                      _ptr(initial_state), _ptr(cu_seqlens),
+                                      N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
+                                      _DT[out_dtype], _ptr(out), _ptr(final_state), ctypes.c_void_p(stream)))
+    return out, final_state
+
+
+def varlen_order(cu_seqlens: torch.Tensor) -> torch.Tensor:
+    """Longest-first order of packed sequences through ``comba_varlen_order``."""
+    _require(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    order = torch.empty((N,), dtype=torch.int32, device=cu_seqlens.device)
+    with torch.cuda.device(cu_seqlens.device):
+        stream = torch.cuda.current_stream(cu_seqlens.device).cuda_stream
+        _check(lib().comba_varlen_order(_ptr(cu_seqlens), N, _ptr(order), ctypes.c_void_p(stream)))
+    return order

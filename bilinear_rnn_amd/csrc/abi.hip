@@ -1,0 +1,138 @@
+// C ABI entry points (declared in include/comba.h): host-side validation,
+// workspace carving and kernel launches on the caller's stream.
+#include <climits>
+#include <cstdio>
+#include <string>
+
+#include "comba.h"
+#include "launch.h"
+
+#define COMBA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Above this many packed sequences the longest-first order (quadratic in N)
+// is skipped and sequences run in their given order.
+constexpr int kMaxOrderedSeqs = 16384;
+
+int32_t fail(int32_t code, const char* what) {
+  g_last_error = what;
+  return code;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+bool supported_dim(int32_t x) { return x == 64 || x == 128; }
+
+// Common argument checks; fills a with everything but the workspace.
+int32_t check_args(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                   const float* d, const float* s0, const int32_t* cu, int32_t num_seqs, int32_t B,
+                   int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
+                   void* o, float* sf, comba::FwdArgs& a) {
+  if (!q || !k || !v || !alpha || !beta || !d || !o)
+    return fail(COMBA_ERR_INVALID_ARG, "q, k, v, alpha, beta, d and o must be non-NULL");
+  if ((in_dtype != COMBA_BF16 && in_dtype != COMBA_FP32) || (out_dtype != COMBA_BF16 && out_dtype != COMBA_FP32))
+    return fail(COMBA_ERR_INVALID_ARG, "in_dtype and out_dtype must be COMBA_BF16 or COMBA_FP32");
+  if (B < 1 || H < 1 || K < 1 || V < 1)
+    return fail(COMBA_ERR_INVALID_ARG, "B, H, K and V must be >= 1");
+  if (cu) {
+    if (B != 1) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens requires B == 1");
+    if (num_seqs < 1) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens requires num_seqs >= 1");
+    if (T < 0) return fail(COMBA_ERR_INVALID_ARG, "T must be >= 0");
+  } else if (T < 1) {
+    return fail(COMBA_ERR_INVALID_ARG, "T must be >= 1 without cu_seqlens");
+  }
+  if (!supported_dim(K) || !supported_dim(V))
+    return fail(COMBA_ERR_UNSUPPORTED, "only K, V in {64, 128} are implemented");
+  const int64_t N = cu ? num_seqs : B;
+  if (N * H * 2 > INT_MAX / 16)
+    return fail(COMBA_ERR_UNSUPPORTED, "too many (sequence, head) pairs for one launch");
+  if (s0 && sf && s0 != sf) {
+    const char* s0b = reinterpret_cast<const char*>(s0);
+    const char* sfb = reinterpret_cast<const char*>(sf);
+    const int64_t bytes = N * H * V * K * 4;
+    if (s0b < sfb + bytes && sfb < s0b + bytes)
+      return fail(COMBA_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
+  }
+  a = comba::FwdArgs{q, k, v, alpha, beta, d, s0, cu, nullptr, static_cast<int>(N), B, T, H, K, V,
+                     in_dtype, out_dtype, o, sf};
+  return COMBA_OK;
+}
+
+int32_t launched(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_error = std::string("HIP launch failed: ") + hipGetErrorString(e);
+    return COMBA_ERR_HIP;
+  }
+  g_last_error.clear();
+  return COMBA_OK;
+}
+
+}  // namespace
+
+COMBA_API int32_t comba_abi_version(void) { return COMBA_ABI_VERSION; }
+
+COMBA_API const char* comba_status_string(int32_t status) {
+  switch (status) {
+    case COMBA_OK: return "COMBA_OK";
+    case COMBA_ERR_INVALID_ARG: return "COMBA_ERR_INVALID_ARG";
+    case COMBA_ERR_UNSUPPORTED: return "COMBA_ERR_UNSUPPORTED";
+    case COMBA_ERR_WORKSPACE: return "COMBA_ERR_WORKSPACE";
+    case COMBA_ERR_HIP: return "COMBA_ERR_HIP";
+    default: return "COMBA_ERR_UNKNOWN";
+  }
+}
+
+COMBA_API const char* comba_last_error(void) { return g_last_error.c_str(); }
+
+COMBA_API size_t comba_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                                int32_t num_seqs, int32_t in_dtype) {
+  (void)B; (void)T; (void)H; (void)K; (void)V; (void)in_dtype;
+  if (num_seqs > 0 && num_seqs <= kMaxOrderedSeqs) return align_up(sizeof(int32_t) * num_seqs);
+  return 0;
+}
+
+COMBA_API int32_t comba_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* d, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                  int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
+                                  void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  comba::FwdArgs a;
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
+                          in_dtype, out_dtype, o, final_state, a);
+  if (rc != COMBA_OK) return rc;
+  const size_t need = comba_chunk_fwd_workspace_size(B, T, H, K, V, cu_seqlens ? num_seqs : 0, in_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(COMBA_ERR_WORKSPACE, "workspace is NULL or smaller than comba_chunk_fwd_workspace_size()");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cu_seqlens && need > 0) {
+    int32_t* order = static_cast<int32_t*>(workspace);
+    rc = launched(comba::launch_varlen_order(cu_seqlens, a.N, order, st));
+    if (rc != COMBA_OK) return rc;
+    a.order = order;
+  }
+  if (in_dtype == COMBA_BF16) return launched(comba::launch_chunk_bf16(a, st));
+  return launched(comba::launch_chunk_fp32(a, st));
+}
+
+COMBA_API int32_t comba_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
+                                       const float* beta, const float* d, const float* initial_state,
+                                       const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                       int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                                       int32_t out_dtype, void* o, float* final_state, void* stream) {
+  comba::FwdArgs a;
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
+                          in_dtype, out_dtype, o, final_state, a);
+  if (rc != COMBA_OK) return rc;
+  return launched(comba::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+}
+
+COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,
+                                     void* stream) {
+  if (!cu_seqlens || !order) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens and order must be non-NULL");
+  if (num_seqs < 1) return fail(COMBA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+  return launched(comba::launch_varlen_order(cu_seqlens, num_seqs, order, static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,34 @@
+// Kernel launchers behind the C ABI. Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace comba {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* d;
+  const float* s0;            // may be null
+  const int32_t* cu_seqlens;  // may be null
+  const int32_t* order;       // longest-first sequence order, may be null
+  int N, B, T, H, K, V;
+  int in_dtype, out_dtype;    // COMBA_BF16 / COMBA_FP32
+  void* o;
+  float* sf;                  // may be null
+};
+
+hipError_t launch_recurrent(const FwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_fp32(const FwdArgs& a, hipStream_t st);
+hipError_t launch_varlen_order(const int32_t* cu_seqlens, int N, int32_t* order, hipStream_t st);
+
+// Grid for work units of NVT tiles each, dealt round-robin over the 8 XCDs so
+// that the tiles of one unit run on the same XCD (and share its L2).
+inline int xcd_grid(int units, int nvt) { return ((units + 7) / 8) * 8 * nvt; }
+
+}  // namespace comba

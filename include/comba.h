@@ -1,0 +1,149 @@
+/*
+ * comba.h — C ABI of the Comba mixer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The mixer (Comba: Improving Bilinear RNNs with Closed-loop Control; arXiv
+ * abstract, and the PaperWeekly write-up, section "Comba架构：基于闭环控制理论")
+ * is a bilinear RNN with a scalar-plus-low-rank state transition in which the
+ * key is the feedback vector that corrects first the value and then the
+ * output. Per head, with S_t a V x K state (one row per value channel):
+ *
+ *     S_t = S_{t-1} (alpha_t I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t (q_t - d k_t)
+ *
+ * The write-up's printed equation was lost from the page text; this is the
+ * plainest form consistent with the three facts above. No 1/sqrt(K) query
+ * scale is applied; callers L2-normalise q and k themselves if they want to.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a DEVICE pointer owned by the caller. Tensors are
+ *   row-major and contiguous:
+ *       q, k           [B, T, H, K]   in_dtype
+ *       v              [B, T, H, V]   in_dtype
+ *       alpha, beta    [B, T, H]      float32, alpha in (0, 1] (log alpha is used)
+ *       d              [H]            float32, output-correction factor per head
+ *       initial_state  [N, H, V, K]   float32, or NULL for zeros
+ *       o              [B, T, H, V]   out_dtype
+ *       final_state    [N, H, V, K]   float32, or NULL (not written)
+ *   The state keeps the value channel as its row index and K contiguous.
+ * - cu_seqlens (int32 [N + 1], device memory) packs N variable-length
+ *   sequences along T of a single batch row: sequence n owns tokens
+ *   cu_seqlens[n] .. cu_seqlens[n+1]-1 and starts from initial_state[n].
+ *   It requires B == 1, cu_seqlens[0] == 0, cu_seqlens[N] == T and
+ *   non-decreasing values. Without it, N == B and every batch row is one
+ *   sequence. A sequence of length 0 returns its initial state. Violating the
+ *   device-side preconditions (monotone cu_seqlens, alpha > 0) gives
+ *   unspecified values but no out-of-bounds access.
+ * - Supported shapes: K, V in {64, 128}; B, H >= 1; T >= 1 (T >= 0 with
+ *   cu_seqlens). dtypes: COMBA_BF16 or COMBA_FP32 for q/k/v and for o.
+ * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream). The
+ *   call returns without synchronising and never allocates device memory.
+ * - Errors detectable on the host (NULL required pointer, bad shape or dtype,
+ *   short workspace) are returned before anything is enqueued. A failed
+ *   launch returns COMBA_ERR_HIP. comba_last_error() then holds a
+ *   human-readable message for the calling thread.
+ * - Entry points keep no state between calls and are thread-safe.
+ */
+#ifndef COMBA_H_
+#define COMBA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define COMBA_ABI_VERSION 1
+
+/* Status codes returned by every entry point. */
+enum {
+  COMBA_OK = 0,
+  COMBA_ERR_INVALID_ARG = -1,  /* NULL required pointer, bad size or dtype code */
+  COMBA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (e.g. K = 96)      */
+  COMBA_ERR_WORKSPACE = -3,    /* workspace NULL or smaller than required       */
+  COMBA_ERR_HIP = -4           /* the HIP runtime reported a launch error       */
+};
+
+/* Element types of q, k, v (in_dtype) and o (out_dtype). */
+enum { COMBA_BF16 = 0, COMBA_FP32 = 1 };
+
+/* Version of this ABI (COMBA_ABI_VERSION of the built library). */
+int32_t comba_abi_version(void);
+
+/* Static text for a status code. Never NULL. */
+const char* comba_status_string(int32_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* comba_last_error(void);
+
+/*
+ * Bytes of device workspace comba_chunk_fwd needs for these sizes (0 when
+ * none; a NULL workspace is then accepted). num_seqs is N when cu_seqlens is
+ * used and 0 otherwise. Returns 0 for invalid sizes as well.
+ */
+size_t comba_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                      int32_t num_seqs, int32_t in_dtype);
+
+/*
+ * Chunk-wise parallel forward (write-up, section "硬件高效的分块并行计算":
+ * recurrent across chunks, parallel matrix products inside a chunk, and one
+ * matrix inverse per chunk for the intermediates W and U).
+ *
+ * Computes o for every token and, if final_state is not NULL, S after the
+ * last token of every sequence. Chunks of 64 tokens restart at every
+ * sequence start; the result does not depend on the chunk size beyond
+ * rounding. Floating point work accumulates in float32; bf16 inputs feed the
+ * matrix cores exactly and every non-input operand is carried as a pair of
+ * bf16 values (high and low part), so the result matches an fp64 evaluation
+ * of the recurrence to the rounding of o itself. fp32 inputs use float32
+ * arithmetic throughout.
+ *
+ * workspace: device memory of at least comba_chunk_fwd_workspace_size(...)
+ * bytes, used only during this call on `stream`. final_state must not
+ * overlap initial_state or any input.
+ */
+int32_t comba_chunk_fwd(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const float* d,
+                        const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                        int32_t in_dtype, int32_t out_dtype,
+                        void* o, float* final_state,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Recurrent form (write-up, section "硬件高效的分块并行计算": the token-by-
+ * token recurrence), one token after another from the initial state. With
+ * T == 1 this is the single-token decode step of generation. Per value row i:
+ *     a = S[i,:] . k,   b = S[i,:] . (q - d k),   u = v_i - a
+ *     S'[i,:] = alpha S[i,:] + beta u k^T,        o_i = alpha b + beta u (k . (q - d k))
+ * which is the recurrence above expanded for one step.
+ *
+ * final_state may be the same pointer as initial_state (in-place update of a
+ * state resident in device memory); any other overlap is not allowed.
+ */
+int32_t comba_recurrent_step(const void* q, const void* k, const void* v,
+                             const float* alpha, const float* beta, const float* d,
+                             const float* initial_state,
+                             const int32_t* cu_seqlens, int32_t num_seqs,
+                             int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                             int32_t in_dtype, int32_t out_dtype,
+                             void* o, float* final_state, void* stream);
+
+/*
+ * Longest-first order of packed sequences (integer work, exact): writes into
+ * order[0..N-1] the sequence indices sorted by decreasing length
+ * cu_seqlens[n+1] - cu_seqlens[n], ties by increasing index. comba_chunk_fwd
+ * runs this itself for packed batches so that the longest sequences start
+ * first; it is exported for callers that schedule their own work and for
+ * testing. cu_seqlens and order are device pointers; N >= 1.
+ */
+int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COMBA_H_ */

@@ -1,0 +1,100 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/comba.h declares, and rejects bad arguments with the
+documented status codes before enqueuing anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bilinear_rnn_amd as comba
+from bilinear_rnn_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "comba.h")
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: every call below fails validation first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(comba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    declared = header_functions()
+    assert declared == sorted(api.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", comba.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (comba_\w+)", out))
+    assert set(declared) <= exported
+    L = comba.lib()
+    for name in declared:
+        assert hasattr(L, name)
+
+
+def test_version_and_status_strings():
+    L = comba.lib()
+    assert L.comba_abi_version() == 1
+    assert api.status_string(0) == "COMBA_OK"
+    assert api.status_string(-1) == "COMBA_ERR_INVALID_ARG"
+    assert api.status_string(-2) == "COMBA_ERR_UNSUPPORTED"
+    assert api.status_string(-3) == "COMBA_ERR_WORKSPACE"
+    assert api.status_string(-4) == "COMBA_ERR_HIP"
+    assert api.status_string(7) == "COMBA_ERR_UNKNOWN"
+
+
+def chunk(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=16, H=2, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None, ws=None, wsb=0)
+    args.update(kw)
+    L = comba.lib()
+    return L.comba_chunk_fwd(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"],
+                             args["s0"], args["cu"], args["n"], args["B"], args["T"], args["H"], args["K"],
+                             args["V"], args["idt"], args["odt"], args["o"], args["sf"], args["ws"],
+                             args["wsb"], None)
+
+
+def step(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=1, H=2, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None)
+    args.update(kw)
+    L = comba.lib()
+    return L.comba_recurrent_step(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"],
+                                  args["s0"], args["cu"], args["n"], args["B"], args["T"], args["H"],
+                                  args["K"], args["V"], args["idt"], args["odt"], args["o"], args["sf"],
+                                  None)
+
+
+@pytest.mark.parametrize("fn", [chunk, step])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
+    (dict(beta=None), -1), (dict(d=None), -1), (dict(o=None), -1),
+    (dict(B=0), -1), (dict(H=0), -1), (dict(T=0), -1), (dict(K=0), -1), (dict(V=-3), -1),
+    (dict(idt=2), -1), (dict(odt=-1), -1),
+    (dict(K=96), -2), (dict(V=32), -2), (dict(K=256), -2),
+    (dict(cu=FAKE, n=3, B=2), -1), (dict(cu=FAKE, n=0), -1), (dict(cu=FAKE, n=2, T=-1), -1),
+    (dict(s0=ctypes.c_void_p(4096), sf=ctypes.c_void_p(4096 + 64)), -1),
+])
+def test_invalid_arguments_are_rejected_before_launch(fn, kw, code):
+    assert fn(**kw) == code
+    assert api.last_error() != ""
+
+
+def test_workspace_rules():
+    assert comba.workspace_size(1, 100, 4, 64, 64, 0) == 0
+    ws = comba.workspace_size(1, 100, 4, 64, 64, 10)
+    assert ws >= 40 and ws % 256 == 0
+    # packed batch with no workspace
+    assert chunk(cu=FAKE, n=10, T=100) == -3
+    assert chunk(cu=FAKE, n=10, T=100, ws=FAKE, wsb=ws - 1) == -3
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    a = torch.ones(1, 4, 2)
+    with pytest.raises(ValueError):
+        comba.chunk_fwd(x, x, x, a, a, torch.zeros(2))
