@@ -6,21 +6,25 @@
 // state-dependent chain of chunk c:
 //
 //   consumers (waves 0-3, 16 value channels each), chunk c:
-//     X = [Q; K] h  ->  R = diag(beta) V - diag(beta e^Gx) K h  ->  Ubar = Tinv R
-//     ->  O = diag(e^G)(Q h - d K h) + P Ubar,   h' = e^Gn h + K^T diag(e^(Gn-G)) Ubar
+//     X = [Q; K] h,  R = diag(beta) V - diag(beta e^Gx) K h,
+//     Ubar = (I + A)^-1 R by 32-token blocks:
+//         Ubar_top = T1 R_top,  Ubar_bot = T2 (R_bot - A21 Ubar_top),
+//     O = diag(e^G)(Q h - d K h) + P Ubar,   h' = e^Gn h + K^T diag(e^(Gn-G)) Ubar
 //     The fp32 state slice h[:, 16 channels] never leaves a consumer's registers.
-//   producers (waves 4-7, one 16-row block each), chunk c+1:
-//     stage q/k/v/alpha/beta in LDS, decays, Q K^T and K K^T, A and P, and the
-//     unit-lower-triangular inverse Tinv = (I + A)^-1: diagonal 16x16 blocks by
-//     forward substitution (vector ALU), off-diagonal blocks by column block,
-//     T_ij = -T_ii sum_m A_im T_mj, on the matrix cores.
+//   producers (waves 4-7, one 16-token row block p each), chunk c+1:
+//     stage q/k/v/alpha/beta in LDS, decays, Q K^T and K K^T of row block p,
+//     A (strictly lower) and P (masked scores), and the two 32x32 diagonal
+//     inverses T1 = (I + A11)^-1, T2 = (I + A22)^-1: each 16x16 diagonal
+//     block by fp32 forward substitution, the off-diagonal 16x16 block as
+//     T_{p,p-1} = -T_pp A_{p,p-1} T_{p-1,p-1} by the odd producer, which
+//     inverts block p-1 again itself so the producers never wait on each other
+//     after staging.
 //
-// Double-buffered LDS holds everything a consumer reads for one chunk. One
-// workgroup barrier per chunk hands a buffer from producers to consumers;
-// the producers synchronise among themselves through an LDS counter.
+// Double-buffered LDS holds everything a consumer reads for one chunk; one
+// workgroup barrier per chunk hands a buffer from producers to consumers.
 //
-// Precision: q, k, v are exact bf16 operands. Every other operand (h, Tinv,
-// P, R, Ubar, A) is split into a high and a low bf16 part; products
+// Precision: q, k, v are exact bf16 operands. Every other operand (h, T1, T2,
+// A21, P, R, Ubar) is split into a high and a low bf16 part; the products
 // hi*hi + hi*lo + lo*hi (or hi + lo against an exact operand) accumulate in
 // fp32, about 16 significant bits per operand. The output correction is
 // applied by linearity (Q h - d K h, Q K^T - d K K^T), never by rounding
@@ -29,10 +33,10 @@
 // Operand layout: a 16x16x32 MFMA takes 8 reduction elements per lane. An
 // fp32 accumulator block holds rows 4*(lane/16)+i, so two accumulator blocks
 // supply exactly the 8 reduction indices a lane needs when the other operand
-// stores its reduction axis in perm32 order. Q and K tiles are stored that
-// way (16-byte chunks XOR-swizzled by row against bank conflicts); K^T
-// operands for the state update come from the same K tile through the
-// transposing LDS read (ds_read_b64_tr_b16), so no transposed copy is kept.
+// stores its reduction axis in perm32 order. Q, K, T and P are stored that way
+// (16-byte chunks XOR-swizzled by row against bank conflicts). K^T operands
+// for the state update and V for R come from row-major tiles through the
+// transposing LDS read (ds_read_b64_tr_b16).
 #include "chunk_common.h"
 #include "launch.h"
 #include "comba.h"
@@ -43,45 +47,54 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 typedef short s8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
-constexpr int kTP = 32 * 32 + 32 * 64;  // packed lower 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
+constexpr int kTP = 32 * 32 + 32 * 64;  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
 
-// Offset of (row, stored position) in a row-major tile of L bf16 per row whose
-// 16-byte chunks are XOR-swizzled by the row index.
 template <int L>
 __device__ __forceinline__ int swz(int row, int pos) {
   constexpr int mask = (L / 8 - 1) < 7 ? (L / 8 - 1) : 7;
   return row * L + (((pos >> 3) ^ (row & mask)) << 3) + (pos & 7);
 }
-// Packed lower-triangular 64x64 (Tinv, P): the upper blocks (0,1) and (2,3)
-// are stored (as zeros) because the 32-wide reduction steps read them.
 __device__ __forceinline__ int tp_off(int row, int pos) {
-  return row < 32 ? swz<32>(row, pos) : 1024 + swz<64>(row - 32, pos);
+  // rows 0-31: 32 per row, chunks swizzled by row & 3; rows 32-63: 64 per row
+  // after the first 1024, swizzled by row & 7 (arithmetic, no branch)
+  const int big = row >> 5;
+  const int base = row * (32 << big) - 1024 * big;
+  const int mask = 3 | (big << 2);
+  return base + (((pos >> 3) ^ (row & mask)) << 3) + (pos & 7);
 }
-__device__ __forceinline__ int bidx(int i, int m) { return i * (i + 1) / 2 + m; }
+// Position of row t of a chunk in the lane-ordered gate arrays: lane group g
+// of a consumer reads its 16 rows t = 16 r4 + 4 g + i as four float4.
+__device__ __forceinline__ int gate_pos(int t) { return ((t >> 2) & 3) * 16 + (t >> 4) * 4 + (t & 3); }
 
+// 16-byte aligned so that buf[1] keeps every b128 / b64 LDS access aligned.
 template <int K, int VT>
-struct ChunkBuf {
-  u16 Q[64 * K];   // Q rows, reduction axis in perm32 order
-  u16 Kc[64 * K];  // K rows, same order
-  u16 Vv[64 * VT]; // V tile rows, natural order
+struct alignas(16) ChunkBuf {
+  u16 Q[64 * K];    // Q rows, reduction axis in perm32 order
+  u16 Kc[64 * K];   // K rows, same order
+  u16 Vv[64 * VT];  // V tile rows, natural order
+  // Th/Tl: rows 0-31 hold T1; rows 32-63 hold -A21 (columns 0-31) and T2
+  // (columns 32-63). Ph/Pl: the masked score matrix P. hi / lo bf16 parts.
   u16 Th[kTP], Tl[kTP], Ph[kTP], Pl[kTP];
-  float beta[64], bEGx[64], EG[64], EGnG[64];
+  float gl[4][64];  // beta, beta e^Gx, e^G, e^(Gn-G) in gate_pos order
   float raw_a[64], raw_b[64];
+  float eGn;
 };
 
-struct ProdScratch {
-  float Am[10 * 256];  // lower 16x16 blocks of A, fp32, row-major
-  float Tm[10 * 256];  // lower 16x16 blocks of Tinv, fp32, row-major
+struct alignas(16) ProdScratch {  // one per producer wave, fp32 16x16 blocks, row-major
+  float Aown[256];                // A_pp
+  float Aoff[256];                // A_{p,p-1} (odd p)
+  float Town[256];                // T_pp
 };
 
 template <int K, int VT>
-struct SmemV2 {
+struct alignas(16) SmemV3 {
   ChunkBuf<K, VT> buf[2];
-  ProdScratch ps;
+  ProdScratch ps[4];
   int prod_bar;
 };
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ f32x4 lds_f4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
 __device__ __forceinline__ void split_pair(const f32x4& m0, const f32x4& m1, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -117,6 +130,60 @@ __device__ __forceinline__ void put_split(u16* hi, u16* lo, int off, float x) {
   lo[off] = __builtin_bit_cast(u16, b);
 }
 
+// 4x4 transpose inside each lane quad (lanes 4m..4m+3): lane 4m+x holds v[i]
+// = M[i][x] on entry and M[x][i] on exit. Two butterfly stages (partner lane
+// x^1, then x^2), each moving two values with DPP quad permutations; the
+// selects are plain two-way choices on the lane bit.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
+}
+__device__ __forceinline__ f32x4 quad_transpose(const f32x4& v, int x) {
+  const bool b0 = (x & 1) != 0, b1 = (x & 2) != 0;
+  // stage 1: 2x2 transposes between lanes x and x^1
+  const float s0 = b0 ? v[0] : v[1], s1 = b0 ? v[2] : v[3];
+  const float r0 = dpp_xor1(s0), r1 = dpp_xor1(s1);
+  f32x4 w;
+  w[0] = b0 ? r0 : v[0];
+  w[1] = b0 ? v[1] : r0;
+  w[2] = b0 ? r1 : v[2];
+  w[3] = b0 ? v[3] : r1;
+  // stage 2: swap 2-element halves between lanes x and x^2
+  const float t0 = b1 ? w[0] : w[2], t1 = b1 ? w[1] : w[3];
+  const float u0 = dpp_xor2(t0), u1 = dpp_xor2(t1);
+  f32x4 z;
+  z[0] = b1 ? u0 : w[0];
+  z[1] = b1 ? u1 : w[1];
+  z[2] = b1 ? w[2] : u0;
+  z[3] = b1 ? w[3] : u1;
+  return z;
+}
+
+// Split four fp32 values into hi / lo bf16 and write them as two 8-byte stores.
+__device__ __forceinline__ void put_split4(u16* hi, u16* lo, int off, const f32x4& x) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    __bf16 a, b;
+    split_bf16(x[j], a, b);
+    h[j] = a;
+    l[j] = b;
+  }
+  *reinterpret_cast<bf16x4*>(hi + off) = h;
+  *reinterpret_cast<bf16x4*>(lo + off) = l;
+}
+
+// hi + lo * (a*b + c) style triple product accumulate with both operands split.
+__device__ __forceinline__ f32x4 mma3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl,
+                                      f32x4 acc) {
+  acc = mfma16x16x32(ah, bh, acc);
+  acc = mfma16x16x32(ah, bl, acc);
+  acc = mfma16x16x32(al, bh, acc);
+  return acc;
+}
+
 // Producer-only barrier (4 wavefronts) through a monotonically increasing LDS counter.
 __device__ __forceinline__ void producer_sync(int* bar, int& epoch, int lane) {
   epoch += 4;
@@ -125,8 +192,26 @@ __device__ __forceinline__ void producer_sync(int* bar, int& epoch, int lane) {
     __builtin_amdgcn_s_sleep(1);
 }
 
-// A operand of K^T (rows = key channels 16kb..16kb+15, reduction = tokens
-// 32s2 + {4g..4g+3, 16+4g..16+4g+3}) read from the row-major K tile.
+// x += (x moved by the DPP control CTRL); lanes without a source add 0.
+#define COMBA_DPP_ADD(x, CTRL, ROWMASK, BOUND)                                                        \
+  (x) += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), CTRL, \
+                                                               ROWMASK, 0xf, BOUND))
+
+// Wavefront inclusive prefix sum: shifts by 1, 2, 4, 8 inside each row of 16
+// lanes, then the last lane of row 0 / 2 into rows 1 / 3, then lane 31 into
+// rows 2 and 3.
+__device__ __forceinline__ float wave_scan_dpp(float x) {
+  COMBA_DPP_ADD(x, 0x111, 0xf, true);  // row_shr:1
+  COMBA_DPP_ADD(x, 0x112, 0xf, true);  // row_shr:2
+  COMBA_DPP_ADD(x, 0x114, 0xf, true);  // row_shr:4
+  COMBA_DPP_ADD(x, 0x118, 0xf, true);  // row_shr:8
+  COMBA_DPP_ADD(x, 0x142, 0xa, false); // row_bcast:15 into rows 1, 3
+  COMBA_DPP_ADD(x, 0x143, 0xc, false); // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// K^T operand (rows = key channels 16kb..16kb+15, reduction = tokens
+// 32s2 + {4g..4g+3, 16+4g..16+4g+3}) from the row-major K tile.
 template <int K>
 __device__ __forceinline__ bf16x8 kt_frag(const u16* Kc, int kb, int s2, int g, int l16) {
   const int pos = perm_col(16 * kb + 4 * (l16 & 3));
@@ -139,14 +224,66 @@ __device__ __forceinline__ bf16x8 kt_frag(const u16* Kc, int kb, int s2, int g, 
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// ---- producer pieces --------------------------------------------------------------------
+// V[16 r4 + 4g + j][col0 + l16], j = 0..3, from the row-major V tile.
+template <int VT>
+__device__ __forceinline__ f32x4 v_frag(const u16* Vv, int r4, int col0, int g, int l16) {
+  const int row = 16 * r4 + 4 * g + (l16 >> 2);
+  const s4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(Vv + swz<VT>(row, col0 + 4 * (l16 & 3))));
+  const uint2 w = __builtin_bit_cast(uint2, x);  // whole-vector reinterpretation (see kt_frag)
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
+}
 
-// Q K^T and K K^T for row block P, then A (fp32, scratch), P (hi/lo, buffer)
-// and the diagonal block of Tinv.
+// ---- producer pieces ---------------------------------------------------------------------
+
+// (I + A)^-1 of a 16x16 block whose strictly lower part is in Ab (fp32,
+// row-major, zeros on and above the diagonal): forward substitution by
+// columns, four lanes per column (lane = 4c + q holds rows 4q..4q+3 of
+// column c), the pivot broadcast inside each lane quad with DPP.
+__device__ __forceinline__ void invert16(const float* Ab, float* Tb, int lane) {
+  const int c = lane >> 2, q = lane & 3;
+  float x[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == c) ? 1.f : 0.f;
+#pragma unroll
+  for (int j4 = 0; j4 < 4; ++j4) {
+    f32x4 a[4];  // rows 4q..4q+3, columns 4 j4 .. 4 j4 + 3
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = lds_f4(Ab + (4 * q + r) * 16 + 4 * j4);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int j = 4 * j4 + jj;
+      if (j == 15) break;
+      // x[j] of this column lives in lane quad member j/4 (= j4), register j%4 (= jj)
+      const int src = __builtin_bit_cast(int, x[jj]);
+      int bc;
+      switch (j4) {
+        case 0: bc = __builtin_amdgcn_update_dpp(0, src, 0x00, 0xf, 0xf, false); break;
+        case 1: bc = __builtin_amdgcn_update_dpp(0, src, 0x55, 0xf, 0xf, false); break;
+        case 2: bc = __builtin_amdgcn_update_dpp(0, src, 0xaa, 0xf, 0xf, false); break;
+        default: bc = __builtin_amdgcn_update_dpp(0, src, 0xff, 0xf, 0xf, false); break;
+      }
+      const float xj = __builtin_bit_cast(float, bc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] -= a[r][jj] * xj;  // a[r][jj] = 0 unless 4q + r > j
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) Tb[(4 * q + r) * 16 + c] = x[r];
+}
+
+// Write a fp32 16x16 row-major block into the buffer's Th/Tl at (row0, col0):
+// lane = 4r + cg writes row r, columns 4cg..4cg+3 (contiguous in perm32 order).
+template <int K, int VT>
+__device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* Tb, int row0, int col0, int lane) {
+  const int r = lane >> 2, cg = lane & 3;
+  put_split4(bf.Th, bf.Tl, tp_off(row0 + r, perm_col(col0 + 4 * cg)), lds_f4(Tb + r * 16 + 4 * cg));
+}
+
 template <int P, int K, int VT>
 __device__ __forceinline__ void producer_rows(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
                                               float G, float rinv, float be) {
-  const int g = lane >> 4, l16 = lane & 15;
+  const int g = lane >> 4, l16 = lane & 15, m4 = l16 >> 2, x4 = l16 & 3;
   f32x4 aqk[P + 1], akk[P + 1];
 #pragma unroll
   for (int bs = 0; bs <= P; ++bs) {
@@ -172,75 +309,65 @@ __device__ __forceinline__ void producer_rows(ChunkBuf<K, VT>& bf, ProdScratch& 
     bt[i] = __shfl(be, t, kWave);
     rt[i] = __shfl(rinv, t, kWave);
   }
+  // Scaled blocks leave the accumulator layout (4 rows x 1 column per lane)
+  // through a quad transpose (1 row x 4 columns per lane): every store below
+  // is then one 8- or 16-byte LDS write.
+  const int trow = 16 * P + 4 * g + x4;  // row held after the transpose
 #pragma unroll
   for (int bs = 0; bs <= P; ++bs) {
     const int s_ = 16 * bs + l16;
     const float Gs = __shfl(G, s_, kWave);
+    f32x4 av, pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * P + 4 * g + i;
-      const float M = __expf(fminf(Gt[i] - Gs, 0.f));  // exp(G_t - G_s), s <= t
+      const float M = __expf(fminf(Gt[i] - Gs, 0.f));  // exp(G_t - G_s) for s <= t
       const float kk = akk[bs][i];
-      ps.Am[bidx(P, bs) * 256 + (4 * g + i) * 16 + l16] = (s_ < t) ? bt[i] * (M * rt[i]) * kk : 0.f;
-      const float pv = (s_ <= t) ? (aqk[bs][i] - dh * kk) * M : 0.f;
-      put_split(bf.Ph, bf.Pl, tp_off(t, perm_col(s_)), pv);
+      av[i] = (s_ < t) ? bt[i] * (M * rt[i]) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+      pv[i] = (s_ <= t) ? (aqk[bs][i] - dh * kk) * M : 0.f;
+    }
+    const f32x4 pT = quad_transpose(pv, x4);
+    const f32x4 aT = quad_transpose(av, x4);
+    const int col = perm_col(16 * bs + 4 * m4);
+    put_split4(bf.Ph, bf.Pl, tp_off(trow, col), pT);
+    if (bs == P) *reinterpret_cast<f32x4*>(&ps.Aown[(4 * g + x4) * 16 + 4 * m4]) = aT;
+    if constexpr ((P & 1) != 0) {
+      if (bs == P - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[(4 * g + x4) * 16 + 4 * m4]) = aT;
+    }
+    if constexpr (P >= 2) {
+      if (bs < 2) put_split4(bf.Th, bf.Tl, tp_off(trow, col), -aT);  // -A21
     }
   }
-  // Diagonal block: column substitution, one lane per column.
-  if (g == 0) {
-    const float* Ab = &ps.Am[bidx(P, P) * 256];
-    const int c = l16;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
-#pragma unroll
-    for (int j = 0; j < 15; ++j) {
-#pragma unroll
-      for (int r = j + 1; r < 16; ++r) x[r] -= Ab[r * 16 + j] * x[j];
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ps.Tm[bidx(P, P) * 256 + r * 16 + c] = x[r];
-      put_split(bf.Th, bf.Tl, tp_off(16 * P + r, perm_col(16 * P + c)), x[r]);
-    }
-  }
+  // diagonal inverse of this row block (reads this wave's own scratch writes)
+  invert16(ps.Aown, ps.Town, lane);
+  store_t_block(bf, ps.Town, 16 * P, 16 * P, lane);
 }
 
-// Off-diagonal blocks of block column P: T_iP = -T_ii sum_{m=P}^{i-1} A_im T_mP.
+// T_{P,P-1} = -T_PP A_{P,P-1} T_{P-1,P-1} for odd P, after the even producer's
+// diagonal inverse is visible.
 template <int P, int K, int VT>
-__device__ __forceinline__ void producer_offdiag(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane) {
+__device__ __forceinline__ void producer_offdiag(ChunkBuf<K, VT>& bf, const ProdScratch& ps,
+                                                 const ProdScratch& prev, int lane) {
   const int g = lane >> 4, l16 = lane & 15;
+  s4 ah, al, bh, bl;
+  split4(lds_f4(&ps.Aoff[l16 * 16 + 4 * g]), ah, al);
+  f32x4 tv;
 #pragma unroll
-  for (int i = P + 1; i < 4; ++i) {
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = P; m < i; ++m) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(&ps.Am[bidx(i, m) * 256 + l16 * 16 + 4 * g]);
-      f32x4 bv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = ps.Tm[bidx(m, P) * 256 + (4 * g + j) * 16 + l16];
-      s4 ah, al, bh, bl;
-      split4(av, ah, al);
-      split4(bv, bh, bl);
-      y = mfma16x16x16(ah, bh, y);
-      y = mfma16x16x16(ah, bl, y);
-      y = mfma16x16x16(al, bh, y);
-    }
-    const f32x4 tv = *reinterpret_cast<const f32x4*>(&ps.Tm[bidx(i, i) * 256 + l16 * 16 + 4 * g]);
-    s4 th, tl, yh, yl;
-    split4(tv, th, tl);
-    split4(y, yh, yl);
-    f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    z = mfma16x16x16(th, yh, z);
-    z = mfma16x16x16(th, yl, z);
-    z = mfma16x16x16(tl, yh, z);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float val = -z[r];
-      ps.Tm[bidx(i, P) * 256 + (4 * g + r) * 16 + l16] = val;
-      put_split(bf.Th, bf.Tl, tp_off(16 * i + 4 * g + r, perm_col(16 * P + l16)), val);
-    }
-  }
+  for (int j = 0; j < 4; ++j) tv[j] = prev.Town[(4 * g + j) * 16 + l16];
+  split4(tv, bh, bl);
+  f32x4 y = {0.f, 0.f, 0.f, 0.f};
+  y = mfma16x16x16(ah, bh, y);
+  y = mfma16x16x16(ah, bl, y);
+  y = mfma16x16x16(al, bh, y);
+  s4 th, tl, yh, yl;
+  split4(lds_f4(&ps.Town[l16 * 16 + 4 * g]), th, tl);
+  split4(y, yh, yl);
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  z = mfma16x16x16(th, yh, z);
+  z = mfma16x16x16(th, yl, z);
+  z = mfma16x16x16(tl, yh, z);
+  const f32x4 zT = quad_transpose(-z, l16 & 3);
+  put_split4(bf.Th, bf.Tl, tp_off(16 * P + 4 * g + (l16 & 3), perm_col(16 * (P - 1) + 4 * (l16 >> 2))), zT);
 }
 
 // ---- kernel -------------------------------------------------------------------------------
@@ -254,7 +381,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     float* __restrict__ sf) {
   static_assert(VT == 64, "four consumer wavefronts of 16 channels");
   constexpr int NVT = V / VT;
-  __shared__ SmemV2<K, VT> sm;
+  __shared__ SmemV3<K, VT> sm;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform role
@@ -269,8 +396,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   const float dh = d[h];
   const int nchunks = (t1 - t0 + 63) / 64;
 
-  // Zero both buffers' Tinv / P storage once: the upper blocks (0,1), (2,3)
-  // are read by the 32-wide reduction steps and never written.
+  // Zero both buffers' T / P storage once: the upper blocks (0,1), (2,3) are
+  // read by the 32-wide reduction steps and never written.
   for (int e = tid; e < kTP; e += 512) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -284,7 +411,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   __syncthreads();
 
   if (wave >= 4) {
-    // ======================= producers: prepare chunk i in iteration i =======================
+    // ======================= producers: prepare chunk it in iteration it =======================
     const int p = wave - 4;
     const int ptid = tid - 256;
     constexpr int KP = K / 8, QPT = 64 * KP / 256, VPR = VT / 8, VPT = 64 * VPR / 256;
@@ -330,6 +457,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     for (int it = 0; it <= nchunks; ++it) {
       if (it < nchunks) {
         ChunkBuf<K, VT>& bf = sm.buf[it & 1];
+        // Opaque per-iteration copy of the lane index: keeps the compiler from
+        // hoisting every lane-dependent LDS address of the four row-block
+        // variants out of the loop (which exhausts the registers and spills).
+        int olane;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
 #pragma unroll
         for (int j = 0; j < QPT; ++j) {
           const int piece = ptid + j * 256, row = piece / KP, c8 = piece % KP;
@@ -348,39 +480,39 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           bf.raw_a[ptid] = ra;
           bf.raw_b[ptid] = rb;
         }
-        if (it + 1 < nchunks) fetch(t0 + (it + 1) * 64);
         producer_sync(&sm.prod_bar, epoch, lane);
 
         // decays: every producer wave computes all 64 rows (lane = row)
         const float a = bf.raw_a[lane], be = bf.raw_b[lane];
         const float lg = __logf(a);
-        const float G = wave_inclusive_scan(lg, lane);
-        const float Gn = __shfl(G, 63, kWave);
+        const float G = wave_scan_dpp(lg);
         const float rinv = 1.f / a;
         if (p == 0) {
-          bf.beta[lane] = be;
-          bf.bEGx[lane] = be * __expf(G - lg);
-          bf.EG[lane] = __expf(G);
-          bf.EGnG[lane] = __expf(Gn - G);
+          const float Gn = __shfl(G, 63, kWave);
+          const int gp = gate_pos(lane);
+          bf.gl[0][gp] = be;
+          bf.gl[1][gp] = be * __expf(G - lg);
+          bf.gl[2][gp] = __expf(G);
+          bf.gl[3][gp] = __expf(Gn - G);
+          if (lane == 63) bf.eGn = __expf(G);
         }
         switch (p) {
-          case 0: producer_rows<0>(bf, sm.ps, lane, dh, G, rinv, be); break;
-          case 1: producer_rows<1>(bf, sm.ps, lane, dh, G, rinv, be); break;
-          case 2: producer_rows<2>(bf, sm.ps, lane, dh, G, rinv, be); break;
-          default: producer_rows<3>(bf, sm.ps, lane, dh, G, rinv, be); break;
+          case 0: producer_rows<0>(bf, sm.ps[0], olane, dh, G, rinv, be); break;
+          case 1: producer_rows<1>(bf, sm.ps[1], olane, dh, G, rinv, be); break;
+          case 2: producer_rows<2>(bf, sm.ps[2], olane, dh, G, rinv, be); break;
+          default: producer_rows<3>(bf, sm.ps[3], olane, dh, G, rinv, be); break;
         }
-        producer_sync(&sm.prod_bar, epoch, lane);
-        switch (p) {
-          case 0: producer_offdiag<0>(bf, sm.ps, lane); break;
-          case 1: producer_offdiag<1>(bf, sm.ps, lane); break;
-          case 2: producer_offdiag<2>(bf, sm.ps, lane); break;
-          default: break;
-        }
+        producer_sync(&sm.prod_bar, epoch, lane);  // diagonal inverses visible
+        if (p == 1) producer_offdiag<1>(bf, sm.ps[1], sm.ps[0], olane);
+        if (p == 3) producer_offdiag<3>(bf, sm.ps[3], sm.ps[2], olane);
+        // Prefetch the next chunk only now: every wait on a vector-memory counter
+        // inside the work above would otherwise also wait for these loads.
+        if (it + 1 < nchunks) fetch(t0 + (it + 1) * 64);
       }
       __syncthreads();
     }
   } else {
-    // ======================= consumers: run chunk i-1 in iteration i =======================
+    // ======================= consumers: run chunk it-1 in iteration it =======================
     const int vloc = wave * 16 + l16;
     const int vcol = vt * VT + vloc;
     f32x4 hs[K / 16];
@@ -400,88 +532,113 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 #pragma unroll
         for (int s = 0; s < K / 32; ++s) split_pair(hs[2 * s], hs[2 * s + 1], hbh[s], hbl[s]);
 
-        // X = [Q; K] h
-        f32x4 QH[4], KH[4];
+        // K h (needed first), then R
+        f32x4 KH[4];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          QH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
           KH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < K / 32; ++s) {
-            const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * r4 + l16, 32 * s + 8 * g)]);
             const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * r4 + l16, 32 * s + 8 * g)]);
-            QH[r4] = mfma16x16x32(aq, hbh[s], QH[r4]);
-            QH[r4] = mfma16x16x32(aq, hbl[s], QH[r4]);
             KH[r4] = mfma16x16x32(ak, hbh[s], KH[r4]);
             KH[r4] = mfma16x16x32(ak, hbl[s], KH[r4]);
           }
         }
-
-        // R = beta V - beta e^Gx K h
         f32x4 R[4];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 bt = lds_f4(&bf.gl[0][16 * g + 4 * r4]);
+          const f32x4 bx = lds_f4(&bf.gl[1][16 * g + 4 * r4]);
+          const f32x4 vv = v_frag<VT>(bf.Vv, r4, wave * 16, g, l16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * r4 + 4 * g + i;
-            R[r4][i] = bf.beta[t] * bf16_bits_to_float(bf.Vv[swz<VT>(t, vloc)]) - bf.bEGx[t] * KH[r4][i];
-          }
+          for (int i = 0; i < 4; ++i) R[r4][i] = bt[i] * vv[i] - bx[i] * KH[r4][i];
+        }
 
-        // Ubar = Tinv R (row block r4 needs reduction steps 0..r4/2)
-        bf16x8 rbh[2], rbl[2];
-        split_pair(R[0], R[1], rbh[0], rbl[0]);
-        split_pair(R[2], R[3], rbh[1], rbl[1]);
-        f32x4 U[4];
+        // Q h (independent of the solve below)
+        f32x4 QH[4];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          U[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
+          QH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s <= (r4 >> 1); ++s) {
-            const int off = tp_off(16 * r4 + l16, 32 * s + 8 * g);
-            const bf16x8 th = lds8(&bf.Th[off]);
-            const bf16x8 tl = lds8(&bf.Tl[off]);
-            U[r4] = mfma16x16x32(th, rbh[s], U[r4]);
-            U[r4] = mfma16x16x32(th, rbl[s], U[r4]);
-            U[r4] = mfma16x16x32(tl, rbh[s], U[r4]);
+          for (int s = 0; s < K / 32; ++s) {
+            const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * r4 + l16, 32 * s + 8 * g)]);
+            QH[r4] = mfma16x16x32(aq, hbh[s], QH[r4]);
+            QH[r4] = mfma16x16x32(aq, hbl[s], QH[r4]);
           }
         }
 
-        // O = e^G (Q h - d K h) + P Ubar, stored straight from the accumulators
-        bf16x8 ubh[2], ubl[2];
-        split_pair(U[0], U[1], ubh[0], ubl[0]);
-        split_pair(U[2], U[3], ubh[1], ubl[1]);
+        // Ubar_top = T1 R_top
+        bf16x8 rbh, rbl;
+        split_pair(R[0], R[1], rbh, rbl);
+        f32x4 U[4];
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          const int off = tp_off(16 * r4 + l16, 8 * g);
+          U[r4] = mma3(lds8(&bf.Th[off]), lds8(&bf.Tl[off]), rbh, rbl, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        bf16x8 ubh0, ubl0;
+        split_pair(U[0], U[1], ubh0, ubl0);
+        // Y = R_bot - A21 Ubar_top ; Ubar_bot = T2 Y
+        f32x4 Y[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int off = tp_off(32 + 16 * r + l16, 8 * g);
+          Y[r] = mma3(lds8(&bf.Th[off]), lds8(&bf.Tl[off]), ubh0, ubl0, R[2 + r]);
+        }
+        bf16x8 ybh, ybl;
+        split_pair(Y[0], Y[1], ybh, ybl);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int off = tp_off(32 + 16 * r + l16, 32 + 8 * g);
+          U[2 + r] = mma3(lds8(&bf.Th[off]), lds8(&bf.Tl[off]), ybh, ybl, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+        bf16x8 ubh1, ubl1;
+        split_pair(U[2], U[3], ubh1, ubl1);
+
+        // O = e^G (Q h - d K h) + P Ubar
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 eg = lds_f4(&bf.gl[2][16 * g + 4 * r4]);
           f32x4 acc;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = bf.EG[16 * r4 + 4 * g + i] * (QH[r4][i] - dh * KH[r4][i]);
-#pragma unroll
-          for (int s = 0; s <= (r4 >> 1); ++s) {
-            const int off = tp_off(16 * r4 + l16, 32 * s + 8 * g);
-            const bf16x8 ph = lds8(&bf.Ph[off]);
-            const bf16x8 pl = lds8(&bf.Pl[off]);
-            acc = mfma16x16x32(ph, ubh[s], acc);
-            acc = mfma16x16x32(ph, ubl[s], acc);
-            acc = mfma16x16x32(pl, ubh[s], acc);
+          for (int i = 0; i < 4; ++i) acc[i] = eg[i] * (QH[r4][i] - dh * KH[r4][i]);
+          const int off0 = tp_off(16 * r4 + l16, 8 * g);
+          acc = mma3(lds8(&bf.Ph[off0]), lds8(&bf.Pl[off0]), ubh0, ubl0, acc);
+          if (r4 >= 2) {
+            const int off1 = tp_off(16 * r4 + l16, 32 + 8 * g);
+            acc = mma3(lds8(&bf.Ph[off1]), lds8(&bf.Pl[off1]), ubh1, ubl1, acc);
           }
+          // quad transpose: this lane then holds row 16 r4 + 4 g + (l16 & 3),
+          // channels 4 (l16 >> 2) .. +3 of its wavefront's 16 -> one store
+          const f32x4 oT = quad_transpose(acc, l16 & 3);
+          const int t = 16 * r4 + 4 * g + (l16 & 3);
+          if (t < nrows) {
+            const int64_t off = ((static_cast<int64_t>(b) * T + c0 + t) * H + h) * V + vt * VT + wave * 16 + 4 * (l16 >> 2);
+            if constexpr (sizeof(OutT) == 2) {
+              bf16x4 ob;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * r4 + 4 * g + i;
-            if (t < nrows)
-              Elem<OutT>::store(o, ((static_cast<int64_t>(b) * T + c0 + t) * H + h) * V + vcol, acc[i]);
+              for (int j = 0; j < 4; ++j) ob[j] = to_bf16(oT[j]);
+              *reinterpret_cast<bf16x4*>(o + off) = ob;
+            } else {
+              *reinterpret_cast<f32x4*>(o + off) = oT;
+            }
           }
         }
 
         // h' = e^Gn h + K^T diag(e^(Gn - G)) Ubar
-        f32x4 Us[4];
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Us[r4][i] = U[r4][i] * bf.EGnG[16 * r4 + 4 * g + i];
         bf16x8 ush[2], usl[2];
-        split_pair(Us[0], Us[1], ush[0], usl[0]);
-        split_pair(Us[2], Us[3], ush[1], usl[1]);
-        const float eGn = bf.EG[63];
+        {
+          f32x4 Us[4];
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 en = lds_f4(&bf.gl[3][16 * g + 4 * r4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Us[r4][i] = U[r4][i] * en[i];
+          }
+          split_pair(Us[0], Us[1], ush[0], usl[0]);
+          split_pair(Us[2], Us[3], ush[1], usl[1]);
+        }
+        const float eGn = bf.eGn;
 #pragma unroll
         for (int kb = 0; kb < K / 16; ++kb) {
           hs[kb] *= eGn;
