@@ -9,6 +9,12 @@ run and reported in GB/s under "decode". The fp64 CPU oracle is timed on
 the host cores on a bounded sample of the same workload ("cpu_baseline").
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Counter calibration: run under `rocprofv3 --pmc FETCH_SIZE` and again under
+`--pmc WRITE_SIZE` with --calibrate-copy (a plain 256 MiB device-to-device
+copy follows the timed work), then `python bench.py --record-traffic
+<fetch_dir> <write_dir>` turns the two counter tables into the HBM bytes per
+chunk-kernel launch, scaled by what the same counter reads for the copy.
 """
 import argparse
 import hashlib
@@ -58,14 +64,90 @@ def kernel_source_hash():
 def measured_traffic(src_hash):
     """HBM bytes per launch of the chunk kernel from the committed rocprofv3
     counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_layer_1p3b_counters.json")
     try:
-        rec = json.load(open(path))
+        rec = json.load(open(COUNTERS_JSON))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_hash") != src_hash:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+COPY_CAL_BYTES = 256 << 20
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_layer_1p3b_counters.json")
+
+
+def calibration_copy(torch, dev):
+    """An elementwise device copy of COPY_CAL_BYTES read and COPY_CAL_BYTES
+    written (fp32 -> int32, so that it runs as a kernel rather than a DMA
+    transfer), three times: the known-size reference the HBM byte counters
+    are scaled by."""
+    src = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty(COPY_CAL_BYTES // 4, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _kernel_and_copy(rows, counter):
+    """Mean counter value (KiB per dispatch) of the chunk kernel, and of the
+    calibration copy: the one kernel dispatched exactly three times after the
+    last chunk-kernel dispatch."""
+    import collections
+    rows = [r for r in rows if r["Counter_Name"] == counter]
+    is_chunk = lambda r: "chunk_fwd_bf16_kernel" in r["Kernel_Name"]
+    ker = [float(r["Counter_Value"]) for r in rows if is_chunk(r)]
+    last = max(int(r["Dispatch_Id"]) for r in rows if is_chunk(r))
+    groups = collections.defaultdict(list)
+    for r in rows:
+        if int(r["Dispatch_Id"]) > last:
+            groups[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    cal = [(name, v) for name, v in groups.items() if len(v) == 3]
+    if len(cal) != 1:
+        raise SystemExit(f"cannot identify the calibration copy among {[(n[:60], len(v)) for n, v in groups.items()]}")
+    name, v = cal[0]
+    return sum(ker) / len(ker), len(ker), sum(v) / len(v), len(v), name
+
+
+def record_traffic(fetch_dir, write_dir):
+    """Write the calibrated per-launch HBM traffic of the chunk kernel."""
+    kf, nkf, cf, ncf, cname = _kernel_and_copy(_counter_rows(fetch_dir), "FETCH_SIZE")
+    kw, nkw, cw, ncw, _ = _kernel_and_copy(_counter_rows(write_dir), "WRITE_SIZE")
+    f_scale = COPY_CAL_BYTES / (cf * 1024.0)   # counter KiB -> true bytes, from the copy's read side
+    w_scale = COPY_CAL_BYTES / (cw * 1024.0)
+    rec = {
+        "kernel": "chunk_fwd_bf16_kernel<128,128,64> on layer_1p3b (B=8 T=4096 H=16 K=V=128)",
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
+        "kernel_dispatches": [nkf, nkw],
+        "copy_kernel": cname, "copy_bytes": COPY_CAL_BYTES,
+        "copy_fetch_kib": cf, "copy_write_kib": cw, "copy_dispatches": [ncf, ncw],
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "hbm_read_bytes_per_launch": kf * 1024.0 * f_scale,
+        "hbm_write_bytes_per_launch": kw * 1024.0 * w_scale,
+    }
+    rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    nbytes, _ = chunk_fwd_algorithmic(8, 4096, 16, 128, 128)
+    rec["algorithmic_bytes_per_launch"] = nbytes
+    rec["traffic_over_algorithmic"] = rec["hbm_bytes_per_launch"] / nbytes
+    with open(COUNTERS_JSON, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def device_inputs(inp, torch, dev):
@@ -118,7 +200,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="finish with a plain 256 MiB device copy (counter calibration runs)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: summarise two rocprofv3 --pmc runs into the counters file")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
               "sharding of this path is a design note, not a built feature.", file=sys.stderr)
@@ -208,6 +297,9 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, H)
+
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
 
     print(json.dumps(result), flush=True)
 

@@ -34,7 +34,10 @@
 // fp32 accumulator block holds rows 4*(lane/16)+i, so two accumulator blocks
 // supply exactly the 8 reduction indices a lane needs when the other operand
 // stores its reduction axis in perm32 order. Q, K, T and P are stored that way
-// (16-byte chunks XOR-swizzled by row against bank conflicts). K^T operands
+// (16-byte chunks XOR-swizzled by row against bank conflicts). Fragments are
+// read as one 16-byte LDS read each: the compiler fuses two 8-byte reads whose
+// addresses differ by a multiple of 512 bytes into one two-address read, which
+// costs about three times as much as a conflict-free 16-byte read. K^T operands
 // for the state update and V for R come from row-major tiles through the
 // transposing LDS read (ds_read_b64_tr_b16).
 #include "chunk_common.h"
@@ -49,9 +52,13 @@ typedef __attribute__((address_space(3))) s4 lds_s4;
 
 constexpr int kTP = 32 * 32 + 32 * 64;  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
 
+// Row-major tile of L bf16 per row: 16-byte chunk c of row r is stored at
+// chunk c ^ (r mod L/8). Sixteen consecutive rows then start on sixteen
+// different bank groups (L = 128), so 16-byte fragment reads of 16 rows are
+// free of bank conflicts.
 template <int L>
 __device__ __forceinline__ int swz(int row, int pos) {
-  constexpr int mask = (L / 8 - 1) < 7 ? (L / 8 - 1) : 7;
+  constexpr int mask = L / 8 - 1;
   return row * L + (((pos >> 3) ^ (row & mask)) << 3) + (pos & 7);
 }
 __device__ __forceinline__ int tp_off(int row, int pos) {
@@ -80,10 +87,14 @@ struct alignas(16) ChunkBuf {
   float eGn;
 };
 
+// Row stride of the fp32 16x16 scratch blocks: 20 floats puts the four rows
+// that a lane quad reads together on different banks.
+constexpr int kSS = 20;
+
 struct alignas(16) ProdScratch {  // one per producer wave, fp32 16x16 blocks, row-major
-  float Aown[256];                // A_pp
-  float Aoff[256];                // A_{p,p-1} (odd p)
-  float Town[256];                // T_pp
+  float Aown[16 * kSS];           // A_pp
+  float Aoff[16 * kSS];           // A_{p,p-1} (odd p)
+  float Town[16 * kSS];           // T_pp
 };
 
 template <int K, int VT>
@@ -249,7 +260,7 @@ __device__ __forceinline__ void invert16(const float* Ab, float* Tb, int lane) {
   for (int j4 = 0; j4 < 4; ++j4) {
     f32x4 a[4];  // rows 4q..4q+3, columns 4 j4 .. 4 j4 + 3
 #pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = lds_f4(Ab + (4 * q + r) * 16 + 4 * j4);
+    for (int r = 0; r < 4; ++r) a[r] = lds_f4(Ab + (4 * q + r) * kSS + 4 * j4);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * j4 + jj;
@@ -269,7 +280,7 @@ __device__ __forceinline__ void invert16(const float* Ab, float* Tb, int lane) {
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) Tb[(4 * q + r) * 16 + c] = x[r];
+  for (int r = 0; r < 4; ++r) Tb[(4 * q + r) * kSS + c] = x[r];
 }
 
 // Write a fp32 16x16 row-major block into the buffer's Th/Tl at (row0, col0):
@@ -277,7 +288,7 @@ __device__ __forceinline__ void invert16(const float* Ab, float* Tb, int lane) {
 template <int K, int VT>
 __device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* Tb, int row0, int col0, int lane) {
   const int r = lane >> 2, cg = lane & 3;
-  put_split4(bf.Th, bf.Tl, tp_off(row0 + r, perm_col(col0 + 4 * cg)), lds_f4(Tb + r * 16 + 4 * cg));
+  put_split4(bf.Th, bf.Tl, tp_off(row0 + r, perm_col(col0 + 4 * cg)), lds_f4(Tb + r * kSS + 4 * cg));
 }
 
 template <int P, int K, int VT>
@@ -330,9 +341,9 @@ __device__ __forceinline__ void producer_rows(ChunkBuf<K, VT>& bf, ProdScratch& 
     const f32x4 aT = quad_transpose(av, x4);
     const int col = perm_col(16 * bs + 4 * m4);
     put_split4(bf.Ph, bf.Pl, tp_off(trow, col), pT);
-    if (bs == P) *reinterpret_cast<f32x4*>(&ps.Aown[(4 * g + x4) * 16 + 4 * m4]) = aT;
+    if (bs == P) *reinterpret_cast<f32x4*>(&ps.Aown[(4 * g + x4) * kSS + 4 * m4]) = aT;
     if constexpr ((P & 1) != 0) {
-      if (bs == P - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[(4 * g + x4) * 16 + 4 * m4]) = aT;
+      if (bs == P - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[(4 * g + x4) * kSS + 4 * m4]) = aT;
     }
     if constexpr (P >= 2) {
       if (bs < 2) put_split4(bf.Th, bf.Tl, tp_off(trow, col), -aT);  // -A21
@@ -350,17 +361,17 @@ __device__ __forceinline__ void producer_offdiag(ChunkBuf<K, VT>& bf, const Prod
                                                  const ProdScratch& prev, int lane) {
   const int g = lane >> 4, l16 = lane & 15;
   s4 ah, al, bh, bl;
-  split4(lds_f4(&ps.Aoff[l16 * 16 + 4 * g]), ah, al);
+  split4(lds_f4(&ps.Aoff[l16 * kSS + 4 * g]), ah, al);
   f32x4 tv;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) tv[j] = prev.Town[(4 * g + j) * 16 + l16];
+  for (int j = 0; j < 4; ++j) tv[j] = prev.Town[(4 * g + j) * kSS + l16];
   split4(tv, bh, bl);
   f32x4 y = {0.f, 0.f, 0.f, 0.f};
   y = mfma16x16x16(ah, bh, y);
   y = mfma16x16x16(ah, bl, y);
   y = mfma16x16x16(al, bh, y);
   s4 th, tl, yh, yl;
-  split4(lds_f4(&ps.Town[l16 * 16 + 4 * g]), th, tl);
+  split4(lds_f4(&ps.Town[l16 * kSS + 4 * g]), th, tl);
   split4(y, yh, yl);
   f32x4 z = {0.f, 0.f, 0.f, 0.f};
   z = mfma16x16x16(th, yh, z);
