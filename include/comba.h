@@ -100,8 +100,10 @@ size_t comba_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K
  * arithmetic throughout.
  *
  * workspace: device memory of at least comba_chunk_fwd_workspace_size(...)
- * bytes, used only during this call on `stream`. final_state must not
- * overlap initial_state or any input.
+ * bytes, used only during this call on `stream`. final_state may be the same
+ * pointer as initial_state (each workgroup reads its slice of the initial
+ * state before it writes the same slice); a partial overlap is rejected with
+ * COMBA_ERR_INVALID_ARG, and final_state must not overlap any other input.
  */
 int32_t comba_chunk_fwd(const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const float* d,

@@ -5,7 +5,8 @@ Gates (rel-L2 over a whole tensor, fp64): 2e-3 for bf16 q/k/v (o in bf16),
 left is the rounding of the kernels' non-input operands, each carried as a
 hi+lo bf16 pair (about 2^-17 relative) and accumulated in fp32; a 1e-4 gate
 there checks that no operand silently dropped to a single bf16 (which costs
-about 2e-4 to 2e-3).
+about 2e-4 to 2e-3 in an fp64 experiment that rounds one intermediate of the
+chunk form at a time).
 """
 import dataclasses
 
