@@ -11,14 +11,15 @@
 //         Ubar_top = T1 R_top,  Ubar_bot = T2 (R_bot - A21 Ubar_top),
 //     O = diag(e^G)(Q h - d K h) + P Ubar,   h' = e^Gn h + K^T diag(e^(Gn-G)) Ubar
 //     The fp32 state slice h[:, 16 channels] never leaves a consumer's registers.
-//   producers (waves 4-7, one 16-token row block p each), chunk c+1:
-//     stage q/k/v/alpha/beta in LDS, decays, Q K^T and K K^T of row block p,
-//     A (strictly lower) and P (masked scores), and the two 32x32 diagonal
-//     inverses T1 = (I + A11)^-1, T2 = (I + A22)^-1: each 16x16 diagonal
-//     block by fp32 forward substitution, the off-diagonal 16x16 block as
-//     T_{p,p-1} = -T_pp A_{p,p-1} T_{p-1,p-1} by the odd producer, which
-//     inverts block p-1 again itself so the producers never wait on each other
-//     after staging.
+//   producers (waves 4-7), chunk c+1:
+//     stage q/k/v/alpha/beta in LDS, decays, then the ten lower-triangular
+//     16x16 blocks of Q K^T and K K^T shared out in balanced sets (wave p
+//     always holds diagonal block p), scaled into A (strictly lower) and P
+//     (masked scores), and the two 32x32 diagonal inverses T1 = (I + A11)^-1,
+//     T2 = (I + A22)^-1: wave p inverts its 16x16 diagonal block by fp32
+//     forward substitution; after a producer-only sync the odd waves form the
+//     off-diagonal block T_{p,p-1} = -T_pp A_{p,p-1} T_{p-1,p-1} on the
+//     matrix cores.
 //
 // Double-buffered LDS holds everything a consumer reads for one chunk; one
 // workgroup barrier per chunk hands a buffer from producers to consumers.
@@ -50,7 +51,21 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 typedef short s8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s4 lds_s4;
 
-constexpr int kTP = 32 * 32 + 32 * 64;  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
+constexpr int kTP = 32 * 32 + 32 * 64;
+// Third descriptor word of a raw buffer resource on gfx9-family parts
+// (32-bit data format, no swizzle): with stride 0, an access at or beyond
+// num_records bytes is dropped (stores) or returns zero (loads).
+constexpr int kBufferWord3 = 0x00020000;
+
+// A wave-uniform pointer held in scalar registers (the value of lane 0): a
+// buffer resource built from it needs no per-lane waterfall loop.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
 
 // Row-major tile of L bf16 per row: 16-byte chunk c of row r is stored at
 // chunk c ^ (r mod L/8). Sixteen consecutive rows then start on sixteen
@@ -107,27 +122,39 @@ struct alignas(16) SmemV3 {
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ f32x4 lds_f4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// hi / lo bf16 split of two floats, packed: hi = round-to-nearest bf16 pair
+// (one v_cvt_pk_bf16_f32), its exact fp32 values by shift and mask, lo = the
+// rounded remainders (a second conversion). Three VALU instructions per value.
+__device__ __forceinline__ void split2(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const bf16x2 h = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
+  hi = __builtin_bit_cast(unsigned, h);
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  const bf16x2 l = __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2);
+  lo = __builtin_bit_cast(unsigned, l);
+}
+
+// Eight values (m0 then m1) as an MFMA operand pair.
 __device__ __forceinline__ void split_pair(const f32x4& m0, const f32x4& m1, bf16x8& hi, bf16x8& lo) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __bf16 a, b;
-    split_bf16(m0[j], a, b);
-    hi[j] = a;
-    lo[j] = b;
-    split_bf16(m1[j], a, b);
-    hi[j + 4] = a;
-    lo[j + 4] = b;
-  }
+  unsigned h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(m0[0], m0[1], h0, l0);
+  split2(m0[2], m0[3], h1, l1);
+  split2(m1[0], m1[1], h2, l2);
+  split2(m1[2], m1[3], h3, l3);
+  hi = __builtin_bit_cast(bf16x8, (u32x4){h0, h1, h2, h3});
+  lo = __builtin_bit_cast(bf16x8, (u32x4){l0, l1, l2, l3});
 }
 
 __device__ __forceinline__ void split4(const f32x4& x, s4& hi, s4& lo) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __bf16 a, b;
-    split_bf16(x[j], a, b);
-    hi[j] = __builtin_bit_cast(short, a);
-    lo[j] = __builtin_bit_cast(short, b);
-  }
+  unsigned h0, h1, l0, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  hi = __builtin_bit_cast(s4, (u32x2){h0, h1});
+  lo = __builtin_bit_cast(s4, (u32x2){l0, l1});
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x16(s4 a, s4 b, f32x4 c) {
@@ -174,16 +201,11 @@ __device__ __forceinline__ f32x4 quad_transpose(const f32x4& v, int x) {
 
 // Split four fp32 values into hi / lo bf16 and write them as two 8-byte stores.
 __device__ __forceinline__ void put_split4(u16* hi, u16* lo, int off, const f32x4& x) {
-  bf16x4 h, l;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    __bf16 a, b;
-    split_bf16(x[j], a, b);
-    h[j] = a;
-    l[j] = b;
-  }
-  *reinterpret_cast<bf16x4*>(hi + off) = h;
-  *reinterpret_cast<bf16x4*>(lo + off) = l;
+  unsigned h0, h1, l0, l1;
+  split2(x[0], x[1], h0, l0);
+  split2(x[2], x[3], h1, l1);
+  *reinterpret_cast<u32x2*>(hi + off) = (u32x2){h0, h1};
+  *reinterpret_cast<u32x2*>(lo + off) = (u32x2){l0, l1};
 }
 
 // hi + lo * (a*b + c) style triple product accumulate with both operands split.
@@ -291,67 +313,71 @@ __device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* 
   put_split4(bf.Th, bf.Tl, tp_off(row0 + r, perm_col(col0 + 4 * cg)), lds_f4(Tb + r * kSS + 4 * cg));
 }
 
-template <int P, int K, int VT>
-__device__ __forceinline__ void producer_rows(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
-                                              float G, float rinv, float be) {
+// One producer's share of the chunk's ten lower-triangular 16x16 blocks
+// (row block R, column block C <= R): its diagonal block (D, D) first, then up
+// to two more, (R1, C1) and (R2, C2). The shares are balanced so that no wave
+// carries more than three blocks next to its diagonal inverse:
+//   wave 0: (0,0) (3,0) (3,1)   wave 1: (1,1) (1,0)
+//   wave 2: (2,2) (2,0) (2,1)   wave 3: (3,3) (3,2)
+// (waves 1 and 3 also form the off-diagonal inverse block afterwards).
+// For each block: Q K^T and K K^T on the matrix cores, then A (strictly lower,
+// beta_t e^(Gx_t - G_s) k_t.k_s) and P ((q_t.k_s - d k_t.k_s) e^(G_t - G_s), s <= t)
+// written as hi / lo bf16. A_DD goes to the wave's scratch for its inverse;
+// A_{R,R-1} (odd R) to the scratch for the off-diagonal step; the A blocks
+// below the 32x32 diagonal enter T's storage negated (-A21).
+template <int D, int NB, int R1, int C1, int R2, int C2, int K, int VT>
+__device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
+                                                float G, float rinv, float be) {
+  constexpr int Rb[3] = {D, R1, R2};
+  constexpr int Cb[3] = {D, C1, C2};
   const int g = lane >> 4, l16 = lane & 15, m4 = l16 >> 2, x4 = l16 & 3;
-  f32x4 aqk[P + 1], akk[P + 1];
+  f32x4 aqk[NB], akk[NB];
 #pragma unroll
-  for (int bs = 0; bs <= P; ++bs) {
-    aqk[bs] = f32x4{0.f, 0.f, 0.f, 0.f};
-    akk[bs] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) {
+    aqk[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    akk[b] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int s = 0; s < K / 32; ++s) {
-    const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * P + l16, 32 * s + 8 * g)]);
-    const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * P + l16, 32 * s + 8 * g)]);
 #pragma unroll
-    for (int bs = 0; bs <= P; ++bs) {
-      const bf16x8 bk = lds8(&bf.Kc[swz<K>(16 * bs + l16, 32 * s + 8 * g)]);
-      aqk[bs] = mfma16x16x32(aq, bk, aqk[bs]);
-      akk[bs] = mfma16x16x32(ak, bk, akk[bs]);
+    for (int b = 0; b < NB; ++b) {
+      const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
+      const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
+      const bf16x8 bk = lds8(&bf.Kc[swz<K>(16 * Cb[b] + l16, 32 * s + 8 * g)]);
+      aqk[b] = mfma16x16x32(aq, bk, aqk[b]);
+      akk[b] = mfma16x16x32(ak, bk, akk[b]);
     }
-  }
-  float Gt[4], bt[4], rt[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = 16 * P + 4 * g + i;
-    Gt[i] = __shfl(G, t, kWave);
-    bt[i] = __shfl(be, t, kWave);
-    rt[i] = __shfl(rinv, t, kWave);
   }
   // Scaled blocks leave the accumulator layout (4 rows x 1 column per lane)
   // through a quad transpose (1 row x 4 columns per lane): every store below
   // is then one 8- or 16-byte LDS write.
-  const int trow = 16 * P + 4 * g + x4;  // row held after the transpose
 #pragma unroll
-  for (int bs = 0; bs <= P; ++bs) {
-    const int s_ = 16 * bs + l16;
+  for (int b = 0; b < NB; ++b) {
+    const int R = Rb[b], C = Cb[b];
+    const int s_ = 16 * C + l16;
     const float Gs = __shfl(G, s_, kWave);
     f32x4 av, pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 16 * P + 4 * g + i;
-      const float M = __expf(fminf(Gt[i] - Gs, 0.f));  // exp(G_t - G_s) for s <= t
-      const float kk = akk[bs][i];
-      av[i] = (s_ < t) ? bt[i] * (M * rt[i]) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
-      pv[i] = (s_ <= t) ? (aqk[bs][i] - dh * kk) * M : 0.f;
+      const int t = 16 * R + 4 * g + i;
+      const float Gt = __shfl(G, t, kWave), bt = __shfl(be, t, kWave), rt = __shfl(rinv, t, kWave);
+      const float M = __expf(fminf(Gt - Gs, 0.f));  // exp(G_t - G_s) for s <= t
+      const float kk = akk[b][i];
+      av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+      pv[i] = (s_ <= t) ? (aqk[b][i] - dh * kk) * M : 0.f;
     }
     const f32x4 pT = quad_transpose(pv, x4);
     const f32x4 aT = quad_transpose(av, x4);
-    const int col = perm_col(16 * bs + 4 * m4);
+    const int trow = 16 * R + 4 * g + x4;  // row held after the transpose
+    const int col = perm_col(16 * C + 4 * m4);
     put_split4(bf.Ph, bf.Pl, tp_off(trow, col), pT);
-    if (bs == P) *reinterpret_cast<f32x4*>(&ps.Aown[(4 * g + x4) * kSS + 4 * m4]) = aT;
-    if constexpr ((P & 1) != 0) {
-      if (bs == P - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[(4 * g + x4) * kSS + 4 * m4]) = aT;
-    }
-    if constexpr (P >= 2) {
-      if (bs < 2) put_split4(bf.Th, bf.Tl, tp_off(trow, col), -aT);  // -A21
-    }
+    if (b == 0) *reinterpret_cast<f32x4*>(&ps.Aown[(4 * g + x4) * kSS + 4 * m4]) = aT;
+    if ((R & 1) != 0 && C == R - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[(4 * g + x4) * kSS + 4 * m4]) = aT;
+    if (R >= 2 && C < 2) put_split4(bf.Th, bf.Tl, tp_off(trow, col), -aT);  // -A21
   }
-  // diagonal inverse of this row block (reads this wave's own scratch writes)
+  // diagonal inverse of this wave's block (reads this wave's own scratch writes)
   invert16(ps.Aown, ps.Town, lane);
-  store_t_block(bf, ps.Town, 16 * P, 16 * P, lane);
+  store_t_block(bf, ps.Town, 16 * D, 16 * D, lane);
 }
 
 // T_{P,P-1} = -T_PP A_{P,P-1} T_{P-1,P-1} for odd P, after the even producer's
@@ -401,9 +427,13 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
   const int h = unit % H;
   int n = unit / H;
-  if (order) n = order[n];
+  if (order) n = __builtin_amdgcn_readfirstlane(order[n]);
   int b, t0, t1;
   sequence_range(cu_seqlens, n, T, b, t0, t1);
+  // The bounds are the same for every lane (loaded values): keep them, and
+  // all address arithmetic derived from them, in scalar registers.
+  t0 = __builtin_amdgcn_readfirstlane(t0);
+  t1 = __builtin_amdgcn_readfirstlane(t1);
   const float dh = d[h];
   const int nchunks = (t1 - t0 + 63) / 64;
 
@@ -508,10 +538,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           if (lane == 63) bf.eGn = __expf(G);
         }
         switch (p) {
-          case 0: producer_rows<0>(bf, sm.ps[0], olane, dh, G, rinv, be); break;
-          case 1: producer_rows<1>(bf, sm.ps[1], olane, dh, G, rinv, be); break;
-          case 2: producer_rows<2>(bf, sm.ps[2], olane, dh, G, rinv, be); break;
-          default: producer_rows<3>(bf, sm.ps[3], olane, dh, G, rinv, be); break;
+          case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], olane, dh, G, rinv, be); break;
+          case 1: producer_blocks<1, 2, 1, 0, 0, 0>(bf, sm.ps[1], olane, dh, G, rinv, be); break;
+          case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], olane, dh, G, rinv, be); break;
+          default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], olane, dh, G, rinv, be); break;
         }
         producer_sync(&sm.prod_bar, epoch, lane);  // diagonal inverses visible
         if (p == 1) producer_offdiag<1>(bf, sm.ps[1], sm.ps[0], olane);
@@ -526,6 +556,12 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     // ======================= consumers: run chunk it-1 in iteration it =======================
     const int vloc = wave * 16 + l16;
     const int vcol = vt * VT + vloc;
+    // Byte offsets of this lane's four output rows (4 g + i) inside a 16-row
+    // block, channel vcol; H * V elements separate consecutive tokens.
+    const int hv = H * V;
+    int ovoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ovoff[i] = ((4 * g + i) * hv + vcol) * static_cast<int>(sizeof(OutT));
     f32x4 hs[K / 16];
     const int64_t srow = ((static_cast<int64_t>(n) * H + h) * V + vcol) * K;
 #pragma unroll
@@ -538,6 +574,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         const ChunkBuf<K, VT>& bf = sm.buf[c & 1];
         const int c0 = t0 + c * 64;
         const int nrows = min(64, t1 - c0);
+        const int64_t obase = ((static_cast<int64_t>(b) * T + c0) * H + h) * V;  // row c0, head h
 
         bf16x8 hbh[K / 32], hbl[K / 32];
 #pragma unroll
@@ -619,20 +656,27 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
             const int off1 = tp_off(16 * r4 + l16, 32 + 8 * g);
             acc = mma3(lds8(&bf.Ph[off1]), lds8(&bf.Pl[off1]), ubh1, ubl1, acc);
           }
-          // quad transpose: this lane then holds row 16 r4 + 4 g + (l16 & 3),
-          // channels 4 (l16 >> 2) .. +3 of its wavefront's 16 -> one store
-          const f32x4 oT = quad_transpose(acc, l16 & 3);
-          const int t = 16 * r4 + 4 * g + (l16 & 3);
-          if (t < nrows) {
-            const int64_t off = ((static_cast<int64_t>(b) * T + c0 + t) * H + h) * V + vt * VT + wave * 16 + 4 * (l16 >> 2);
-            if constexpr (sizeof(OutT) == 2) {
-              bf16x4 ob;
+          // Stored straight from the accumulator layout: this lane holds rows
+          // 16 r4 + 4 g + i of its wavefront's channel l16; the 16 lanes of a
+          // row write 32 contiguous bytes and the four consumer waves complete
+          // the workgroup's segment of that row. The buffer resource covers
+          // only the rows of this 16-row block that lie inside the sequence,
+          // so stores to rows past its end are dropped by the range check.
+          const int vrows = min(max(nrows - 16 * r4, 0), 16);
+          const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+              uniform_ptr(o + obase + static_cast<int64_t>(16 * r4) * hv), static_cast<short>(0),
+              __builtin_amdgcn_readfirstlane(vrows * hv * static_cast<int>(sizeof(OutT))), kBufferWord3);
+          if constexpr (sizeof(OutT) == 2) {
+            const unsigned p01 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){acc[0], acc[1]}, bf16x2));
+            const unsigned p23 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){acc[2], acc[3]}, bf16x2));
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<u16>(p01), orsrc, ovoff[0], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<u16>(p01 >> 16), orsrc, ovoff[1], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<u16>(p23), orsrc, ovoff[2], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<u16>(p23 >> 16), orsrc, ovoff[3], 0, 0);
+          } else {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) ob[j] = to_bf16(oT[j]);
-              *reinterpret_cast<bf16x4*>(o + off) = ob;
-            } else {
-              *reinterpret_cast<f32x4*>(o + off) = oT;
-            }
+            for (int i = 0; i < 4; ++i)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), orsrc, ovoff[i], 0, 0);
           }
         }
 
