@@ -49,8 +49,8 @@ int32_t check_args(const void* q, const void* k, const void* v, const float* alp
   const int64_t N = cu ? num_seqs : B;
   if (N * H * 2 > INT_MAX / 16)
     return fail(COMBA_ERR_UNSUPPORTED, "too many (sequence, head) pairs for one launch");
-  if (static_cast<int64_t>(H) * V > (1 << 24))
-    return fail(COMBA_ERR_UNSUPPORTED, "H * V above 2^24 (per-token row offsets must fit 32 bits)");
+  if (static_cast<int64_t>(H) * (K > V ? K : V) > (1 << 24))
+    return fail(COMBA_ERR_UNSUPPORTED, "H * max(K, V) above 2^24 (chunk offsets must fit 32 bits)");
   if (s0 && sf && s0 != sf) {
     const char* s0b = reinterpret_cast<const char*>(s0);
     const char* sfb = reinterpret_cast<const char*>(sf);

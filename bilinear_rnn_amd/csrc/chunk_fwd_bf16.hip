@@ -110,6 +110,12 @@ struct alignas(16) ProdScratch {  // one per producer wave, fp32 16x16 blocks, r
   float Aown[16 * kSS];           // A_pp
   float Aoff[16 * kSS];           // A_{p,p-1} (odd p)
   float Town[16 * kSS];           // T_pp
+  // Per-token decay factors of this wave's blocks, indexed by token in chunk:
+  // diagonal block: G_t, beta_t, 1/alpha_t; off-diagonal block j (column
+  // block C, last token r = 16 C + 15): beta_t e^(Gx_t - G_r), e^(G_t - G_r)
+  // (rows) and e^(G_r - G_s) (columns).
+  float dG[64], dB[64], dR[64];
+  float oA[2][64], oP[2][64], oS[2][64];
 };
 
 template <int K, int VT>
@@ -327,10 +333,23 @@ __device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* 
 // below the 32x32 diagonal enter T's storage negated (-A21).
 template <int D, int NB, int R1, int C1, int R2, int C2, int K, int VT>
 __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
-                                                float G, float rinv, float be) {
+                                                float G, float lg, float rinv, float be) {
   constexpr int Rb[3] = {D, R1, R2};
   constexpr int Cb[3] = {D, C1, C2};
   const int g = lane >> 4, l16 = lane & 15, m4 = l16 >> 2, x4 = l16 & 3;
+  // Decay tables (lane = token). Off-diagonal blocks (every s < every t)
+  // factor e^(G_t - G_s) = e^(G_t - G_r) e^(G_r - G_s) through the column
+  // block's last token r: both factors lie in (0, 1], so no per-element exp.
+  ps.dG[lane] = G;
+  ps.dB[lane] = be;
+  ps.dR[lane] = rinv;
+#pragma unroll
+  for (int b = 1; b < NB; ++b) {
+    const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 16 * Cb[b] + 15));
+    ps.oA[b - 1][lane] = be * __expf(fminf(G - lg - Gr, 0.f));  // beta_t e^(Gx_t - G_r), t > r
+    ps.oP[b - 1][lane] = __expf(fminf(G - Gr, 0.f));            // e^(G_t - G_r), t > r
+    ps.oS[b - 1][lane] = __expf(fminf(Gr - G, 0.f));            // e^(G_r - G_s), s <= r
+  }
   f32x4 aqk[NB], akk[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -354,17 +373,30 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int R = Rb[b], C = Cb[b];
-    const int s_ = 16 * C + l16;
-    const float Gs = __shfl(G, s_, kWave);
     f32x4 av, pv;
+    if (b == 0) {
+      // diagonal block: masks and one exp per element (both tokens in one block)
+      const f32x4 Gt = lds_f4(&ps.dG[16 * R + 4 * g]), bt = lds_f4(&ps.dB[16 * R + 4 * g]);
+      const f32x4 rt = lds_f4(&ps.dR[16 * R + 4 * g]);
+      const int s_ = 16 * C + l16;
+      const float Gs = ps.dG[s_];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * R + 4 * g + i;
-      const float Gt = __shfl(G, t, kWave), bt = __shfl(be, t, kWave), rt = __shfl(rinv, t, kWave);
-      const float M = __expf(fminf(Gt - Gs, 0.f));  // exp(G_t - G_s) for s <= t
-      const float kk = akk[b][i];
-      av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
-      pv[i] = (s_ <= t) ? (aqk[b][i] - dh * kk) * M : 0.f;
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * R + 4 * g + i;
+        const float M = __expf(fminf(Gt[i] - Gs, 0.f));  // exp(G_t - G_s) for s <= t
+        const float kk = akk[b][i];
+        av[i] = (s_ < t) ? bt[i] * (M * rt[i]) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+        pv[i] = (s_ <= t) ? (aqk[b][i] - dh * kk) * M : 0.f;
+      }
+    } else {
+      const f32x4 ta = lds_f4(&ps.oA[b - 1][16 * R + 4 * g]), tp = lds_f4(&ps.oP[b - 1][16 * R + 4 * g]);
+      const float ts = ps.oS[b - 1][16 * C + l16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float kk = akk[b][i] * ts;
+        av[i] = ta[i] * kk;
+        pv[i] = (aqk[b][i] * ts - dh * kk) * tp[i];
+      }
     }
     const f32x4 pT = quad_transpose(pv, x4);
     const f32x4 aT = quad_transpose(av, x4);
@@ -456,39 +488,50 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     const int p = wave - 4;
     const int ptid = tid - 256;
     constexpr int KP = K / 8, QPT = 64 * KP / 256, VPR = VT / 8, VPT = 64 * VPR / 256;
-    uint4 rq[QPT], rk[QPT], rv[VPT];
+    u32x4 rq[QPT], rk[QPT], rv[VPT];
     float ra = 1.f, rb = 0.f;
     int epoch = 0;
+    // Byte offsets of this thread's 16-byte pieces inside one chunk (row of
+    // the chunk times the token stride, plus the column): the same for every
+    // chunk, so each load below is one buffer instruction without address
+    // arithmetic. Rows past the end of the sequence lie beyond the chunk's
+    // buffer range and load as zeros (the padding the chunk algebra needs).
+    int qkoff[QPT], voff[VPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int piece = ptid + j * 256, row = piece / KP, c8 = piece % KP;
+      qkoff[j] = (row * H * K + c8 * 8) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR;
+      voff[j] = (row * H * V + c8 * 8) * 2;
+    }
     auto fetch = [&](int c0) {
+      const int nrows = min(64, t1 - c0);
+      const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;  // token c0, head h
+      const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(const_cast<u16*>(q + tok0 * K)), static_cast<short>(0),
+          __builtin_amdgcn_readfirstlane(nrows * H * K * 2), kBufferWord3);
+      const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(const_cast<u16*>(k + tok0 * K)), static_cast<short>(0),
+          __builtin_amdgcn_readfirstlane(nrows * H * K * 2), kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          uniform_ptr(const_cast<u16*>(v + tok0 * V + vt * VT)), static_cast<short>(0),
+          __builtin_amdgcn_readfirstlane(nrows * H * V * 2), kBufferWord3);
 #pragma unroll
       for (int j = 0; j < QPT; ++j) {
-        const int piece = ptid + j * 256, row = piece / KP, c8 = piece % KP, t = c0 + row;
-        if (t < t1) {
-          const int64_t off = ((static_cast<int64_t>(b) * T + t) * H + h) * K + c8 * 8;
-          rq[j] = *reinterpret_cast<const uint4*>(q + off);
-          rk[j] = *reinterpret_cast<const uint4*>(k + off);
-        } else {
-          rq[j] = make_uint4(0, 0, 0, 0);
-          rk[j] = make_uint4(0, 0, 0, 0);
-        }
+        rq[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, qkoff[j], 0, 0);
+        rk[j] = __builtin_amdgcn_raw_buffer_load_b128(kr, qkoff[j], 0, 0);
       }
 #pragma unroll
-      for (int j = 0; j < VPT; ++j) {
-        const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR, t = c0 + row;
-        if (t < t1) {
-          const int64_t off = ((static_cast<int64_t>(b) * T + t) * H + h) * V + vt * VT + c8 * 8;
-          rv[j] = *reinterpret_cast<const uint4*>(v + off);
-        } else {
-          rv[j] = make_uint4(0, 0, 0, 0);
-        }
-      }
+      for (int j = 0; j < VPT; ++j) rv[j] = __builtin_amdgcn_raw_buffer_load_b128(vr, voff[j], 0, 0);
       if (ptid < 64) {
-        const int t = c0 + ptid;
-        if (t < t1) {
-          const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
+        if (ptid < nrows) {
+          const int64_t tok = tok0 + static_cast<int64_t>(ptid) * H;
           ra = alpha[tok];
           rb = beta[tok];
-        } else {
+        } else {  // padding token: no decay, no write
           ra = 1.f;
           rb = 0.f;
         }
@@ -515,12 +558,17 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
           const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR;
-          *reinterpret_cast<uint4*>(&bf.Vv[swz<VT>(row, c8 * 8)]) = rv[j];
+          *reinterpret_cast<u32x4*>(&bf.Vv[swz<VT>(row, c8 * 8)]) = rv[j];
         }
         if (ptid < 64) {
           bf.raw_a[ptid] = ra;
           bf.raw_b[ptid] = rb;
         }
+        // The staging registers are free again: fetch the next chunk now, so
+        // that its loads are in flight during all of this chunk's work (the
+        // work below issues no other vector-memory access that would wait on
+        // them).
+        if (it + 1 < nchunks) fetch(t0 + (it + 1) * 64);
         producer_sync(&sm.prod_bar, epoch, lane);
 
         // decays: every producer wave computes all 64 rows (lane = row)
@@ -538,17 +586,14 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           if (lane == 63) bf.eGn = __expf(G);
         }
         switch (p) {
-          case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], olane, dh, G, rinv, be); break;
-          case 1: producer_blocks<1, 2, 1, 0, 0, 0>(bf, sm.ps[1], olane, dh, G, rinv, be); break;
-          case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], olane, dh, G, rinv, be); break;
-          default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], olane, dh, G, rinv, be); break;
+          case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], olane, dh, G, lg, rinv, be); break;
+          case 1: producer_blocks<1, 2, 1, 0, 0, 0>(bf, sm.ps[1], olane, dh, G, lg, rinv, be); break;
+          case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], olane, dh, G, lg, rinv, be); break;
+          default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], olane, dh, G, lg, rinv, be); break;
         }
         producer_sync(&sm.prod_bar, epoch, lane);  // diagonal inverses visible
         if (p == 1) producer_offdiag<1>(bf, sm.ps[1], sm.ps[0], olane);
         if (p == 3) producer_offdiag<3>(bf, sm.ps[3], sm.ps[2], olane);
-        // Prefetch the next chunk only now: every wait on a vector-memory counter
-        // inside the work above would otherwise also wait for these loads.
-        if (it + 1 < nchunks) fetch(t0 + (it + 1) * 64);
       }
       __syncthreads();
     }
