@@ -174,37 +174,6 @@ __device__ __forceinline__ void put_split(u16* hi, u16* lo, int off, float x) {
   lo[off] = __builtin_bit_cast(u16, b);
 }
 
-// 4x4 transpose inside each lane quad (lanes 4m..4m+3): lane 4m+x holds v[i]
-// = M[i][x] on entry and M[x][i] on exit. Two butterfly stages (partner lane
-// x^1, then x^2), each moving two values with DPP quad permutations; the
-// selects are plain two-way choices on the lane bit.
-__device__ __forceinline__ float dpp_xor1(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xb1, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4e, 0xf, 0xf, false));
-}
-__device__ __forceinline__ f32x4 quad_transpose(const f32x4& v, int x) {
-  const bool b0 = (x & 1) != 0, b1 = (x & 2) != 0;
-  // stage 1: 2x2 transposes between lanes x and x^1
-  const float s0 = b0 ? v[0] : v[1], s1 = b0 ? v[2] : v[3];
-  const float r0 = dpp_xor1(s0), r1 = dpp_xor1(s1);
-  f32x4 w;
-  w[0] = b0 ? r0 : v[0];
-  w[1] = b0 ? v[1] : r0;
-  w[2] = b0 ? r1 : v[2];
-  w[3] = b0 ? v[3] : r1;
-  // stage 2: swap 2-element halves between lanes x and x^2
-  const float t0 = b1 ? w[0] : w[2], t1 = b1 ? w[1] : w[3];
-  const float u0 = dpp_xor2(t0), u1 = dpp_xor2(t1);
-  f32x4 z;
-  z[0] = b1 ? u0 : w[0];
-  z[1] = b1 ? u1 : w[1];
-  z[2] = b1 ? w[2] : u0;
-  z[3] = b1 ? w[3] : u1;
-  return z;
-}
-
 // Split four fp32 values into hi / lo bf16 and write them as two 8-byte stores.
 __device__ __forceinline__ void put_split4(u16* hi, u16* lo, int off, const f32x4& x) {
   unsigned h0, h1, l0, l1;
@@ -350,6 +319,10 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
     ps.oP[b - 1][lane] = __expf(fminf(G - Gr, 0.f));            // e^(G_t - G_r), t > r
     ps.oS[b - 1][lane] = __expf(fminf(Gr - G, 0.f));            // e^(G_r - G_s), s <= r
   }
+  // Each block is formed transposed, K_C Q_R^T and K_C K_R^T (K K^T is
+  // symmetric): the accumulator then gives a lane one row t = 16 R + l16 and
+  // four consecutive columns s = 16 C + 4 g + i, i.e. a contiguous 8-byte
+  // piece of a row of P, A or T, written without any lane exchange.
   f32x4 aqk[NB], akk[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -363,49 +336,42 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
       const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
       const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
       const bf16x8 bk = lds8(&bf.Kc[swz<K>(16 * Cb[b] + l16, 32 * s + 8 * g)]);
-      aqk[b] = mfma16x16x32(aq, bk, aqk[b]);
-      akk[b] = mfma16x16x32(ak, bk, akk[b]);
+      aqk[b] = mfma16x16x32(bk, aq, aqk[b]);
+      akk[b] = mfma16x16x32(bk, ak, akk[b]);
     }
   }
-  // Scaled blocks leave the accumulator layout (4 rows x 1 column per lane)
-  // through a quad transpose (1 row x 4 columns per lane): every store below
-  // is then one 8- or 16-byte LDS write.
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const int R = Rb[b], C = Cb[b];
+    const int t = 16 * R + l16;  // row of this lane; columns s = 16 C + 4 g + i
     f32x4 av, pv;
     if (b == 0) {
       // diagonal block: masks and one exp per element (both tokens in one block)
-      const f32x4 Gt = lds_f4(&ps.dG[16 * R + 4 * g]), bt = lds_f4(&ps.dB[16 * R + 4 * g]);
-      const f32x4 rt = lds_f4(&ps.dR[16 * R + 4 * g]);
-      const int s_ = 16 * C + l16;
-      const float Gs = ps.dG[s_];
+      const float Gt = ps.dG[t], bt = ps.dB[t], rt = ps.dR[t];
+      const f32x4 Gs = lds_f4(&ps.dG[16 * C + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * R + 4 * g + i;
-        const float M = __expf(fminf(Gt[i] - Gs, 0.f));  // exp(G_t - G_s) for s <= t
+        const int s_ = 16 * C + 4 * g + i;
+        const float M = __expf(fminf(Gt - Gs[i], 0.f));  // exp(G_t - G_s) for s <= t
         const float kk = akk[b][i];
-        av[i] = (s_ < t) ? bt[i] * (M * rt[i]) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+        av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
         pv[i] = (s_ <= t) ? (aqk[b][i] - dh * kk) * M : 0.f;
       }
     } else {
-      const f32x4 ta = lds_f4(&ps.oA[b - 1][16 * R + 4 * g]), tp = lds_f4(&ps.oP[b - 1][16 * R + 4 * g]);
-      const float ts = ps.oS[b - 1][16 * C + l16];
+      const float ta = ps.oA[b - 1][t], tp = ps.oP[b - 1][t];
+      const f32x4 ts = lds_f4(&ps.oS[b - 1][16 * C + 4 * g]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float kk = akk[b][i] * ts;
-        av[i] = ta[i] * kk;
-        pv[i] = (aqk[b][i] * ts - dh * kk) * tp[i];
+        const float kk = akk[b][i] * ts[i];
+        av[i] = ta * kk;
+        pv[i] = (aqk[b][i] * ts[i] - dh * kk) * tp;
       }
     }
-    const f32x4 pT = quad_transpose(pv, x4);
-    const f32x4 aT = quad_transpose(av, x4);
-    const int trow = 16 * R + 4 * g + x4;  // row held after the transpose
-    const int col = perm_col(16 * C + 4 * m4);
-    put_split4(bf.Ph, bf.Pl, tp_off(trow, col), pT);
-    if (b == 0) *reinterpret_cast<f32x4*>(&ps.Aown[(4 * g + x4) * kSS + 4 * m4]) = aT;
-    if ((R & 1) != 0 && C == R - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[(4 * g + x4) * kSS + 4 * m4]) = aT;
-    if (R >= 2 && C < 2) put_split4(bf.Th, bf.Tl, tp_off(trow, col), -aT);  // -A21
+    const int col = perm_col(16 * C + 4 * g);
+    put_split4(bf.Ph, bf.Pl, tp_off(t, col), pv);
+    if (b == 0) *reinterpret_cast<f32x4*>(&ps.Aown[l16 * kSS + 4 * g]) = av;
+    if ((R & 1) != 0 && C == R - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[l16 * kSS + 4 * g]) = av;
+    if (R >= 2 && C < 2) put_split4(bf.Th, bf.Tl, tp_off(t, col), -av);  // -A21
   }
   // diagonal inverse of this wave's block (reads this wave's own scratch writes)
   invert16(ps.Aown, ps.Town, lane);
@@ -431,12 +397,14 @@ __device__ __forceinline__ void producer_offdiag(ChunkBuf<K, VT>& bf, const Prod
   s4 th, tl, yh, yl;
   split4(lds_f4(&ps.Town[l16 * kSS + 4 * g]), th, tl);
   split4(y, yh, yl);
-  f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  z = mfma16x16x16(th, yh, z);
-  z = mfma16x16x16(th, yl, z);
-  z = mfma16x16x16(tl, yh, z);
-  const f32x4 zT = quad_transpose(-z, l16 & 3);
-  put_split4(bf.Th, bf.Tl, tp_off(16 * P + 4 * g + (l16 & 3), perm_col(16 * (P - 1) + 4 * (l16 >> 2))), zT);
+  // (T_PP Y)^T = Y^T T_PP^T: Y's accumulator layout is exactly the A operand
+  // of the transposed product, and its result gives a lane row l16 and four
+  // consecutive columns 4 g .. 4 g + 3 of T_{P,P-1}, one 8-byte piece.
+  f32x4 zt = {0.f, 0.f, 0.f, 0.f};
+  zt = mfma16x16x16(yh, th, zt);
+  zt = mfma16x16x16(yl, th, zt);
+  zt = mfma16x16x16(yh, tl, zt);
+  put_split4(bf.Th, bf.Tl, tp_off(16 * P + l16, perm_col(16 * (P - 1) + 4 * g)), -zt);
 }
 
 // ---- kernel -------------------------------------------------------------------------------
