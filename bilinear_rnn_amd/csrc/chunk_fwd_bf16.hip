@@ -123,6 +123,7 @@ struct alignas(16) SmemV3 {
   ChunkBuf<K, VT> buf[2];
   ProdScratch ps[4];
   int prod_bar;
+  int pair_flag[2];
 };
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -288,6 +289,90 @@ __device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* 
   put_split4(bf.Th, bf.Tl, tp_off(row0 + r, perm_col(col0 + 4 * cg)), lds_f4(Tb + r * kSS + 4 * cg));
 }
 
+// Scale one transposed block (see producer_blocks) into P and A and write
+// them: this lane holds row t = 16 R + l16, columns s = 16 C + 4 g + i.
+// B = 0 is the wave's diagonal block; B >= 1 an off-diagonal one whose decay
+// factors are in the wave's tables (slot B - 1).
+template <int B, int R, int C, int K, int VT>
+__device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
+                                            const f32x4& qk, const f32x4& kk4) {
+  const int g = lane >> 4, l16 = lane & 15;
+  const int t = 16 * R + l16;
+  f32x4 av, pv;
+  if constexpr (B == 0) {
+    // diagonal block: masks and one exp per element (both tokens in one block)
+    const float Gt = ps.dG[t], bt = ps.dB[t], rt = ps.dR[t];
+    const f32x4 Gs = lds_f4(&ps.dG[16 * C + 4 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s_ = 16 * C + 4 * g + i;
+      const float M = __expf(fminf(Gt - Gs[i], 0.f));  // exp(G_t - G_s) for s <= t
+      const float kk = kk4[i];
+      av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+      pv[i] = (s_ <= t) ? (qk[i] - dh * kk) * M : 0.f;
+    }
+  } else {
+    const float ta = ps.oA[B - 1][t], tp = ps.oP[B - 1][t];
+    const f32x4 ts = lds_f4(&ps.oS[B - 1][16 * C + 4 * g]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float kk = kk4[i] * ts[i];
+      av[i] = ta * kk;
+      pv[i] = (qk[i] * ts[i] - dh * kk) * tp;
+    }
+  }
+  const int col = perm_col(16 * C + 4 * g);
+  put_split4(bf.Ph, bf.Pl, tp_off(t, col), pv);
+  if constexpr (B == 0) *reinterpret_cast<f32x4*>(&ps.Aown[l16 * kSS + 4 * g]) = av;
+  if constexpr ((R & 1) != 0 && C == R - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[l16 * kSS + 4 * g]) = av;
+  if constexpr (R >= 2 && C < 2) put_split4(bf.Th, bf.Tl, tp_off(t, col), -av);  // -A21
+}
+
+// One-way hand-over between two producer waves through an LDS flag that
+// holds the index (plus one) of the last chunk whose data is ready.
+__device__ __forceinline__ void pair_signal(int* flag, int tag, int lane) {
+  if (lane == 0) __hip_atomic_store(flag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void pair_wait(const int* flag, int tag) {
+  while (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < tag)
+    __builtin_amdgcn_s_sleep(1);
+}
+
+// T_{D,D-1} = -T_DD A_{D,D-1} T_{D-1,D-1} for odd D. The first product uses
+// only this wave's data and runs before waiting for the even neighbour's
+// T_{D-1,D-1}. Both are formed transposed: W^T = A^T T_DD^T leaves W^T in the
+// layout of a B operand, and (W T_{D-1,D-1})^T = T_{D-1,D-1}^T W^T gives a
+// lane row l16 and columns 4 g .. 4 g + 3 of the result, one 8-byte piece.
+template <int D, int K, int VT>
+__device__ __forceinline__ void offdiag_inverse(ChunkBuf<K, VT>& bf, const ProdScratch& ps,
+                                                const ProdScratch& prev, const int* pair_flag, int tag,
+                                                int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+  f32x4 acol;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acol[j] = ps.Aoff[(4 * g + j) * kSS + l16];
+  s4 ah, al, th, tl;
+  split4(acol, ah, al);
+  split4(lds_f4(&ps.Town[l16 * kSS + 4 * g]), th, tl);
+  f32x4 wt = {0.f, 0.f, 0.f, 0.f};
+  wt = mfma16x16x16(ah, th, wt);
+  wt = mfma16x16x16(ah, tl, wt);
+  wt = mfma16x16x16(al, th, wt);
+  s4 wh, wl;
+  split4(wt, wh, wl);
+  pair_wait(pair_flag, tag);
+  f32x4 pcol;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pcol[j] = prev.Town[(4 * g + j) * kSS + l16];
+  s4 ph, pl;
+  split4(pcol, ph, pl);
+  f32x4 r = {0.f, 0.f, 0.f, 0.f};
+  r = mfma16x16x16(ph, wh, r);
+  r = mfma16x16x16(ph, wl, r);
+  r = mfma16x16x16(pl, wh, r);
+  put_split4(bf.Th, bf.Tl, tp_off(16 * D + l16, perm_col(16 * (D - 1) + 4 * g)), -r);
+}
+
 // One producer's share of the chunk's ten lower-triangular 16x16 blocks
 // (row block R, column block C <= R): its diagonal block (D, D) first, then up
 // to two more, (R1, C1) and (R2, C2). The shares are balanced so that no wave
@@ -301,7 +386,8 @@ __device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* 
 // A_{R,R-1} (odd R) to the scratch for the off-diagonal step; the A blocks
 // below the 32x32 diagonal enter T's storage negated (-A21).
 template <int D, int NB, int R1, int C1, int R2, int C2, int K, int VT>
-__device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
+__device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, const ProdScratch& prev,
+                                                int* pair_flag, int chunk_tag, int lane, float dh,
                                                 float G, float lg, float rinv, float be) {
   constexpr int Rb[3] = {D, R1, R2};
   constexpr int Cb[3] = {D, C1, C2};
@@ -340,71 +426,20 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
       akk[b] = mfma16x16x32(bk, ak, akk[b]);
     }
   }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int R = Rb[b], C = Cb[b];
-    const int t = 16 * R + l16;  // row of this lane; columns s = 16 C + 4 g + i
-    f32x4 av, pv;
-    if (b == 0) {
-      // diagonal block: masks and one exp per element (both tokens in one block)
-      const float Gt = ps.dG[t], bt = ps.dB[t], rt = ps.dR[t];
-      const f32x4 Gs = lds_f4(&ps.dG[16 * C + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s_ = 16 * C + 4 * g + i;
-        const float M = __expf(fminf(Gt - Gs[i], 0.f));  // exp(G_t - G_s) for s <= t
-        const float kk = akk[b][i];
-        av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
-        pv[i] = (s_ <= t) ? (aqk[b][i] - dh * kk) * M : 0.f;
-      }
-    } else {
-      const float ta = ps.oA[b - 1][t], tp = ps.oP[b - 1][t];
-      const f32x4 ts = lds_f4(&ps.oS[b - 1][16 * C + 4 * g]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float kk = akk[b][i] * ts[i];
-        av[i] = ta * kk;
-        pv[i] = (aqk[b][i] * ts[i] - dh * kk) * tp;
-      }
-    }
-    const int col = perm_col(16 * C + 4 * g);
-    put_split4(bf.Ph, bf.Pl, tp_off(t, col), pv);
-    if (b == 0) *reinterpret_cast<f32x4*>(&ps.Aown[l16 * kSS + 4 * g]) = av;
-    if ((R & 1) != 0 && C == R - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[l16 * kSS + 4 * g]) = av;
-    if (R >= 2 && C < 2) put_split4(bf.Th, bf.Tl, tp_off(t, col), -av);  // -A21
-  }
+  scale_block<0, D, D>(bf, ps, lane, dh, aqk[0], akk[0]);
+  if constexpr ((D & 1) != 0) scale_block<1, R1, C1>(bf, ps, lane, dh, aqk[1], akk[1]);  // A_{D,D-1}
   // diagonal inverse of this wave's block (reads this wave's own scratch writes)
   invert16(ps.Aown, ps.Town, lane);
   store_t_block(bf, ps.Town, 16 * D, 16 * D, lane);
-}
-
-// T_{P,P-1} = -T_PP A_{P,P-1} T_{P-1,P-1} for odd P, after the even producer's
-// diagonal inverse is visible.
-template <int P, int K, int VT>
-__device__ __forceinline__ void producer_offdiag(ChunkBuf<K, VT>& bf, const ProdScratch& ps,
-                                                 const ProdScratch& prev, int lane) {
-  const int g = lane >> 4, l16 = lane & 15;
-  s4 ah, al, bh, bl;
-  split4(lds_f4(&ps.Aoff[l16 * kSS + 4 * g]), ah, al);
-  f32x4 tv;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) tv[j] = prev.Town[(4 * g + j) * kSS + l16];
-  split4(tv, bh, bl);
-  f32x4 y = {0.f, 0.f, 0.f, 0.f};
-  y = mfma16x16x16(ah, bh, y);
-  y = mfma16x16x16(ah, bl, y);
-  y = mfma16x16x16(al, bh, y);
-  s4 th, tl, yh, yl;
-  split4(lds_f4(&ps.Town[l16 * kSS + 4 * g]), th, tl);
-  split4(y, yh, yl);
-  // (T_PP Y)^T = Y^T T_PP^T: Y's accumulator layout is exactly the A operand
-  // of the transposed product, and its result gives a lane row l16 and four
-  // consecutive columns 4 g .. 4 g + 3 of T_{P,P-1}, one 8-byte piece.
-  f32x4 zt = {0.f, 0.f, 0.f, 0.f};
-  zt = mfma16x16x16(yh, th, zt);
-  zt = mfma16x16x16(yl, th, zt);
-  zt = mfma16x16x16(yh, tl, zt);
-  put_split4(bf.Th, bf.Tl, tp_off(16 * P + l16, perm_col(16 * (P - 1) + 4 * g)), -zt);
+  if constexpr ((D & 1) == 0) {
+    // T_DD is what the odd neighbour waits for: signal it before the rest.
+    pair_signal(pair_flag, chunk_tag, lane);
+    if constexpr (NB > 1) scale_block<1, R1, C1>(bf, ps, lane, dh, aqk[1], akk[1]);
+    if constexpr (NB > 2) scale_block<2, R2, C2>(bf, ps, lane, dh, aqk[2], akk[2]);
+  } else {
+    static_assert(NB == 2 && R1 == D && C1 == D - 1, "odd waves hold (D, D) and (D, D-1)");
+    offdiag_inverse<D>(bf, ps, prev, pair_flag, chunk_tag, lane);
+  }
 }
 
 // ---- kernel -------------------------------------------------------------------------------
@@ -448,7 +483,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
       sm.buf[bb].Pl[e] = 0;
     }
   }
-  if (tid == 0) sm.prod_bar = 0;
+  if (tid == 0) {
+    sm.prod_bar = 0;
+    sm.pair_flag[0] = 0;
+    sm.pair_flag[1] = 0;
+  }
   __syncthreads();
 
   if (wave >= 4) {
@@ -553,15 +592,15 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           bf.gl[3][gp] = __expf(Gn - G);
           if (lane == 63) bf.eGn = __expf(G);
         }
+        // Waves 0 / 1 and 2 / 3 form pairs: the even wave hands its diagonal
+        // inverse to the odd one through pair_flag[p / 2].
+        const int tag = it + 1;
         switch (p) {
-          case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], olane, dh, G, lg, rinv, be); break;
-          case 1: producer_blocks<1, 2, 1, 0, 0, 0>(bf, sm.ps[1], olane, dh, G, lg, rinv, be); break;
-          case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], olane, dh, G, lg, rinv, be); break;
-          default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], olane, dh, G, lg, rinv, be); break;
+          case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be); break;
+          case 1: producer_blocks<1, 2, 1, 0, 0, 0>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be); break;
+          case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be); break;
+          default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be); break;
         }
-        producer_sync(&sm.prod_bar, epoch, lane);  // diagonal inverses visible
-        if (p == 1) producer_offdiag<1>(bf, sm.ps[1], sm.ps[0], olane);
-        if (p == 3) producer_offdiag<3>(bf, sm.ps[3], sm.ps[2], olane);
       }
       __syncthreads();
     }
