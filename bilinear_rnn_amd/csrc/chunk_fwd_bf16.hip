@@ -628,21 +628,64 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         const int nrows = min(64, t1 - c0);
         const int64_t obase = ((static_cast<int64_t>(b) * T + c0) * H + h) * V;  // row c0, head h
 
-        bf16x8 hbh[K / 32], hbl[K / 32];
-#pragma unroll
-        for (int s = 0; s < K / 32; ++s) split_pair(hs[2 * s], hs[2 * s + 1], hbh[s], hbl[s]);
+        // The body is software-pipelined by hand: every stage issues the LDS
+        // reads of the next one before its own matrix products, and
+        // scheduling barriers keep that order, so the products rarely wait on
+        // LDS latency.
+        constexpr int NS = K / 32;  // 32-wide reduction steps over the key dimension
+        auto kfrag = [&](int r4, int s_) { return lds8(&bf.Kc[swz<K>(16 * r4 + l16, 32 * s_ + 8 * g)]); };
+        auto qfrag = [&](int r4, int s_) { return lds8(&bf.Q[swz<K>(16 * r4 + l16, 32 * s_ + 8 * g)]); };
 
-        // K h (needed first), then R
-        f32x4 KH[4];
+        bf16x8 hbh[NS], hbl[NS];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          KH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s_ = 0; s_ < NS; ++s_) split_pair(hs[2 * s_], hs[2 * s_ + 1], hbh[s_], hbl[s_]);
+
+        // ---- stage A: K h and Q h, in steps of two reduction slices of one row block
+        constexpr int NSTEP = 4 * NS / 2;
+        bf16x8 fk[2], fq[2];
+        fk[0] = kfrag(0, 0);
+        fk[1] = kfrag(0, 1);
+        fq[0] = qfrag(0, 0);
+        fq[1] = qfrag(0, 1);
+        f32x4 KH[4], QH[4];
 #pragma unroll
-          for (int s = 0; s < K / 32; ++s) {
-            const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * r4 + l16, 32 * s + 8 * g)]);
-            KH[r4] = mfma16x16x32(ak, hbh[s], KH[r4]);
-            KH[r4] = mfma16x16x32(ak, hbl[s], KH[r4]);
+        for (int j = 0; j < NSTEP; ++j) {
+          const int r4 = j / (NS / 2), s0 = 2 * (j % (NS / 2));
+          bf16x8 nk[2], nq[2];
+          if (j + 1 < NSTEP) {
+            const int r4n = (j + 1) / (NS / 2), s0n = 2 * ((j + 1) % (NS / 2));
+            nk[0] = kfrag(r4n, s0n);
+            nk[1] = kfrag(r4n, s0n + 1);
+            nq[0] = qfrag(r4n, s0n);
+            nq[1] = qfrag(r4n, s0n + 1);
           }
+          __builtin_amdgcn_sched_barrier(0);
+          if (s0 == 0) {
+            KH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            QH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            KH[r4] = mfma16x16x32(fk[u], hbh[s0 + u], KH[r4]);
+            KH[r4] = mfma16x16x32(fk[u], hbl[s0 + u], KH[r4]);
+            QH[r4] = mfma16x16x32(fq[u], hbh[s0 + u], QH[r4]);
+            QH[r4] = mfma16x16x32(fq[u], hbl[s0 + u], QH[r4]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (j + 1 < NSTEP) {
+            fk[0] = nk[0];
+            fk[1] = nk[1];
+            fq[0] = nq[0];
+            fq[1] = nq[1];
+          }
+        }
+
+        // ---- stage B: R, then Ubar_top = T1 R_top (T1 read before R is formed)
+        bf16x8 t1h[2], t1l[2];
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          t1h[r4] = lds8(&bf.Th[tp_off(16 * r4 + l16, 8 * g)]);
+          t1l[r4] = lds8(&bf.Tl[tp_off(16 * r4 + l16, 8 * g)]);
         }
         f32x4 R[4];
 #pragma unroll
@@ -653,60 +696,71 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) R[r4][i] = bt[i] * vv[i] - bx[i] * KH[r4][i];
         }
-
-        // Q h (independent of the solve below)
-        f32x4 QH[4];
+        // A21 and T2 for stage C
+        bf16x8 a2h[2], a2l[2], t2h[2], t2l[2];
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          QH[r4] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s = 0; s < K / 32; ++s) {
-            const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * r4 + l16, 32 * s + 8 * g)]);
-            QH[r4] = mfma16x16x32(aq, hbh[s], QH[r4]);
-            QH[r4] = mfma16x16x32(aq, hbl[s], QH[r4]);
-          }
+        for (int r = 0; r < 2; ++r) {
+          const int row = 32 + 16 * r + l16;
+          a2h[r] = lds8(&bf.Th[tp_off(row, 8 * g)]);
+          a2l[r] = lds8(&bf.Tl[tp_off(row, 8 * g)]);
+          t2h[r] = lds8(&bf.Th[tp_off(row, 32 + 8 * g)]);
+          t2l[r] = lds8(&bf.Tl[tp_off(row, 32 + 8 * g)]);
         }
-
-        // Ubar_top = T1 R_top
+        __builtin_amdgcn_sched_barrier(0);
         bf16x8 rbh, rbl;
         split_pair(R[0], R[1], rbh, rbl);
         f32x4 U[4];
 #pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-          const int off = tp_off(16 * r4 + l16, 8 * g);
-          U[r4] = mma3(lds8(&bf.Th[off]), lds8(&bf.Tl[off]), rbh, rbl, f32x4{0.f, 0.f, 0.f, 0.f});
-        }
+        for (int r4 = 0; r4 < 2; ++r4) U[r4] = mma3(t1h[r4], t1l[r4], rbh, rbl, f32x4{0.f, 0.f, 0.f, 0.f});
         bf16x8 ubh0, ubl0;
         split_pair(U[0], U[1], ubh0, ubl0);
-        // Y = R_bot - A21 Ubar_top ; Ubar_bot = T2 Y
+
+        // ---- stage C: Y = R_bot - A21 Ubar_top ; Ubar_bot = T2 Y (P rows 0-31 read meanwhile)
+        bf16x8 p0h[2], p0l[2];
+#pragma unroll
+        for (int r4 = 0; r4 < 2; ++r4) {
+          p0h[r4] = lds8(&bf.Ph[tp_off(16 * r4 + l16, 8 * g)]);
+          p0l[r4] = lds8(&bf.Pl[tp_off(16 * r4 + l16, 8 * g)]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 Y[2];
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int off = tp_off(32 + 16 * r + l16, 8 * g);
-          Y[r] = mma3(lds8(&bf.Th[off]), lds8(&bf.Tl[off]), ubh0, ubl0, R[2 + r]);
-        }
+        for (int r = 0; r < 2; ++r) Y[r] = mma3(a2h[r], a2l[r], ubh0, ubl0, R[2 + r]);
         bf16x8 ybh, ybl;
         split_pair(Y[0], Y[1], ybh, ybl);
+        // P rows 32-63 for stage D
+        bf16x8 p1h[2][2], p1l[2][2];
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
-          const int off = tp_off(32 + 16 * r + l16, 32 + 8 * g);
-          U[2 + r] = mma3(lds8(&bf.Th[off]), lds8(&bf.Tl[off]), ybh, ybl, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            p1h[r][hf] = lds8(&bf.Ph[tp_off(32 + 16 * r + l16, 32 * hf + 8 * g)]);
+            p1l[r][hf] = lds8(&bf.Pl[tp_off(32 + 16 * r + l16, 32 * hf + 8 * g)]);
+          }
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = 0; r < 2; ++r) U[2 + r] = mma3(t2h[r], t2l[r], ybh, ybl, f32x4{0.f, 0.f, 0.f, 0.f});
         bf16x8 ubh1, ubl1;
         split_pair(U[2], U[3], ubh1, ubl1);
 
-        // O = e^G (Q h - d K h) + P Ubar
+        // ---- stage D: O = e^G (Q h - d K h) + P Ubar, stored straight from the
+        // accumulator layout (K^T fragments of the first key block read meanwhile)
+        bf16x8 kt0[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) kt0[s2] = kt_frag<K>(bf.Kc, 0, s2, g, l16);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 eg = lds_f4(&bf.gl[2][16 * g + 4 * r4]);
           f32x4 acc;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] = eg[i] * (QH[r4][i] - dh * KH[r4][i]);
-          const int off0 = tp_off(16 * r4 + l16, 8 * g);
-          acc = mma3(lds8(&bf.Ph[off0]), lds8(&bf.Pl[off0]), ubh0, ubl0, acc);
-          if (r4 >= 2) {
-            const int off1 = tp_off(16 * r4 + l16, 32 + 8 * g);
-            acc = mma3(lds8(&bf.Ph[off1]), lds8(&bf.Pl[off1]), ubh1, ubl1, acc);
+          if (r4 < 2) {
+            acc = mma3(p0h[r4], p0l[r4], ubh0, ubl0, acc);
+          } else {
+            acc = mma3(p1h[r4 - 2][0], p1l[r4 - 2][0], ubh0, ubl0, acc);
+            acc = mma3(p1h[r4 - 2][1], p1l[r4 - 2][1], ubh1, ubl1, acc);
           }
           // Stored straight from the accumulator layout: this lane holds rows
           // 16 r4 + 4 g + i of its wavefront's channel l16; the 16 lanes of a
@@ -732,7 +786,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           }
         }
 
-        // h' = e^Gn h + K^T diag(e^(Gn - G)) Ubar
+        // ---- stage E: h' = e^Gn h + K^T diag(e^(Gn - G)) Ubar, K^T fragments
+        // double-buffered by key block
         bf16x8 ush[2], usl[2];
         {
           f32x4 Us[4];
@@ -746,14 +801,25 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           split_pair(Us[2], Us[3], ush[1], usl[1]);
         }
         const float eGn = bf.eGn;
+        bf16x8 ktc[2] = {kt0[0], kt0[1]};
 #pragma unroll
         for (int kb = 0; kb < K / 16; ++kb) {
+          bf16x8 ktn[2];
+          if (kb + 1 < K / 16) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) ktn[s2] = kt_frag<K>(bf.Kc, kb + 1, s2, g, l16);
+          }
+          __builtin_amdgcn_sched_barrier(0);
           hs[kb] *= eGn;
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const bf16x8 a = kt_frag<K>(bf.Kc, kb, s2, g, l16);
-            hs[kb] = mfma16x16x32(a, ush[s2], hs[kb]);
-            hs[kb] = mfma16x16x32(a, usl[s2], hs[kb]);
+            hs[kb] = mfma16x16x32(ktc[s2], ush[s2], hs[kb]);
+            hs[kb] = mfma16x16x32(ktc[s2], usl[s2], hs[kb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (kb + 1 < K / 16) {
+            ktc[0] = ktn[0];
+            ktc[1] = ktn[1];
           }
         }
       }
