@@ -4,10 +4,12 @@
 //   a = S[i,:] . k,  b = S[i,:] . qt,  qt = q - d k,  u = v_i - a
 //   S'[i,:] = alpha S[i,:] + beta u k^T,   o_i = alpha b + beta u (k . qt)
 // One read and one write of the fp32 state per token range: the kernel is
-// bound by HBM bandwidth. Each state row (K floats) is spread over K/4 lanes
-// holding 4 contiguous floats (one 16-byte access per lane), so a wavefront
-// reads whole 512-byte rows; the two K-reductions per row are butterfly
-// shuffles inside those lanes. The state stays in registers across tokens.
+// bound by HBM bandwidth. A state row (K floats) is spread over the 16 lanes
+// of one DPP row, each holding K/16 floats as 16-byte pieces at columns
+// 4 j + 64 f (lane j of the row, piece f): every load instruction reads
+// 256 contiguous bytes of four rows. The two K-reductions per row are four
+// DPP steps inside those 16 lanes (no LDS traffic). The state stays in
+// registers across tokens.
 #include "device_common.h"
 #include "launch.h"
 #include "comba.h"
@@ -31,78 +33,105 @@ template <> struct Load4<u16> {
   }
 };
 
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = LPR / 2; m > 0; m >>= 1) x += __shfl_xor(x, m, LPR);
+// x summed over the 16 lanes of each DPP row, result in all 16 lanes:
+// swap neighbours, swap pairs, mirror the 8-lane halves, mirror the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));
   return x;
 }
 
-template <int K, int V, typename InT, typename OutT>
+// One workgroup per (sequence, head, block of VB value rows).
+template <int K, int V, int VB, typename InT, typename OutT>
 __global__ __launch_bounds__(256) void recurrent_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* s0, const int32_t* __restrict__ cu_seqlens, int T, int H,
     OutT* __restrict__ o, float* sf) {
-  constexpr int LPR = K / 4;        // lanes per state row
-  constexpr int RPW = kWave / LPR;  // rows per wavefront
-  constexpr int RPP = RPW * 4;      // rows per pass of the 4 wavefronts
-  constexpr int NP = V / RPP;       // passes
-  const int h = blockIdx.x % H;
-  const int n = blockIdx.x / H;
+  constexpr int F4 = K / 64;   // 16-byte pieces per lane and row
+  constexpr int RPP = 16;       // rows per pass: 4 per wavefront
+  constexpr int NP = VB / RPP;  // passes
+  constexpr int NB = V / VB;    // row blocks per (sequence, head)
+  const int vb = blockIdx.x % NB;
+  const int h = (blockIdx.x / NB) % H;
+  const int n = blockIdx.x / (NB * H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int rw = lane / LPR, c4 = lane % LPR;
+  const int rw = lane >> 4, j = lane & 15;
   int b, t0, t1;
   sequence_range(cu_seqlens, n, T, b, t0, t1);
 
-  const int64_t sbase = (static_cast<int64_t>(n) * H + h) * V * K + 4 * c4;
-  f32x4 S[NP];
+  const int64_t sbase = (static_cast<int64_t>(n) * H + h) * V * K + 4 * j;
+  f32x4 S[NP][F4];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const int row = p * RPP + w * RPW + rw;
-    if (s0)
-      S[p] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(s0 + sbase + row * K));
-    else
-      S[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int row = vb * VB + p * RPP + w * 4 + rw;
+#pragma unroll
+    for (int f = 0; f < F4; ++f)
+      S[p][f] = s0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(s0 + sbase + row * K + 64 * f))
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const float dh = d[h];
 
   for (int t = t0; t < t1; ++t) {
     const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
-    float kk[4], qt[4];
-    Load4<InT>::get(k, tok * K + 4 * c4, kk);
-    Load4<InT>::get(q, tok * K + 4 * c4, qt);
+    float kk[F4][4], qt[F4][4];
+    float kq = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) qt[j] -= dh * kk[j];
-    const float kq = group_sum<LPR>(kk[0] * qt[0] + kk[1] * qt[1] + kk[2] * qt[2] + kk[3] * qt[3]);
+    for (int f = 0; f < F4; ++f) {
+      Load4<InT>::get(k, tok * K + 4 * j + 64 * f, kk[f]);
+      Load4<InT>::get(q, tok * K + 4 * j + 64 * f, qt[f]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qt[f][e] -= dh * kk[f][e];
+        kq += kk[f][e] * qt[f][e];
+      }
+    }
+    kq = row16_sum(kq);
     const float a = alpha[tok], be = beta[tok];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int row = p * RPP + w * RPW + rw;
-      float sk = S[p][0] * kk[0] + S[p][1] * kk[1] + S[p][2] * kk[2] + S[p][3] * kk[3];
-      float sq = S[p][0] * qt[0] + S[p][1] * qt[1] + S[p][2] * qt[2] + S[p][3] * qt[3];
-      sk = group_sum<LPR>(sk);
-      sq = group_sum<LPR>(sq);
+      const int row = vb * VB + p * RPP + w * 4 + rw;
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int f = 0; f < F4; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk += S[p][f][e] * kk[f][e];
+          sq += S[p][f][e] * qt[f][e];
+        }
+      sk = row16_sum(sk);
+      sq = row16_sum(sq);
       const float u = Elem<InT>::load(v, tok * V + row) - sk;
       const float bu = be * u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S[p][j] = a * S[p][j] + bu * kk[j];
-      if (c4 == 0) Elem<OutT>::store(o, tok * V + row, a * sq + bu * kq);
+      for (int f = 0; f < F4; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) S[p][f][e] = a * S[p][f][e] + bu * kk[f][e];
+      if (j == 0) Elem<OutT>::store(o, tok * V + row, a * sq + bu * kq);
     }
   }
   if (sf) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      const int row = p * RPP + w * RPW + rw;
-      __builtin_nontemporal_store(S[p], reinterpret_cast<f32x4*>(sf + sbase + row * K));
+      const int row = vb * VB + p * RPP + w * 4 + rw;
+#pragma unroll
+      for (int f = 0; f < F4; ++f)
+        __builtin_nontemporal_store(S[p][f], reinterpret_cast<f32x4*>(sf + sbase + row * K + 64 * f));
     }
   }
 }
 
 template <int K, int V, typename InT, typename OutT>
 static hipError_t launch_rec_t(const FwdArgs& a, hipStream_t st) {
-  const int grid = a.N * a.H;
-  recurrent_kernel<K, V, InT, OutT><<<grid, 256, 0, st>>>(
+  // 32 value rows per workgroup (16 KB of state at K = 128): few enough
+  // registers for eight wavefronts per SIMD and a grid of N H V / 32
+  // workgroups. Measured on the decode workload: 16 rows per workgroup is
+  // slower (more redundant k / q loads), 64 rows too (fewer waves in flight).
+  constexpr int VB = 32;
+  const int grid = a.N * a.H * (V / VB);
+  recurrent_kernel<K, V, VB, InT, OutT><<<grid, 256, 0, st>>>(
       static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v),
       a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.T, a.H, static_cast<OutT*>(a.o), a.sf);
   return hipGetLastError();
