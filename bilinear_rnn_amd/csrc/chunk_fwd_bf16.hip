@@ -111,7 +111,7 @@ struct alignas(16) ProdScratch {  // one per producer wave, fp32 16x16 blocks, r
   float Aoff[16 * kSS];           // A_{p,p-1} (odd p)
   float Town[16 * kSS];           // T_pp
   // Per-token decay factors of this wave's blocks, indexed by token in chunk:
-  // diagonal block: G_t, beta_t, 1/alpha_t; off-diagonal block j (column
+  // diagonal block: G_t (cumulative log2 alpha), beta_t, 1/alpha_t; off-diagonal block j (column
   // block C, last token r = 16 C + 15): beta_t e^(Gx_t - G_r), e^(G_t - G_r)
   // (rows) and e^(G_r - G_s) (columns).
   float dG[64], dB[64], dR[64];
@@ -163,6 +163,9 @@ __device__ __forceinline__ void split4(const f32x4& x, s4& hi, s4& lo) {
   hi = __builtin_bit_cast(s4, (u32x2){h0, h1});
   lo = __builtin_bit_cast(s4, (u32x2){l0, l1});
 }
+
+// 2^x with the hardware instruction (about 1 ulp; x <= 0 here, underflow to 0 is exact enough).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f32x4 mfma16x16x16(s4 a, s4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -306,7 +309,7 @@ __device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s_ = 16 * C + 4 * g + i;
-      const float M = __expf(fminf(Gt - Gs[i], 0.f));  // exp(G_t - G_s) for s <= t
+      const float M = exp2_fast(fminf(Gt - Gs[i], 0.f));  // e^(G_t - G_s) for s <= t
       const float kk = kk4[i];
       av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
       pv[i] = (s_ <= t) ? (qk[i] - dh * kk) * M : 0.f;
@@ -401,9 +404,9 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
 #pragma unroll
   for (int b = 1; b < NB; ++b) {
     const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 16 * Cb[b] + 15));
-    ps.oA[b - 1][lane] = be * __expf(fminf(G - lg - Gr, 0.f));  // beta_t e^(Gx_t - G_r), t > r
-    ps.oP[b - 1][lane] = __expf(fminf(G - Gr, 0.f));            // e^(G_t - G_r), t > r
-    ps.oS[b - 1][lane] = __expf(fminf(Gr - G, 0.f));            // e^(G_r - G_s), s <= r
+    ps.oA[b - 1][lane] = be * exp2_fast(fminf(G - lg - Gr, 0.f));  // beta_t e^(Gx_t - G_r), t > r
+    ps.oP[b - 1][lane] = exp2_fast(fminf(G - Gr, 0.f));            // e^(G_t - G_r), t > r
+    ps.oS[b - 1][lane] = exp2_fast(fminf(Gr - G, 0.f));            // e^(G_r - G_s), s <= r
   }
   // Each block is formed transposed, K_C Q_R^T and K_C K_R^T (K K^T is
   // symmetric): the accumulator then gives a lane one row t = 16 R + l16 and
@@ -580,17 +583,20 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 
         // decays: every producer wave computes all 64 rows (lane = row)
         const float a = bf.raw_a[lane], be = bf.raw_b[lane];
-        const float lg = __logf(a);
+        // Decays in base 2: G (and lg, Gn) hold cumulative log2(alpha), so
+        // every decay factor is one v_exp_f32. alpha is clamped to the
+        // smallest normal float so that the hardware log stays finite.
+        const float lg = __builtin_amdgcn_logf(fmaxf(a, 1.17549435e-38f));
         const float G = wave_scan_dpp(lg);
-        const float rinv = 1.f / a;
+        const float rinv = __builtin_amdgcn_rcpf(a);
         if (p == 0) {
           const float Gn = __shfl(G, 63, kWave);
           const int gp = gate_pos(lane);
           bf.gl[0][gp] = be;
-          bf.gl[1][gp] = be * __expf(G - lg);
-          bf.gl[2][gp] = __expf(G);
-          bf.gl[3][gp] = __expf(Gn - G);
-          if (lane == 63) bf.eGn = __expf(G);
+          bf.gl[1][gp] = be * exp2_fast(G - lg);
+          bf.gl[2][gp] = exp2_fast(G);
+          bf.gl[3][gp] = exp2_fast(Gn - G);
+          if (lane == 63) bf.eGn = exp2_fast(G);
         }
         // Waves 0 / 1 and 2 / 3 form pairs: the even wave hands its diagonal
         // inverse to the odd one through pair_flag[p / 2].
