@@ -248,20 +248,26 @@ __device__ __forceinline__ f32x4 v_frag(const u16* Vv, int r4, int col0, int g, 
 
 // ---- producer pieces ---------------------------------------------------------------------
 
-// (I + A)^-1 of a 16x16 block whose strictly lower part is in Ab (fp32,
-// row-major, zeros on and above the diagonal): forward substitution by
+// (I + A)^-1 of a 16x16 diagonal block whose strictly lower part is in Ab
+// (fp32, row-major, zeros on and above the diagonal): forward substitution by
 // columns, four lanes per column (lane = 4c + q holds rows 4q..4q+3 of
-// column c), the pivot broadcast inside each lane quad with DPP.
-__device__ __forceinline__ void invert16(const float* Ab, float* Tb, int lane) {
+// column c), the pivot broadcast inside each lane quad with DPP. All of A is
+// read before the substitution starts, so the chain waits on LDS once. The
+// result goes to Tb (fp32, for the off-diagonal step) and, split into hi / lo
+// bf16, straight from the registers into the T tile at (row0, row0).
+template <int K, int VT>
+__device__ __forceinline__ void invert16(ChunkBuf<K, VT>& bf, const float* Ab, float* Tb, int row0, int lane) {
   const int c = lane >> 2, q = lane & 3;
+  f32x4 a[4][4];  // [column block j4][row 4q + r]: A[4q + r][4 j4 .. 4 j4 + 3]
+#pragma unroll
+  for (int j4 = 0; j4 < 4; ++j4)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[j4][r] = lds_f4(Ab + (4 * q + r) * kSS + 4 * j4);
   float x[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) x[r] = (4 * q + r == c) ? 1.f : 0.f;
 #pragma unroll
   for (int j4 = 0; j4 < 4; ++j4) {
-    f32x4 a[4];  // rows 4q..4q+3, columns 4 j4 .. 4 j4 + 3
-#pragma unroll
-    for (int r = 0; r < 4; ++r) a[r] = lds_f4(Ab + (4 * q + r) * kSS + 4 * j4);
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int j = 4 * j4 + jj;
@@ -277,20 +283,24 @@ __device__ __forceinline__ void invert16(const float* Ab, float* Tb, int lane) {
       }
       const float xj = __builtin_bit_cast(float, bc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] -= a[r][jj] * xj;  // a[r][jj] = 0 unless 4q + r > j
+      for (int r = 0; r < 4; ++r) x[r] -= a[j4][r][jj] * xj;  // a = 0 unless 4q + r > j
     }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) Tb[(4 * q + r) * kSS + c] = x[r];
+  unsigned h01, l01, h23, l23;
+  split2(x[0], x[1], h01, l01);
+  split2(x[2], x[3], h23, l23);
+  const unsigned hw[4] = {h01, h01 >> 16, h23, h23 >> 16}, lw[4] = {l01, l01 >> 16, l23, l23 >> 16};
+  const int pc = perm_col(row0 + c);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int off = tp_off(row0 + 4 * q + r, pc);
+    bf.Th[off] = static_cast<u16>(hw[r]);
+    bf.Tl[off] = static_cast<u16>(lw[r]);
+  }
 }
 
-// Write a fp32 16x16 row-major block into the buffer's Th/Tl at (row0, col0):
-// lane = 4r + cg writes row r, columns 4cg..4cg+3 (contiguous in perm32 order).
-template <int K, int VT>
-__device__ __forceinline__ void store_t_block(ChunkBuf<K, VT>& bf, const float* Tb, int row0, int col0, int lane) {
-  const int r = lane >> 2, cg = lane & 3;
-  put_split4(bf.Th, bf.Tl, tp_off(row0 + r, perm_col(col0 + 4 * cg)), lds_f4(Tb + r * kSS + 4 * cg));
-}
 
 // Scale one transposed block (see producer_blocks) into P and A and write
 // them: this lane holds row t = 16 R + l16, columns s = 16 C + 4 g + i.
@@ -432,8 +442,7 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
   scale_block<0, D, D>(bf, ps, lane, dh, aqk[0], akk[0]);
   if constexpr ((D & 1) != 0) scale_block<1, R1, C1>(bf, ps, lane, dh, aqk[1], akk[1]);  // A_{D,D-1}
   // diagonal inverse of this wave's block (reads this wave's own scratch writes)
-  invert16(ps.Aown, ps.Town, lane);
-  store_t_block(bf, ps.Town, 16 * D, 16 * D, lane);
+  invert16(bf, ps.Aown, ps.Town, 16 * D, lane);
   if constexpr ((D & 1) == 0) {
     // T_DD is what the odd neighbour waits for: signal it before the rest.
     pair_signal(pair_flag, chunk_tag, lane);
@@ -496,6 +505,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   if (wave >= 4) {
     // ======================= producers: prepare chunk it in iteration it =======================
     const int p = wave - 4;
+    // The producers' chain sets the pace (the consumers wait at the chunk
+    // barrier): when both wavefronts of a SIMD are ready, issue the producer's
+    // instruction first.
+    __builtin_amdgcn_s_setprio(2);
     const int ptid = tid - 256;
     constexpr int KP = K / 8, QPT = 64 * KP / 256, VPR = VT / 8, VPT = 64 * VPR / 256;
     u32x4 rq[QPT], rk[QPT], rv[VPT];
