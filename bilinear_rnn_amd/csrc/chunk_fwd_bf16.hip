@@ -505,10 +505,6 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   if (wave >= 4) {
     // ======================= producers: prepare chunk it in iteration it =======================
     const int p = wave - 4;
-    // The producers' chain sets the pace (the consumers wait at the chunk
-    // barrier): when both wavefronts of a SIMD are ready, issue the producer's
-    // instruction first.
-    __builtin_amdgcn_s_setprio(2);
     const int ptid = tid - 256;
     constexpr int KP = K / 8, QPT = 64 * KP / 256, VPR = VT / 8, VPT = 64 * VPR / 256;
     u32x4 rq[QPT], rk[QPT], rv[VPT];
@@ -613,6 +609,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         }
         // Waves 0 / 1 and 2 / 3 form pairs: the even wave hands its diagonal
         // inverse to the odd one through pair_flag[p / 2].
+        // The block / inverse chain is the latency-critical part of the
+        // producers' work: while it runs, a producer's instruction issues first
+        // when both wavefronts of a SIMD are ready (staging and gates run at
+        // normal priority so that the consumers keep their share).
+        __builtin_amdgcn_s_setprio(2);
         const int tag = it + 1;
         switch (p) {
           case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be); break;
@@ -620,6 +621,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be); break;
           default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be); break;
         }
+        __builtin_amdgcn_s_setprio(0);
       }
       __syncthreads();
     }
