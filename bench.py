@@ -5,7 +5,10 @@ T=4096, K=V=128, bf16 q/k/v/o, fp32 alpha/beta/state, non-zero initial
 state), inputs resident in device memory. The reported value is sequence
 tokens (B*T) per second. The decode step (256 sequences x 16 heads,
 K=V=128, fp32 state updated in place in device memory) is timed in the same
-run and reported in GB/s under "decode". The fp64 CPU oracle is timed on
+run and reported in GB/s under "decode". The same 1.3B-layer forward with
+input-side fusion (raw q/k normalised in the kernel, alpha/beta given as
+logits) is timed under "fused", beside the same preprocessing done by
+separate torch ops before an unfused call. The fp64 CPU oracle is timed on
 the host cores on a bounded sample of the same workload ("cpu_baseline").
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -204,6 +207,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with a plain 256 MiB device copy (counter calibration runs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -298,6 +302,38 @@ def main():
                             "us_per_step": dms * 1e3, "GB/s": dbytes / (dms * 1e-3) / 1e9,
                             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                             "algorithmic_bytes": dbytes, "kernel": "recurrent_kernel<128,128,bf16,bf16>"}
+
+    if not args.no_fused:
+        raw = make_inputs(w, raw=True)
+        tr = device_inputs(raw, torch, dev)
+
+        def fstep(_):
+            comba.chunk_fwd(tr["q"], tr["k"], tr["v"], tr["alpha"], tr["beta"], tr["d"], tr["s0"], out=o,
+                            final_state=sf, gate_logits=True, qk_l2norm=True)
+
+        fms, _ = time_loop(torch, fstep, args.steps, args.warmup)
+        fo = o.float().cpu().numpy()
+        b, h = 3, 6
+        rq, rk, ra, rb = oracle.fused_inputs(raw.q[b:b + 1, :, h:h + 1], raw.k[b:b + 1, :, h:h + 1],
+                                             raw.alpha[b:b + 1, :, h:h + 1], raw.beta[b:b + 1, :, h:h + 1],
+                                             gate_logits=True, qk_l2norm=True)
+        ro, _ = oracle.comba_forward_c(rq, rk, raw.v[b:b + 1, :, h:h + 1], ra, rb, raw.d[h:h + 1],
+                                       raw.s0[b:b + 1, h:h + 1])
+
+        def split_step(_):
+            # the same input steps as separate torch ops (bf16 q/k written back), then the unfused call
+            qn = torch.nn.functional.normalize(tr["q"].float(), dim=-1, eps=1e-3).to(torch.bfloat16)
+            kn = torch.nn.functional.normalize(tr["k"].float(), dim=-1, eps=1e-3).to(torch.bfloat16)
+            comba.chunk_fwd(qn, kn, tr["v"], torch.sigmoid(tr["alpha"]), torch.sigmoid(tr["beta"]), tr["d"],
+                            tr["s0"], out=o, final_state=sf)
+
+        sms, _ = time_loop(torch, split_step, max(args.steps // 4, 10), min(args.warmup, 20))
+        result["fused"] = {"workload": "layer_1p3b, raw q/k and gate logits", "flags": "gate_logits|qk_l2norm",
+                           "us_per_step": fms * 1e3, "tokens/s": B * T / (fms * 1e-3),
+                           "hbm_frac": nbytes / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "torch_preprocess_then_chunk_us": sms * 1e3,
+                           "parity_sampled_o_rel_l2": oracle.rel_l2(fo[b:b + 1, :, h:h + 1], ro)}
+        del tr
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, H)

@@ -24,10 +24,12 @@ COMBA_ERR_WORKSPACE = -3
 COMBA_ERR_HIP = -4
 COMBA_BF16 = 0
 COMBA_FP32 = 1
+COMBA_FUSE_GATE_LOGITS = 1
+COMBA_FUSE_QK_L2NORM = 2
 
 EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
-            "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_recurrent_step",
-            "comba_varlen_order")
+            "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_chunk_fwd_fused",
+            "comba_recurrent_step", "comba_recurrent_step_fused", "comba_varlen_order")
 
 
 class CombaError(RuntimeError):
@@ -60,9 +62,15 @@ def lib() -> ctypes.CDLL:
         L.comba_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
                                       i32, i32, vp, fp, vp, sz, vp]
         L.comba_chunk_fwd.restype = i32
+        L.comba_chunk_fwd_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
+                                            i32, i32, vp, fp, vp, sz, ctypes.c_uint32, vp]
+        L.comba_chunk_fwd_fused.restype = i32
         L.comba_recurrent_step.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
                                            i32, i32, vp, fp, vp]
         L.comba_recurrent_step.restype = i32
+        L.comba_recurrent_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32,
+                                                 i32, i32, i32, vp, fp, ctypes.c_uint32, vp]
+        L.comba_recurrent_step_fused.restype = i32
         L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
         L.comba_varlen_order.restype = i32
         _lib = L
@@ -128,6 +136,10 @@ def _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype):
     return B, T, H, K, V, N, out_dtype
 
 
+def _fusion(gate_logits: bool, qk_l2norm: bool) -> int:
+    return (COMBA_FUSE_GATE_LOGITS if gate_logits else 0) | (COMBA_FUSE_QK_L2NORM if qk_l2norm else 0)
+
+
 def workspace_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0,
                    dtype: torch.dtype = torch.bfloat16) -> int:
     return int(lib().comba_chunk_fwd_workspace_size(B, T, H, K, V, num_seqs, _DT[dtype]))
@@ -138,8 +150,13 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               cu_seqlens: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Chunk-wise forward through ``comba_chunk_fwd``. Returns (o, final_state)."""
+              workspace: Optional[torch.Tensor] = None, gate_logits: bool = False,
+              qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunk-wise forward through ``comba_chunk_fwd``. Returns (o, final_state).
+
+    ``gate_logits``: alpha and beta hold pre-sigmoid logits; ``qk_l2norm``: q
+    and k are L2-normalised per head and token inside the kernel. Either flag
+    routes the call through ``comba_chunk_fwd_fused``."""
     B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     L = lib()
     if out is None:
@@ -152,13 +169,17 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     nws = int(L.comba_chunk_fwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0, _DT[q.dtype]))
     if nws > 0 and (workspace is None or workspace.numel() < nws):
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+    fusion = _fusion(gate_logits, qk_l2norm)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        _check(L.comba_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d),
-                                 _ptr(initial_state), _ptr(cu_seqlens), N if cu_seqlens is not None else 0,
-                                 B, T, H, K, V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state),
-                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                                 ctypes.c_void_p(stream)))
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
+                _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
+                _DT[out_dtype], _ptr(out), _ptr(final_state), _ptr(workspace),
+                0 if workspace is None else workspace.numel())
+        if fusion:
+            _check(L.comba_chunk_fwd_fused(*args, fusion, ctypes.c_void_p(stream)))
+        else:
+            _check(L.comba_chunk_fwd(*args, ctypes.c_void_p(stream)))
     return out, final_state
 
 
@@ -167,10 +188,13 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
                    cu_seqlens: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
                    in_place: bool = False, output_final_state: bool = True,
                    out: Optional[torch.Tensor] = None,
-                   final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                   final_state: Optional[torch.Tensor] = None, gate_logits: bool = False,
+                   qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Token-by-token recurrence through ``comba_recurrent_step`` (T == 1: decode).
 
-    With ``in_place`` the state is updated in ``initial_state`` itself."""
+    With ``in_place`` the state is updated in ``initial_state`` itself.
+    ``gate_logits`` and ``qk_l2norm`` as in ``chunk_fwd`` (through
+    ``comba_recurrent_step_fused``)."""
     B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     L = lib()
     if out is None:
@@ -184,12 +208,16 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
         final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _require(final_state, "final_state", torch.float32, (N, H, V, K))
+    fusion = _fusion(gate_logits, qk_l2norm)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        _check(L.comba_recurrent_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d),
-                                      _ptr(initial_state), _ptr(cu_seqlens),
-                                      N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
-                                      _DT[out_dtype], _ptr(out), _ptr(final_state), ctypes.c_void_p(stream)))
+        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
+                _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
+                _DT[out_dtype], _ptr(out), _ptr(final_state))
+        if fusion:
+            _check(L.comba_recurrent_step_fused(*args, fusion, ctypes.c_void_p(stream)))
+        else:
+            _check(L.comba_recurrent_step(*args, ctypes.c_void_p(stream)))
     return out, final_state
 
 

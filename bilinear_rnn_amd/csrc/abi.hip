@@ -59,7 +59,7 @@ int32_t check_args(const void* q, const void* k, const void* v, const float* alp
       return fail(COMBA_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
   }
   a = comba::FwdArgs{q, k, v, alpha, beta, d, s0, cu, nullptr, static_cast<int>(N), B, T, H, K, V,
-                     in_dtype, out_dtype, o, sf};
+                     in_dtype, out_dtype, o, sf, 0u};
   return COMBA_OK;
 }
 
@@ -96,16 +96,21 @@ COMBA_API size_t comba_chunk_fwd_workspace_size(int32_t B, int32_t T, int32_t H,
   return 0;
 }
 
-COMBA_API int32_t comba_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
-                                  const float* beta, const float* d, const float* initial_state,
-                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
-                                  int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
-                                  void* o, float* final_state, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+namespace {
+
+constexpr uint32_t kKnownFusion = COMBA_FUSE_GATE_LOGITS | COMBA_FUSE_QK_L2NORM;
+
+int32_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                       const float* d, const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                       int32_t out_dtype, void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                       uint32_t fusion, void* stream) {
+  if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
   comba::FwdArgs a;
   int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
                           in_dtype, out_dtype, o, final_state, a);
   if (rc != COMBA_OK) return rc;
+  a.fusion = fusion;
   const size_t need = comba_chunk_fwd_workspace_size(B, T, H, K, V, cu_seqlens ? num_seqs : 0, in_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(COMBA_ERR_WORKSPACE, "workspace is NULL or smaller than comba_chunk_fwd_workspace_size()");
@@ -120,16 +125,58 @@ COMBA_API int32_t comba_chunk_fwd(const void* q, const void* k, const void* v, c
   return launched(comba::launch_chunk_fp32(a, st));
 }
 
+int32_t recurrent_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                       const float* d, const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                       int32_t out_dtype, void* o, float* final_state, uint32_t fusion, void* stream) {
+  if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
+  comba::FwdArgs a;
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
+                          in_dtype, out_dtype, o, final_state, a);
+  if (rc != COMBA_OK) return rc;
+  a.fusion = fusion;
+  return launched(comba::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+COMBA_API int32_t comba_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* d, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                  int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
+                                  void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+                        out_dtype, o, final_state, workspace, workspace_bytes, 0u, stream);
+}
+
+COMBA_API int32_t comba_chunk_fwd_fused(const void* q, const void* k, const void* v, const float* alpha,
+                                        const float* beta, const float* d, const float* initial_state,
+                                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                        int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
+                                        void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                        uint32_t fusion, void* stream) {
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+                        out_dtype, o, final_state, workspace, workspace_bytes, fusion, stream);
+}
+
 COMBA_API int32_t comba_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
                                        const float* beta, const float* d, const float* initial_state,
                                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
                                        int32_t H, int32_t K, int32_t V, int32_t in_dtype,
                                        int32_t out_dtype, void* o, float* final_state, void* stream) {
-  comba::FwdArgs a;
-  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
-                          in_dtype, out_dtype, o, final_state, a);
-  if (rc != COMBA_OK) return rc;
-  return launched(comba::launch_recurrent(a, static_cast<hipStream_t>(stream)));
+  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+                        out_dtype, o, final_state, 0u, stream);
+}
+
+COMBA_API int32_t comba_recurrent_step_fused(const void* q, const void* k, const void* v, const float* alpha,
+                                             const float* beta, const float* d, const float* initial_state,
+                                             const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                             int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                                             int32_t out_dtype, void* o, float* final_state, uint32_t fusion,
+                                             void* stream) {
+  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+                        out_dtype, o, final_state, fusion, stream);
 }
 
 COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,

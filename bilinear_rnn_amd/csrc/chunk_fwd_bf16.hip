@@ -97,8 +97,11 @@ struct alignas(16) ChunkBuf {
   // Th/Tl: rows 0-31 hold T1; rows 32-63 hold -A21 (columns 0-31) and T2
   // (columns 32-63). Ph/Pl: the masked score matrix P. hi / lo bf16 parts.
   u16 Th[kTP], Tl[kTP], Ph[kTP], Pl[kTP];
-  float gl[4][64];  // beta, beta e^Gx, e^G, e^(Gn-G) in gate_pos order
+  // beta, beta e^Gx r_k, e^G r_q, e^(Gn-G) r_k, d e^G r_k in gate_pos order (r_q, r_k:
+  // the per-token L2 factors of q and k when they are normalised in the kernel, else 1)
+  float gl[5][64];
   float raw_a[64], raw_b[64];
+  float rn[2][64];  // r_q, r_k by token (normalisation only)
   float eGn;
 };
 
@@ -111,10 +114,11 @@ struct alignas(16) ProdScratch {  // one per producer wave, fp32 16x16 blocks, r
   float Aoff[16 * kSS];           // A_{p,p-1} (odd p)
   float Town[16 * kSS];           // T_pp
   // Per-token decay factors of this wave's blocks, indexed by token in chunk:
-  // diagonal block: G_t (cumulative log2 alpha), beta_t, 1/alpha_t; off-diagonal block j (column
+  // diagonal block: G_t (cumulative log2 alpha), beta_t, 1/alpha_t and, when q and k are
+  // normalised in the kernel, G_t - log2 r_k(t) (column factor); off-diagonal block j (column
   // block C, last token r = 16 C + 15): beta_t e^(Gx_t - G_r), e^(G_t - G_r)
   // (rows) and e^(G_r - G_s) (columns).
-  float dG[64], dB[64], dR[64];
+  float dG[64], dB[64], dR[64], dGk[64];
   float oA[2][64], oP[2][64], oS[2][64];
 };
 
@@ -166,6 +170,14 @@ __device__ __forceinline__ void split4(const f32x4& x, s4& hi, s4& lo) {
 
 // 2^x with the hardware instruction (about 1 ulp; x <= 0 here, underflow to 0 is exact enough).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// sigmoid(x) = 1 / (1 + e^-x), from e = e^-|x| in (0, 1] so that nothing
+// overflows; hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  const float e = exp2_fast(-fabsf(x) * 1.44269504f);
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  return x >= 0.f ? r : e * r;
+}
 
 __device__ __forceinline__ f32x4 mfma16x16x16(s4 a, s4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
@@ -306,32 +318,48 @@ __device__ __forceinline__ void invert16(ChunkBuf<K, VT>& bf, const float* Ab, f
 // them: this lane holds row t = 16 R + l16, columns s = 16 C + 4 g + i.
 // B = 0 is the wave's diagonal block; B >= 1 an off-diagonal one whose decay
 // factors are in the wave's tables (slot B - 1).
-template <int B, int R, int C, int K, int VT>
+template <int B, int R, int C, bool NORM, int K, int VT>
 __device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
                                             const f32x4& qk, const f32x4& kk4) {
   const int g = lane >> 4, l16 = lane & 15;
   const int t = 16 * R + l16;
   f32x4 av, pv;
   if constexpr (B == 0) {
-    // diagonal block: masks and one exp per element (both tokens in one block)
-    const float Gt = ps.dG[t], bt = ps.dB[t], rt = ps.dR[t];
-    const f32x4 Gs = lds_f4(&ps.dG[16 * C + 4 * g]);
+    // diagonal block: masks and one exp per element (both tokens in one block).
+    // With normalisation the column factor r_k(s) rides in the exponent
+    // (G_s - log2 r_k(s)) and the row factors in per-row constants; the clamp
+    // only matters for the masked entries s > t.
+    const float Gt = ps.dG[t];
+    const f32x4 Gs = lds_f4(&(NORM ? ps.dGk : ps.dG)[16 * C + 4 * g]);
+    float ca = ps.dB[t] * ps.dR[t], cq = 1.f, ck = dh;  // beta_t / alpha_t, then r_k(t), r_q(t), d r_k(t)
+    if constexpr (NORM) {
+      const float rqt = bf.rn[0][t], rkt = bf.rn[1][t];
+      ca *= rkt;
+      cq = rqt;
+      ck = dh * rkt;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s_ = 16 * C + 4 * g + i;
-      const float M = exp2_fast(fminf(Gt - Gs[i], 0.f));  // e^(G_t - G_s) for s <= t
+      const float M = exp2_fast(fminf(Gt - Gs[i], NORM ? 64.f : 0.f));  // e^(G_t - G_s) [r_k(s)], s <= t
       const float kk = kk4[i];
-      av[i] = (s_ < t) ? bt * (M * rt) * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
-      pv[i] = (s_ <= t) ? (qk[i] - dh * kk) * M : 0.f;
+      av[i] = (s_ < t) ? ca * M * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+      pv[i] = (s_ <= t) ? (NORM ? qk[i] * cq - ck * kk : qk[i] - dh * kk) * M : 0.f;
     }
   } else {
+    // ta and ts carry r_k(t) and r_k(s) when q and k are normalised
     const float ta = ps.oA[B - 1][t], tp = ps.oP[B - 1][t];
     const f32x4 ts = lds_f4(&ps.oS[B - 1][16 * C + 4 * g]);
+    float cq = tp, ck = dh * tp;  // e^(G_t - G_r) [r_q(t)], d e^(G_t - G_r) [r_k(t)]
+    if constexpr (NORM) {
+      cq *= bf.rn[0][t];
+      ck *= bf.rn[1][t];
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float kk = kk4[i] * ts[i];
       av[i] = ta * kk;
-      pv[i] = (qk[i] * ts[i] - dh * kk) * tp;
+      pv[i] = qk[i] * ts[i] * cq - kk * ck;
     }
   }
   const int col = perm_col(16 * C + 4 * g);
@@ -398,25 +426,26 @@ __device__ __forceinline__ void offdiag_inverse(ChunkBuf<K, VT>& bf, const ProdS
 // written as hi / lo bf16. A_DD goes to the wave's scratch for its inverse;
 // A_{R,R-1} (odd R) to the scratch for the off-diagonal step; the A blocks
 // below the 32x32 diagonal enter T's storage negated (-A21).
-template <int D, int NB, int R1, int C1, int R2, int C2, int K, int VT>
+template <int D, int NB, int R1, int C1, int R2, int C2, bool NORM, int K, int VT>
 __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, const ProdScratch& prev,
                                                 int* pair_flag, int chunk_tag, int lane, float dh,
-                                                float G, float lg, float rinv, float be) {
+                                                float G, float lg, float rinv, float be, float rk) {
   constexpr int Rb[3] = {D, R1, R2};
   constexpr int Cb[3] = {D, C1, C2};
-  const int g = lane >> 4, l16 = lane & 15, m4 = l16 >> 2, x4 = l16 & 3;
+  const int g = lane >> 4, l16 = lane & 15;
   // Decay tables (lane = token). Off-diagonal blocks (every s < every t)
   // factor e^(G_t - G_s) = e^(G_t - G_r) e^(G_r - G_s) through the column
   // block's last token r: both factors lie in (0, 1], so no per-element exp.
   ps.dG[lane] = G;
   ps.dB[lane] = be;
   ps.dR[lane] = rinv;
+  if constexpr (NORM) ps.dGk[lane] = G - __builtin_amdgcn_logf(rk);
 #pragma unroll
   for (int b = 1; b < NB; ++b) {
     const float Gr = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, G), 16 * Cb[b] + 15));
-    ps.oA[b - 1][lane] = be * exp2_fast(fminf(G - lg - Gr, 0.f));  // beta_t e^(Gx_t - G_r), t > r
-    ps.oP[b - 1][lane] = exp2_fast(fminf(G - Gr, 0.f));            // e^(G_t - G_r), t > r
-    ps.oS[b - 1][lane] = exp2_fast(fminf(Gr - G, 0.f));            // e^(G_r - G_s), s <= r
+    ps.oA[b - 1][lane] = be * exp2_fast(fminf(G - lg - Gr, 0.f)) * rk;  // beta_t e^(Gx_t - G_r) r_k, t > r
+    ps.oP[b - 1][lane] = exp2_fast(fminf(G - Gr, 0.f));                 // e^(G_t - G_r), t > r
+    ps.oS[b - 1][lane] = exp2_fast(fminf(Gr - G, 0.f)) * rk;            // e^(G_r - G_s) r_k, s <= r
   }
   // Each block is formed transposed, K_C Q_R^T and K_C K_R^T (K K^T is
   // symmetric): the accumulator then gives a lane one row t = 16 R + l16 and
@@ -439,30 +468,85 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
       akk[b] = mfma16x16x32(bk, ak, akk[b]);
     }
   }
-  scale_block<0, D, D>(bf, ps, lane, dh, aqk[0], akk[0]);
-  if constexpr ((D & 1) != 0) scale_block<1, R1, C1>(bf, ps, lane, dh, aqk[1], akk[1]);  // A_{D,D-1}
+  scale_block<0, D, D, NORM>(bf, ps, lane, dh, aqk[0], akk[0]);
+  if constexpr ((D & 1) != 0) scale_block<1, R1, C1, NORM>(bf, ps, lane, dh, aqk[1], akk[1]);  // A_{D,D-1}
   // diagonal inverse of this wave's block (reads this wave's own scratch writes)
   invert16(bf, ps.Aown, ps.Town, 16 * D, lane);
   if constexpr ((D & 1) == 0) {
     // T_DD is what the odd neighbour waits for: signal it before the rest.
     pair_signal(pair_flag, chunk_tag, lane);
-    if constexpr (NB > 1) scale_block<1, R1, C1>(bf, ps, lane, dh, aqk[1], akk[1]);
-    if constexpr (NB > 2) scale_block<2, R2, C2>(bf, ps, lane, dh, aqk[2], akk[2]);
+    if constexpr (NB > 1) scale_block<1, R1, C1, NORM>(bf, ps, lane, dh, aqk[1], akk[1]);
+    if constexpr (NB > 2) scale_block<2, R2, C2, NORM>(bf, ps, lane, dh, aqk[2], akk[2]);
   } else {
     static_assert(NB == 2 && R1 == D && C1 == D - 1, "odd waves hold (D, D) and (D, D-1)");
     offdiag_inverse<D>(bf, ps, prev, pair_flag, chunk_tag, lane);
   }
 }
 
+// Value of the lane whose position in the group differs in bit B (the lane
+// mirrored within its 16, 8 or 4 lanes, or its neighbour): DPP row_mirror,
+// row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2].
+template <int B>
+__device__ __forceinline__ float dpp_flip(float x) {
+  constexpr int ctrl = B == 3 ? 0x140 : B == 2 ? 0x141 : B == 1 ? 0x4e : 0xb1;
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+
+// One reduce-scatter step over lane bit B: lanes with the bit clear keep the
+// lower N of their 2N partial sums, lanes with it set the upper N, and each
+// adds the partner lane's copy of the half it keeps.
+template <int B, int N>
+__device__ __forceinline__ void halve_dpp(float* v, int lane) {
+  const bool hi = (lane >> B) & 1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float keep = hi ? v[i + N] : v[i], send = hi ? v[i] : v[i + N];
+    v[i] = keep + dpp_flip<B>(send);
+  }
+}
+
+// Sums each of L values v[0 .. L/2 - 1] over its group of L consecutive lanes
+// (L = 16 or 8). Returns in every lane one complete sum: that of value
+// (lane >> 1) & (L/2 - 1), the same in both lanes of a pair.
+template <int L>
+__device__ __forceinline__ float group_sums_scatter(float* v, int lane) {
+  if constexpr (L == 16) {
+    halve_dpp<3, 4>(v, lane);
+    halve_dpp<2, 2>(v, lane);
+    halve_dpp<1, 1>(v, lane);
+  } else {
+    static_assert(L == 8, "groups of 16 or 8 lanes");
+    halve_dpp<2, 2>(v, lane);
+    halve_dpp<1, 1>(v, lane);
+  }
+  return v[0] + dpp_flip<0>(v[0]);
+}
+
+// Sum of squares of the eight bf16 values in a 16-byte piece: four bf16-pair
+// dot products accumulated in fp32 (each bf16 square is exact in fp32). The
+// words go through scalar copies: a bit cast applied directly to a vector
+// subscript reads element 0 for every index with this compiler.
+__device__ __forceinline__ float sumsq8(const u32x4& w) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const unsigned e[4] = {w.x, w.y, w.z, w.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = __builtin_bit_cast(bf16x2, e[i]);
+    ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
+  }
+  return ss;
+}
+
 // ---- kernel -------------------------------------------------------------------------------
 
-template <int K, int V, int VT, typename OutT>
+template <int K, int V, int VT, typename OutT, bool NORM>
 __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int T, int H, int N, OutT* __restrict__ o,
-    float* __restrict__ sf) {
+    float* __restrict__ sf, unsigned fusion) {
   static_assert(VT == 64, "four consumer wavefronts of 16 channels");
   constexpr int NVT = V / VT;
   __shared__ SmemV3<K, VT> sm;
@@ -579,15 +663,43 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR;
           *reinterpret_cast<u32x4*>(&bf.Vv[swz<VT>(row, c8 * 8)]) = rv[j];
         }
+        const int nrows_c = min(64, t1 - (t0 + it * 64));
         if (ptid < 64) {
-          bf.raw_a[ptid] = ra;
-          bf.raw_b[ptid] = rb;
+          float a_ = ra, b_ = rb;
+          if ((fusion & kFuseGateLogits) && ptid < nrows_c) {  // logits -> alpha, beta
+            a_ = sigmoid_fast(a_);
+            b_ = sigmoid_fast(b_);
+          }
+          bf.raw_a[ptid] = a_;
+          bf.raw_b[ptid] = b_;
+        }
+        // Normalisation: per-piece sums of squares of q and k here, while the
+        // staging registers still hold them ...
+        float ss[2 * QPT];  // q pieces, then k pieces
+        if constexpr (NORM) {
+#pragma unroll
+          for (int j = 0; j < QPT; ++j) {
+            ss[j] = sumsq8(rq[j]);
+            ss[QPT + j] = sumsq8(rk[j]);
+          }
         }
         // The staging registers are free again: fetch the next chunk now, so
         // that its loads are in flight during all of this chunk's work (the
         // work below issues no other vector-memory access that would wait on
         // them).
         if (it + 1 < nchunks) fetch(t0 + (it + 1) * 64);
+        if constexpr (NORM) {
+          // ... then the row sums over the KP consecutive lanes that hold a
+          // row's pieces (256 % KP == 0: a thread's pieces all sit at the same
+          // position in their rows), scattered so that each lane pair ends with
+          // one of the 2 QPT sums, and 1 / sqrt(sum + eps) with the hardware
+          // reciprocal square root (about 1 ulp).
+          static_assert(2 * QPT == KP / 2, "one sum per lane pair");
+          const float tot = group_sums_scatter<KP>(ss, ptid);
+          const int idx = (ptid >> 1) & (2 * QPT - 1), j = idx % QPT;
+          if ((ptid & 1) == 0)
+            bf.rn[idx / QPT][ptid / KP + j * (256 / KP)] = __builtin_amdgcn_rsqf(tot + kL2NormEps);
+        }
         producer_sync(&sm.prod_bar, epoch, lane);
 
         // decays: every producer wave computes all 64 rows (lane = row)
@@ -598,13 +710,15 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         const float lg = __builtin_amdgcn_logf(fmaxf(a, 1.17549435e-38f));
         const float G = wave_scan_dpp(lg);
         const float rinv = __builtin_amdgcn_rcpf(a);
+        const float rql = NORM ? bf.rn[0][lane] : 1.f, rkl = NORM ? bf.rn[1][lane] : 1.f;
         if (p == 0) {
           const float Gn = __shfl(G, 63, kWave);
           const int gp = gate_pos(lane);
           bf.gl[0][gp] = be;
-          bf.gl[1][gp] = be * exp2_fast(G - lg);
-          bf.gl[2][gp] = exp2_fast(G);
-          bf.gl[3][gp] = exp2_fast(Gn - G);
+          bf.gl[1][gp] = be * exp2_fast(G - lg) * rkl;
+          bf.gl[2][gp] = exp2_fast(G) * rql;
+          bf.gl[3][gp] = exp2_fast(Gn - G) * rkl;
+          if constexpr (NORM) bf.gl[4][gp] = dh * exp2_fast(G) * rkl;
           if (lane == 63) bf.eGn = exp2_fast(G);
         }
         // Waves 0 / 1 and 2 / 3 form pairs: the even wave hands its diagonal
@@ -616,10 +730,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         __builtin_amdgcn_s_setprio(2);
         const int tag = it + 1;
         switch (p) {
-          case 0: producer_blocks<0, 3, 3, 0, 3, 1>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be); break;
-          case 1: producer_blocks<1, 2, 1, 0, 0, 0>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be); break;
-          case 2: producer_blocks<2, 3, 2, 0, 2, 1>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be); break;
-          default: producer_blocks<3, 2, 3, 2, 0, 0>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be); break;
+          case 0: producer_blocks<0, 3, 3, 0, 3, 1, NORM>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          case 1: producer_blocks<1, 2, 1, 0, 0, 0, NORM>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          case 2: producer_blocks<2, 3, 2, 0, 2, 1, NORM>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          default: producer_blocks<3, 2, 3, 2, 0, 0, NORM>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -777,6 +891,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           f32x4 acc;
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] = eg[i] * (QH[r4][i] - dh * KH[r4][i]);
+          if constexpr (NORM) {  // e^G r_q (Q h) - d e^G r_k (K h)
+            const f32x4 egk = lds_f4(&bf.gl[4][16 * g + 4 * r4]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = eg[i] * QH[r4][i] - egk[i] * KH[r4][i];
+          }
           if (r4 < 2) {
             acc = mma3(p0h[r4], p0l[r4], ubh0, ubl0, acc);
           } else {
@@ -853,20 +972,26 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   }
 }
 
-template <int K, int V, typename OutT>
+template <int K, int V, typename OutT, bool NORM>
 static hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t st) {
   constexpr int VT = 64, NVT = V / VT;
   const int units = a.N * a.H;
-  chunk_fwd_bf16_kernel<K, V, VT, OutT><<<xcd_grid(units, NVT), 512, 0, st>>>(
+  chunk_fwd_bf16_kernel<K, V, VT, OutT, NORM><<<xcd_grid(units, NVT), 512, 0, st>>>(
       static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.alpha,
-      a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.N, static_cast<OutT*>(a.o), a.sf);
+      a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
   return hipGetLastError();
+}
+
+template <int K, int V, bool NORM>
+static hipError_t launch_bf16_n(const FwdArgs& a, hipStream_t st) {
+  if (a.out_dtype == COMBA_BF16) return launch_bf16_t<K, V, u16, NORM>(a, st);
+  return launch_bf16_t<K, V, float, NORM>(a, st);
 }
 
 template <int K, int V>
 static hipError_t launch_bf16_kv(const FwdArgs& a, hipStream_t st) {
-  if (a.out_dtype == COMBA_BF16) return launch_bf16_t<K, V, u16>(a, st);
-  return launch_bf16_t<K, V, float>(a, st);
+  if (a.fusion & kFuseQkL2Norm) return launch_bf16_n<K, V, true>(a, st);
+  return launch_bf16_n<K, V, false>(a, st);
 }
 
 hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st) {

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int T, int H, int N, OutT* __restrict__ o,
-    float* __restrict__ sf) {
+    float* __restrict__ sf, unsigned fusion) {
   constexpr int NT = 256, VT = SmemF32<K>::VT, LDH = SmemF32<K>::LDH, NVT = V / VT, LQ = K + 1;
   __shared__ SmemF32<K> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -67,10 +67,29 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     }
     if (tid < 64) {
       const int64_t tok = (static_cast<int64_t>(b) * T + c0 + tid) * H + h;
-      sm.gt.raw_a[tid] = tid < nrows ? alpha[tok] : 1.f;
-      sm.gt.raw_b[tid] = tid < nrows ? beta[tok] : 0.f;
+      float ra = 1.f, rb = 0.f;  // padding rows: no decay, no write
+      if (tid < nrows) {
+        ra = alpha[tok];
+        rb = beta[tok];
+        if (fusion & kFuseGateLogits) {
+          ra = sigmoid_stable(ra);
+          rb = sigmoid_stable(rb);
+        }
+      }
+      sm.gt.raw_a[tid] = ra;
+      sm.gt.raw_b[tid] = rb;
     }
     __syncthreads();
+    if (fusion & kFuseQkL2Norm) {  // normalise the staged q and k rows in place
+      if (tid < 128) {
+        float* row = (tid < 64 ? sm.Qs : sm.Ks) + (tid & 63) * LQ;
+        float ss = 0.f;
+        for (int c = 0; c < K; ++c) ss += row[c] * row[c];
+        const float r = 1.f / sqrtf(ss + kL2NormEps);
+        for (int c = 0; c < K; ++c) row[c] *= r;
+      }
+      __syncthreads();
+    }
     if (wave == 0) chunk_gates(sm.gt, lane, nrows);
     __syncthreads();
 
@@ -149,7 +168,7 @@ static hipError_t launch_f32_t(const FwdArgs& a, hipStream_t st) {
   constexpr int NVT = V / SmemF32<K>::VT;
   chunk_fwd_fp32_kernel<K, V, OutT><<<xcd_grid(a.N * a.H, NVT), 256, 0, st>>>(
       static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.N, static_cast<OutT*>(a.o), a.sf);
+      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
   return hipGetLastError();
 }
 

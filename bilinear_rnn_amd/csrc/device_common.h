@@ -26,6 +26,17 @@ __device__ __forceinline__ u16 float_to_bf16_bits(float x) {
   return __builtin_bit_cast(u16, b);
 }
 
+// Input-side fusion flags (the COMBA_FUSE_* values of comba.h).
+constexpr unsigned kFuseGateLogits = 1u, kFuseQkL2Norm = 2u;
+constexpr float kL2NormEps = 1e-6f;  // x / sqrt(sum x^2 + eps)
+
+// sigmoid(x) = 1 / (1 + e^-x) without overflow: e^-|x| is at most 1, and the
+// two branches are the two algebraic forms of the same value.
+__device__ __forceinline__ float sigmoid_stable(float x) {
+  const float e = expf(-fabsf(x));
+  return x >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+}
+
 // x ~= hi + lo with hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   hi = to_bf16(x);

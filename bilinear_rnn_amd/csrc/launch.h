@@ -20,6 +20,7 @@ struct FwdArgs {
   int in_dtype, out_dtype;    // COMBA_BF16 / COMBA_FP32
   void* o;
   float* sf;                  // may be null
+  unsigned fusion;            // COMBA_FUSE_* flags
 };
 
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t st);

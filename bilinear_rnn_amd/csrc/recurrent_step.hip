@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* s0, const int32_t* __restrict__ cu_seqlens, int T, int H,
-    OutT* __restrict__ o, float* sf) {
+    OutT* __restrict__ o, float* sf, unsigned fusion) {
   constexpr int F4 = K / 64;   // 16-byte pieces per lane and row
   constexpr int RPP = 16;       // rows per pass: 4 per wavefront
   constexpr int NP = VB / RPP;  // passes
@@ -82,14 +82,38 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
     for (int f = 0; f < F4; ++f) {
       Load4<InT>::get(k, tok * K + 4 * j + 64 * f, kk[f]);
       Load4<InT>::get(q, tok * K + 4 * j + 64 * f, qt[f]);
+    }
+    if (fusion & kFuseQkL2Norm) {  // q, k / sqrt(sum of squares + eps), in float32
+      float sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int f = 0; f < F4; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sk += kk[f][e] * kk[f][e];
+          sq += qt[f][e] * qt[f][e];
+        }
+      const float rk = 1.f / sqrtf(row16_sum(sk) + kL2NormEps), rq = 1.f / sqrtf(row16_sum(sq) + kL2NormEps);
+#pragma unroll
+      for (int f = 0; f < F4; ++f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kk[f][e] *= rk;
+          qt[f][e] *= rq;
+        }
+    }
+#pragma unroll
+    for (int f = 0; f < F4; ++f)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         qt[f][e] -= dh * kk[f][e];
         kq += kk[f][e] * qt[f][e];
       }
-    }
     kq = row16_sum(kq);
-    const float a = alpha[tok], be = beta[tok];
+    float a = alpha[tok], be = beta[tok];
+    if (fusion & kFuseGateLogits) {
+      a = sigmoid_stable(a);
+      be = sigmoid_stable(be);
+    }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       const int row = vb * VB + p * RPP + w * 4 + rw;
@@ -133,7 +157,7 @@ static hipError_t launch_rec_t(const FwdArgs& a, hipStream_t st) {
   const int grid = a.N * a.H * (V / VB);
   recurrent_kernel<K, V, VB, InT, OutT><<<grid, 256, 0, st>>>(
       static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v),
-      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.T, a.H, static_cast<OutT*>(a.o), a.sf);
+      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.T, a.H, static_cast<OutT*>(a.o), a.sf, a.fusion);
   return hipGetLastError();
 }
 

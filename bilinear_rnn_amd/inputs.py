@@ -14,6 +14,11 @@ lengths (variable-length workloads only) -> q -> k -> v -> alpha logits ->
 beta logits -> initial state. All draws are float32. q and k are
 L2-normalised per (token, head) in float32 and then rounded to the workload's
 dtype; alpha = sigmoid(logit) and beta = sigmoid(logit) stay float32.
+
+With ``raw=True`` the same draws are returned before those two steps: q and
+k un-normalised (rounded to the workload's dtype), alpha and beta holding the
+logits. That is the input of the fused entry points, which normalise and
+apply the sigmoid themselves.
 """
 from __future__ import annotations
 
@@ -108,6 +113,7 @@ class Inputs:
     s0: Optional[np.ndarray]        # [N, H, V, K] or None
     cu_seqlens: Optional[np.ndarray]  # int32 [N + 1] or None
     dtype: str
+    raw: bool = False               # q, k un-normalised; alpha, beta are logits
     q_bits: Optional[np.ndarray] = None
     k_bits: Optional[np.ndarray] = None
     v_bits: Optional[np.ndarray] = None
@@ -120,7 +126,7 @@ class Inputs:
 def make_inputs(w: Workload, *, B: Optional[int] = None, T: Optional[int] = None,
                 H: Optional[int] = None, num_seqs: Optional[int] = None,
                 seed: Optional[int] = None, s0_std: Optional[float] = None,
-                lengths: Optional[np.ndarray] = None) -> Inputs:
+                lengths: Optional[np.ndarray] = None, raw: bool = False) -> Inputs:
     """Draw the inputs of workload ``w``; keyword overrides shrink it for tests."""
     B = w.B if B is None else B
     T = w.T if T is None else T
@@ -150,11 +156,14 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, T: Optional[int] = None
     if s0_std > 0:
         s0 = rng.standard_normal((nseq, H, V, K), dtype=np.float32) * np.float32(s0_std)
 
-    q = _l2_normalise(q)
-    k = _l2_normalise(k)
-    out = Inputs(q=q, k=k, v=v, alpha=_sigmoid(a_logit), beta=_sigmoid(b_logit),
+    if raw:
+        alpha, beta = a_logit, b_logit
+    else:
+        q, k = _l2_normalise(q), _l2_normalise(k)
+        alpha, beta = _sigmoid(a_logit), _sigmoid(b_logit)
+    out = Inputs(q=q, k=k, v=v, alpha=alpha, beta=beta,
                  d=np.full((H,), w.d_value, dtype=np.float32), s0=s0,
-                 cu_seqlens=cu, dtype=w.dtype)
+                 cu_seqlens=cu, dtype=w.dtype, raw=raw)
     if w.dtype == "bf16":
         out.q_bits, out.k_bits, out.v_bits = bf16_bits(q), bf16_bits(k), bf16_bits(v)
         out.q = bf16_bits_to_f32(out.q_bits)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define COMBA_ABI_VERSION 1
+#define COMBA_ABI_VERSION 2
 
 /* Status codes returned by every entry point. */
 enum {
@@ -132,6 +132,53 @@ int32_t comba_recurrent_step(const void* q, const void* k, const void* v,
                              int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                              int32_t in_dtype, int32_t out_dtype,
                              void* o, float* final_state, void* stream);
+
+/*
+ * Input-side fusion (CARVE summary, section 2.3 "键轴衰减与融合": the decay
+ * gate is evaluated inside the kernel; the GLA/KDA blog, sections 2.1 and
+ * 3.1: log-sigmoid and sigmoid gates; the normalisation of q and k is not
+ * spelled out by the pages and is taken as the plain per-token L2 norm that
+ * keeps the Comba transition alpha I - beta k k^T contractive). Flags for the
+ * fused entry points below; any combination, 0 = no fusion:
+ *   COMBA_FUSE_GATE_LOGITS  alpha and beta hold logits a, b; the kernels use
+ *                           alpha = sigmoid(a) and beta = sigmoid(b), formed
+ *                           from e^-|x| so that no logit overflows (alpha
+ *                           below the smallest normal float is clamped to it).
+ *   COMBA_FUSE_QK_L2NORM    q and k are normalised per (token, head) inside
+ *                           the kernels: x / sqrt(sum_i x_i^2 + 1e-6).
+ * The normalisation never rounds a normalised q or k to bf16: the factor
+ * 1 / sqrt(...) of each token is computed in float32 (in the bf16 chunk
+ * kernel with the hardware reciprocal square root, about 1 ulp) and applied
+ * to the float32 results of the products in which q or k take part, so fused
+ * and unfused calls meet the same accuracy bounds.
+ */
+enum { COMBA_FUSE_GATE_LOGITS = 1, COMBA_FUSE_QK_L2NORM = 2 };
+
+/*
+ * comba_chunk_fwd with input-side fusion: same arguments, layouts, workspace
+ * and errors, plus `fusion` (an OR of COMBA_FUSE_* flags; unknown bits are
+ * COMBA_ERR_INVALID_ARG). With fusion == 0 it is comba_chunk_fwd.
+ */
+int32_t comba_chunk_fwd_fused(const void* q, const void* k, const void* v,
+                              const float* alpha, const float* beta, const float* d,
+                              const float* initial_state,
+                              const int32_t* cu_seqlens, int32_t num_seqs,
+                              int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                              int32_t in_dtype, int32_t out_dtype,
+                              void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, uint32_t fusion, void* stream);
+
+/*
+ * comba_recurrent_step with input-side fusion (same arguments plus `fusion`,
+ * as for comba_chunk_fwd_fused). With fusion == 0 it is comba_recurrent_step.
+ */
+int32_t comba_recurrent_step_fused(const void* q, const void* k, const void* v,
+                                   const float* alpha, const float* beta, const float* d,
+                                   const float* initial_state,
+                                   const int32_t* cu_seqlens, int32_t num_seqs,
+                                   int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                   int32_t in_dtype, int32_t out_dtype,
+                                   void* o, float* final_state, uint32_t fusion, void* stream);
 
 /*
  * Longest-first order of packed sequences (integer work, exact): writes into

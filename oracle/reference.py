@@ -136,6 +136,36 @@ def comba_forward_chunked(q, k, v, alpha, beta, d, s0=None, cu_seqlens=None,
     return o, s_final
 
 
+L2NORM_EPS = 1e-6
+
+
+def fused_inputs(q, k, alpha, beta, gate_logits: bool = False, qk_l2norm: bool = False):
+    """Input-side steps that the fused entry points take inside their kernels, in fp64.
+
+    - ``qk_l2norm``: q and k are L2-normalised per (token, head), x / sqrt(sum x^2 + eps)
+      with eps = 1e-6. The pages do not spell this step out; it is the plainest
+      reading of the unit-norm keys that keep the transition alpha I - beta k k^T
+      of the Comba write-up (section "Comba架构") a contraction for beta <= 1.
+    - ``gate_logits``: alpha and beta arrive as logits and become sigmoid(logit),
+      the gate of the GLA/KDA comparison (sections 2.1 and 3.1) that CARVE
+      evaluates inside its kernel (GDN-2/CARVE summary, section 2.3).
+
+    Returns (q, k, alpha, beta) as float64 arrays ready for :func:`comba_forward`.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    if qk_l2norm:
+        q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + L2NORM_EPS)
+        k = k / np.sqrt(np.sum(k * k, axis=-1, keepdims=True) + L2NORM_EPS)
+    if gate_logits:
+        with np.errstate(over="ignore"):
+            alpha = 1.0 / (1.0 + np.exp(-alpha))
+            beta = 1.0 / (1.0 + np.exp(-beta))
+    return q, k, alpha, beta
+
+
 def rel_l2(x, ref) -> float:
     """||x - ref||_2 / ||ref||_2 over the whole tensor, in fp64."""
     x = np.asarray(x, dtype=np.float64)

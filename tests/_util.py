@@ -24,10 +24,15 @@ def dev_inputs(inp, device="cuda"):
     return out
 
 
-def oracle_of(inp, heads=None, seqs=None, nthreads=0):
+def oracle_of(inp, heads=None, seqs=None, nthreads=0, gate_logits=None, qk_l2norm=None):
     """fp64 oracle on the exact inputs, optionally restricted to some heads and
-    batch rows (full sequences). Returns (o, final_state) in the same order."""
+    batch rows (full sequences). Returns (o, final_state) in the same order.
+
+    For raw inputs (``inp.raw``) the oracle's own input steps run first: gate
+    logits and q/k normalisation both default to on, each can be switched off."""
     q, k, v, a, b, d, s0 = inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, inp.s0
+    gate_logits = inp.raw if gate_logits is None else gate_logits
+    qk_l2norm = inp.raw if qk_l2norm is None else qk_l2norm
     cu = inp.cu_seqlens
     if seqs is not None:
         assert cu is None
@@ -37,6 +42,8 @@ def oracle_of(inp, heads=None, seqs=None, nthreads=0):
         q, k, v, a, b = (x[:, :, heads] for x in (q, k, v, a, b))
         d = d[heads]
         s0 = None if s0 is None else s0[:, heads]
+    if gate_logits or qk_l2norm:
+        q, k, a, b = oracle.fused_inputs(q, k, a, b, gate_logits=gate_logits, qk_l2norm=qk_l2norm)
     return oracle.comba_forward_c(q, k, v, a, b, d, s0, cu, nthreads=nthreads)
 
 

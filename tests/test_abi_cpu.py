@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = comba.lib()
-    assert L.comba_abi_version() == 1
+    assert L.comba_abi_version() == 2
     assert api.status_string(0) == "COMBA_OK"
     assert api.status_string(-1) == "COMBA_ERR_INVALID_ARG"
     assert api.status_string(-2) == "COMBA_ERR_UNSUPPORTED"
@@ -46,29 +46,41 @@ def test_version_and_status_strings():
     assert api.status_string(7) == "COMBA_ERR_UNKNOWN"
 
 
-def chunk(**kw):
+def chunk(fusion=None, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
                 B=1, T=16, H=2, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None, ws=None, wsb=0)
     args.update(kw)
     L = comba.lib()
-    return L.comba_chunk_fwd(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"],
-                             args["s0"], args["cu"], args["n"], args["B"], args["T"], args["H"], args["K"],
-                             args["V"], args["idt"], args["odt"], args["o"], args["sf"], args["ws"],
-                             args["wsb"], None)
+    a = (args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"], args["s0"], args["cu"],
+         args["n"], args["B"], args["T"], args["H"], args["K"], args["V"], args["idt"], args["odt"],
+         args["o"], args["sf"], args["ws"], args["wsb"])
+    if fusion is None:
+        return L.comba_chunk_fwd(*a, None)
+    return L.comba_chunk_fwd_fused(*a, fusion, None)
 
 
-def step(**kw):
+def step(fusion=None, **kw):
     args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
                 B=1, T=1, H=2, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None)
     args.update(kw)
     L = comba.lib()
-    return L.comba_recurrent_step(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"],
-                                  args["s0"], args["cu"], args["n"], args["B"], args["T"], args["H"],
-                                  args["K"], args["V"], args["idt"], args["odt"], args["o"], args["sf"],
-                                  None)
+    a = (args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"], args["s0"], args["cu"],
+         args["n"], args["B"], args["T"], args["H"], args["K"], args["V"], args["idt"], args["odt"],
+         args["o"], args["sf"])
+    if fusion is None:
+        return L.comba_recurrent_step(*a, None)
+    return L.comba_recurrent_step_fused(*a, fusion, None)
 
 
-@pytest.mark.parametrize("fn", [chunk, step])
+def chunk_fused(**kw):
+    return chunk(fusion=api.COMBA_FUSE_GATE_LOGITS | api.COMBA_FUSE_QK_L2NORM, **kw)
+
+
+def step_fused(**kw):
+    return step(fusion=api.COMBA_FUSE_QK_L2NORM, **kw)
+
+
+@pytest.mark.parametrize("fn", [chunk, step, chunk_fused, step_fused])
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
     (dict(beta=None), -1), (dict(d=None), -1), (dict(o=None), -1),
@@ -81,6 +93,13 @@ def step(**kw):
 def test_invalid_arguments_are_rejected_before_launch(fn, kw, code):
     assert fn(**kw) == code
     assert api.last_error() != ""
+
+
+@pytest.mark.parametrize("fn", [chunk, step])
+@pytest.mark.parametrize("fusion", [4, 8, 0x80000000, 0xFFFFFFFF])
+def test_unknown_fusion_bits_are_rejected(fn, fusion):
+    assert fn(fusion=fusion) == api.COMBA_ERR_INVALID_ARG
+    assert "fusion" in api.last_error()
 
 
 def test_workspace_rules():

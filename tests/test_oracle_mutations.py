@@ -35,6 +35,12 @@ MUTATIONS = {
     "chunk_state_weights": ("Kc.T @ (np.exp(G[-1] - G)[:, None] * Ubar)",
                             "Kc.T @ (np.exp(G[-1] - Gx)[:, None] * Ubar)"),
     "chunk_W_without_decay": ("W = Tinv @ ((bet * np.exp(Gx))[:, None] * Kc)", "W = Tinv @ (bet[:, None] * Kc)"),
+    # input-side steps of the fused entry points
+    "l2norm_eps_outside_sqrt": ("q = q / np.sqrt(np.sum(q * q, axis=-1, keepdims=True) + L2NORM_EPS)",
+                                "q = q / (np.sqrt(np.sum(q * q, axis=-1, keepdims=True)) + L2NORM_EPS)"),
+    "l2norm_k_by_q_norm": ("k = k / np.sqrt(np.sum(k * k, axis=-1",
+                           "k = k / np.sqrt(np.sum(q * q, axis=-1"),
+    "sigmoid_sign": ("alpha = 1.0 / (1.0 + np.exp(-alpha))", "alpha = 1.0 / (1.0 + np.exp(alpha))"),
 }
 
 
@@ -49,7 +55,7 @@ def _run_pins_on_copy(tmp_path, before=None, after=None):
         ref.write_text(src.replace(before, after))
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           "-k", "numpy or chunk", "tests/test_oracle_pins.py"],
+                           "-k", "numpy or chunk or fused", "tests/test_oracle_pins.py"],
                           cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
 
 

@@ -331,3 +331,59 @@ def test_c_and_numpy_oracles_agree_on_varlen_workload():
     o2, f2 = oracle.comba_forward_c(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, None,
                                     inp.cu_seqlens)
     assert rel_l2(o2, o1) < 1e-14 and rel_l2(f2, f1) < 1e-14
+
+
+# --- input-side steps of the fused entry points ------------------------------------------
+
+def test_fused_inputs_l2norm_matches_library_norm_and_eps():
+    rng = np.random.default_rng(41)
+    q = rng.standard_normal((2, 5, 3, 16)) * 7.0
+    k = rng.standard_normal((2, 5, 3, 16)) * 0.3
+    a = rng.standard_normal((2, 5, 3))
+    qn, kn, an, bn = oracle.fused_inputs(q, k, a, a, qk_l2norm=True)
+    # far above eps the step is division by numpy's 2-norm
+    np.testing.assert_allclose(qn, q / np.linalg.norm(q, axis=-1, keepdims=True), rtol=1e-7)
+    np.testing.assert_allclose(kn, k / np.linalg.norm(k, axis=-1, keepdims=True), rtol=1e-5)
+    np.testing.assert_array_equal(an, a)
+    np.testing.assert_array_equal(bn, a)
+    # near eps: x = 1e-4 e_1 gives 1e-4 / sqrt(1e-8 + 1e-6) = 0.0995037...
+    x = np.zeros((1, 1, 1, 8))
+    x[..., 0] = 1e-4
+    xn = oracle.fused_inputs(x, x, a[:1, :1, :1], a[:1, :1, :1], qk_l2norm=True)[0]
+    assert abs(xn[0, 0, 0, 0] - 1e-4 / np.sqrt(1.01e-6)) < 1e-12
+    # a zero row stays zero
+    z = oracle.fused_inputs(np.zeros((1, 1, 1, 8)), x, a[:1, :1, :1], a[:1, :1, :1], qk_l2norm=True)[0]
+    assert np.all(z == 0)
+
+
+def test_fused_inputs_sigmoid_special_values():
+    from scipy.special import expit
+    a = np.array([[[0.0, 1.5, -2.25, 30.0, -30.0, 800.0, -800.0]]])
+    b = -a
+    q = np.ones((1, 1, 7, 4))
+    qn, kn, an, bn = oracle.fused_inputs(q, q, a, b, gate_logits=True)
+    np.testing.assert_array_equal(qn, q)
+    assert an[0, 0, 0] == 0.5
+    np.testing.assert_allclose(an, expit(a), rtol=1e-14, atol=0)
+    np.testing.assert_allclose(an + bn, 1.0, rtol=0, atol=1e-15)  # sigma(a) + sigma(-a) = 1
+    assert an[0, 0, 5] == 1.0 and an[0, 0, 6] == 0.0 and np.isfinite(an).all()
+    assert abs(an[0, 0, 4] - np.exp(-30.0)) < 1e-25      # sigma(a) ~ e^a for a << 0
+
+
+def test_fused_inputs_make_the_forward_scale_invariant_in_q_and_k():
+    q, k, v, alpha, beta, d, S0 = small_case(43, K=8, V=5)
+    a_logit = np.log(alpha / (1 - alpha))
+    b_logit = np.log(np.maximum(beta, 1e-3) / (1 - np.maximum(beta, 1e-3)))
+    ref = comba_forward(*oracle.fused_inputs(q, k, a_logit, b_logit, True, True)[:2], v,
+                        *oracle.fused_inputs(q, k, a_logit, b_logit, True, True)[2:], d, S0)
+    # |k| = 1 here: eps = 1e-6 moves a normalised k by about 5e-7 relative,
+    # so scales of 5 and 3 change the result by about that much
+    scaled = comba_forward(*oracle.fused_inputs(5 * q, 3 * k, a_logit, b_logit, True, True)[:2], v,
+                           *oracle.fused_inputs(5 * q, 3 * k, a_logit, b_logit, True, True)[2:], d, S0)
+    for x, y in zip(ref, scaled):
+        assert rel_l2(y, x) < 3e-6
+    # logits of the gates used directly give back the unfused forward
+    direct = comba_forward(q / np.linalg.norm(q, axis=-1, keepdims=True), k, v, alpha,
+                           np.maximum(beta, 1e-3), d, S0)
+    for x, y in zip(ref, direct):
+        assert rel_l2(x, y) < 1e-6
