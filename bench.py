@@ -8,7 +8,9 @@ K=V=128, fp32 state updated in place in device memory) is timed in the same
 run and reported in GB/s under "decode". The same 1.3B-layer forward with
 input-side fusion (raw q/k normalised in the kernel, alpha/beta given as
 logits) is timed under "fused", beside the same preprocessing done by
-separate torch ops before an unfused call. The fp64 CPU oracle is timed on
+separate torch ops before an unfused call. The 64K-token single-sequence
+workload is timed plain and segment-parallel under "long_context" (context,
+not the metric). The fp64 CPU oracle is timed on
 the host cores on a bounded sample of the same workload ("cpu_baseline").
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -216,6 +218,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with a plain 256 MiB device copy (counter calibration runs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -342,6 +345,29 @@ def main():
                            "torch_preprocess_then_chunk_us": sms * 1e3,
                            "parity_sampled_o_rel_l2": oracle.rel_l2(fo[b:b + 1, :, h:h + 1], ro)}
         del tr
+
+    if not args.no_long:
+        # one 64K-token sequence: 32 workgroups plain, segment-parallel fills the chip
+        wl_ = WORKLOADS["long_context"]
+        li = make_inputs(wl_)
+        tl = device_inputs(li, torch, dev)
+        lo = torch.empty((1, wl_.T, wl_.H, wl_.V), dtype=torch.bfloat16, device=dev)
+        lsf = torch.empty((1, wl_.H, wl_.V, wl_.K), dtype=torch.float32, device=dev)
+        nws = comba.segmented_workspace_size(1, wl_.T, wl_.H, wl_.K, wl_.V, 0)
+        lws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
+
+        def lstep(seg):
+            return lambda _: comba.chunk_fwd(tl["q"], tl["k"], tl["v"], tl["alpha"], tl["beta"], tl["d"], None,
+                                             out=lo, final_state=lsf, workspace=lws, segments=seg)
+
+        lsteps, lwarm = max(args.steps // 10, 5), min(args.warmup // 10 + 2, 12)
+        pms, _ = time_loop(torch, lstep(None), lsteps, lwarm)
+        sms_, _ = time_loop(torch, lstep(0), lsteps, lwarm)
+        result["long_context"] = {"workload": "long_context", "B": 1, "T": wl_.T, "H": wl_.H, "K": wl_.K, "V": wl_.V,
+                                  "plain_us": pms * 1e3, "segmented_us": sms_ * 1e3,
+                                  "segmented_tokens/s": wl_.T / (sms_ * 1e-3), "plain_tokens/s": wl_.T / (pms * 1e-3),
+                                  "segments": "automatic (8 x 8192 tokens)", "workspace_bytes": nws}
+        del tl, li
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, H)

@@ -6,6 +6,7 @@ correction, as hand-written HIP kernels behind a C ABI (include/comba.h).
 This package is the thin Python binding over that library.
 """
 from .api import (CombaError, chunk_fwd, lib, library_path, recurrent_step,  # noqa: F401
-                  varlen_order, workspace_size)
+                  segmented_workspace_size, varlen_order, workspace_size)
 
-__all__ = ["chunk_fwd", "recurrent_step", "varlen_order", "workspace_size", "CombaError"]
+__all__ = ["chunk_fwd", "recurrent_step", "varlen_order", "workspace_size", "segmented_workspace_size",
+           "CombaError"]

@@ -29,7 +29,8 @@ COMBA_FUSE_QK_L2NORM = 2
 
 EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_chunk_fwd_fused",
-            "comba_recurrent_step", "comba_recurrent_step_fused", "comba_varlen_order")
+            "comba_recurrent_step", "comba_recurrent_step_fused", "comba_chunk_fwd_segmented_workspace_size",
+            "comba_chunk_fwd_segmented", "comba_varlen_order")
 
 
 class CombaError(RuntimeError):
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.comba_recurrent_step_fused.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32,
                                                  i32, i32, i32, vp, fp, ctypes.c_uint32, vp]
         L.comba_recurrent_step_fused.restype = i32
+        L.comba_chunk_fwd_segmented_workspace_size.argtypes = [i32] * 6
+        L.comba_chunk_fwd_segmented_workspace_size.restype = sz
+        L.comba_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, i32,
+                                                vp, fp, i32, vp, sz, ctypes.c_uint32, vp]
+        L.comba_chunk_fwd_segmented.restype = i32
         L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
         L.comba_varlen_order.restype = i32
         _lib = L
@@ -151,12 +157,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, gate_logits: bool = False,
-              qk_l2norm: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              qk_l2norm: bool = False,
+              segments: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunk-wise forward through ``comba_chunk_fwd``. Returns (o, final_state).
 
     ``gate_logits``: alpha and beta hold pre-sigmoid logits; ``qk_l2norm``: q
     and k are L2-normalised per head and token inside the kernel. Either flag
-    routes the call through ``comba_chunk_fwd_fused``."""
+    routes the call through ``comba_chunk_fwd_fused``. ``segments`` (an int,
+    0 = automatic; fixed-length batches only) routes it through the
+    segment-parallel ``comba_chunk_fwd_segmented``."""
     B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     L = lib()
     if out is None:
@@ -166,10 +175,23 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
         final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
     if final_state is not None:
         _require(final_state, "final_state", torch.float32, (N, H, V, K))
+    fusion = _fusion(gate_logits, qk_l2norm)
+    if segments is not None:
+        if cu_seqlens is not None:
+            raise ValueError("segments applies to fixed-length batches (no cu_seqlens)")
+        nws = int(L.comba_chunk_fwd_segmented_workspace_size(B, T, H, K, V, int(segments)))
+        if nws > 0 and (workspace is None or workspace.numel() < nws):
+            workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+        with torch.cuda.device(q.device):
+            stream = torch.cuda.current_stream(q.device).cuda_stream
+            _check(L.comba_chunk_fwd_segmented(
+                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state), B, T, H, K, V,
+                _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state), int(segments), _ptr(workspace),
+                0 if workspace is None else workspace.numel(), fusion, ctypes.c_void_p(stream)))
+        return out, final_state
     nws = int(L.comba_chunk_fwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0, _DT[q.dtype]))
     if nws > 0 and (workspace is None or workspace.numel() < nws):
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
-    fusion = _fusion(gate_logits, qk_l2norm)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
@@ -219,6 +241,10 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
         else:
             _check(L.comba_recurrent_step(*args, ctypes.c_void_p(stream)))
     return out, final_state
+
+
+def segmented_workspace_size(B: int, T: int, H: int, K: int, V: int, segments: int = 0) -> int:
+    return int(lib().comba_chunk_fwd_segmented_workspace_size(B, T, H, K, V, segments))
 
 
 def varlen_order(cu_seqlens: torch.Tensor) -> torch.Tensor:

@@ -179,6 +179,124 @@ COMBA_API int32_t comba_recurrent_step_fused(const void* q, const void* k, const
                         out_dtype, o, final_state, fusion, stream);
 }
 
+namespace {
+
+// Workgroups that fill the chip once (one chunk-kernel workgroup per CU).
+constexpr int kTargetWorkgroups = 256;
+// Automatic segments are at least this many tokens long.
+constexpr int kMinAutoSegment = 512;
+
+struct SegPlan {
+  int S;  // segments per sequence (1: no segmentation)
+  int L;  // tokens per segment (a multiple of 64)
+};
+
+SegPlan plan_segments(int32_t B, int32_t T, int32_t H, int32_t V, int32_t num_segments) {
+  const int chunks = (T + 63) / 64;
+  int S = num_segments;
+  if (S <= 0) {
+    const int64_t units = static_cast<int64_t>(B) * H * ((V + 63) / 64);
+    const int64_t fill = units >= kTargetWorkgroups ? 1 : kTargetWorkgroups / units;
+    S = static_cast<int>(fill < T / kMinAutoSegment ? fill : T / kMinAutoSegment);
+  }
+  if (S > chunks) S = chunks;
+  if (S < 1) S = 1;
+  const int L = ((chunks + S - 1) / S) * 64;
+  return SegPlan{(T + L - 1) / L, L};
+}
+
+struct SegWorkspace {
+  size_t cu, bst, phi, x, total;
+};
+
+SegWorkspace seg_workspace(int64_t NS, int32_t H, int32_t K, int32_t V) {
+  SegWorkspace w;
+  w.cu = 0;
+  w.bst = align_up(sizeof(int32_t) * (NS + 1));
+  w.phi = w.bst + align_up(static_cast<size_t>(NS) * H * V * K * 4);
+  w.x = w.phi + align_up(static_cast<size_t>(NS) * H * K * K * 4);
+  w.total = w.x + align_up(static_cast<size_t>(NS) * H * V * K * 4);
+  return w;
+}
+
+}  // namespace
+
+COMBA_API size_t comba_chunk_fwd_segmented_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                                          int32_t num_segments) {
+  if (B < 1 || T < 1 || H < 1 || K < 1 || V < 1) return 0;
+  const SegPlan p = plan_segments(B, T, H, V, num_segments);
+  if (p.S <= 1) return 0;
+  return seg_workspace(static_cast<int64_t>(B) * p.S, H, K, V).total;
+}
+
+COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v, const float* alpha,
+                                            const float* beta, const float* d, const float* initial_state,
+                                            int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                            int32_t in_dtype, int32_t out_dtype, void* o, float* final_state,
+                                            int32_t num_segments, void* workspace, size_t workspace_bytes,
+                                            uint32_t fusion, void* stream) {
+  if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
+  if (num_segments < 0) return fail(COMBA_ERR_INVALID_ARG, "num_segments must be >= 0 (0: automatic)");
+  comba::FwdArgs a;
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, nullptr, 0, B, T, H, K, V, in_dtype, out_dtype,
+                          o, final_state, a);
+  if (rc != COMBA_OK) return rc;
+  if (static_cast<int64_t>(B) * T > INT_MAX)
+    return fail(COMBA_ERR_UNSUPPORTED, "B * T above 2^31 - 1 tokens");
+  const SegPlan p = plan_segments(B, T, H, V, num_segments);
+  if (p.S <= 1)
+    return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, nullptr, 0, B, T, H, K, V, in_dtype, out_dtype, o,
+                          final_state, nullptr, 0, fusion, stream);
+  const int NS = B * p.S;
+  if (static_cast<int64_t>(NS) * H * 2 > INT_MAX / 16)
+    return fail(COMBA_ERR_UNSUPPORTED, "too many (segment, head) pairs for one launch");
+  const SegWorkspace w = seg_workspace(NS, H, K, V);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(COMBA_ERR_WORKSPACE,
+                "workspace is NULL or smaller than comba_chunk_fwd_segmented_workspace_size()");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* cu = reinterpret_cast<int32_t*>(ws + w.cu);
+  float* bst = reinterpret_cast<float*>(ws + w.bst);
+  float* phi = reinterpret_cast<float*>(ws + w.phi);
+  float* X = reinterpret_cast<float*>(ws + w.x);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto launch = [&](const comba::FwdArgs& x) {
+    return in_dtype == COMBA_BF16 ? comba::launch_chunk_bf16(x, st) : comba::launch_chunk_fp32(x, st);
+  };
+  rc = launched(comba::launch_segment_bounds(B, T, p.L, p.S, cu, st));
+  if (rc != COMBA_OK) return rc;
+  // every segment as a packed sequence of one long row of B T tokens
+  comba::FwdArgs seg = a;
+  seg.cu_seqlens = cu;
+  seg.order = nullptr;
+  seg.N = NS;
+  seg.B = 1;
+  seg.T = B * T;
+  seg.fusion = fusion;
+  // b_j: final states from zero states, no output
+  comba::FwdArgs p1 = seg;
+  p1.s0 = nullptr;
+  p1.sf = bst;
+  p1.fusion = fusion | comba::kModeNoOutput;
+  rc = launched(launch(p1));
+  if (rc != COMBA_OK) return rc;
+  // Phi_j: v = 0 from the identity, a K x K state
+  comba::FwdArgs p2 = p1;
+  p2.V = K;
+  p2.sf = phi;
+  p2.fusion = fusion | comba::kModeNoOutput | comba::kModeZeroV | comba::kModeIdentityInit;
+  rc = launched(launch(p2));
+  if (rc != COMBA_OK) return rc;
+  // X_{j+1} = X_j Phi_j + b_j; the last one is the final state
+  rc = launched(comba::launch_segment_scan(initial_state, bst, phi, X, final_state, B, H, K, V, p.S, st));
+  if (rc != COMBA_OK) return rc;
+  // outputs: every segment from its true initial state
+  comba::FwdArgs p3 = seg;
+  p3.s0 = X;
+  p3.sf = nullptr;
+  return launched(launch(p3));
+}
+
 COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,
                                      void* stream) {
   if (!cu_seqlens || !order) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens and order must be non-NULL");

@@ -621,7 +621,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           __builtin_amdgcn_readfirstlane(nrows * H * K * 2), kBufferWord3);
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(const_cast<u16*>(v + tok0 * V + vt * VT)), static_cast<short>(0),
-          __builtin_amdgcn_readfirstlane(nrows * H * V * 2), kBufferWord3);
+          __builtin_amdgcn_readfirstlane((fusion & kModeZeroV) ? 0 : nrows * H * V * 2), kBufferWord3);
 #pragma unroll
       for (int j = 0; j < QPT; ++j) {
         rq[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, qkoff[j], 0, 0);
@@ -752,8 +752,13 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     f32x4 hs[K / 16];
     const int64_t srow = ((static_cast<int64_t>(n) * H + h) * V + vcol) * K;
 #pragma unroll
-    for (int kb = 0; kb < K / 16; ++kb)
+    for (int kb = 0; kb < K / 16; ++kb) {
       hs[kb] = s0 ? *reinterpret_cast<const f32x4*>(s0 + srow + 16 * kb + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (fusion & kModeIdentityInit) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hs[kb][i] = (16 * kb + 4 * g + i == vcol) ? 1.f : 0.f;
+      }
+    }
 
     for (int it = 0; it <= nchunks; ++it) {
       if (it > 0) {
@@ -911,7 +916,8 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           const int vrows = min(max(nrows - 16 * r4, 0), 16);
           const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
               uniform_ptr(o + obase + static_cast<int64_t>(16 * r4) * hv), static_cast<short>(0),
-              __builtin_amdgcn_readfirstlane(vrows * hv * static_cast<int>(sizeof(OutT))), kBufferWord3);
+              __builtin_amdgcn_readfirstlane((fusion & kModeNoOutput) ? 0 : vrows * hv * static_cast<int>(sizeof(OutT))),
+              kBufferWord3);
           if constexpr (sizeof(OutT) == 2) {
             const unsigned p01 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){acc[0], acc[1]}, bf16x2));
             const unsigned p23 = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){acc[2], acc[3]}, bf16x2));

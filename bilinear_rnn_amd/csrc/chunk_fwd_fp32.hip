@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
 
   for (int e = tid; e < K * VT; e += NT) {
     const int kk = e % K, c = e / K;
-    sm.Hs[kk * LDH + c] = s0 ? s0[sbase + static_cast<int64_t>(vt * VT + c) * K + kk] : 0.f;
+    sm.Hs[kk * LDH + c] = (fusion & kModeIdentityInit) ? (vt * VT + c == kk ? 1.f : 0.f)
+                          : s0 ? s0[sbase + static_cast<int64_t>(vt * VT + c) * K + kk] : 0.f;
   }
 
   const int nchunks = (t1 - t0 + 63) / 64;
@@ -63,7 +64,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     }
     for (int e = tid; e < 64 * VT; e += NT) {
       const int row = e / VT, c = e % VT, t = c0 + row;
-      sm.Vs[e] = row < nrows ? v[((static_cast<int64_t>(b) * T + t) * H + h) * V + vt * VT + c] : 0.f;
+      sm.Vs[e] = (row < nrows && !(fusion & kModeZeroV)) ? v[((static_cast<int64_t>(b) * T + t) * H + h) * V + vt * VT + c]
+                                                        : 0.f;
     }
     if (tid < 64) {
       const int64_t tok = (static_cast<int64_t>(b) * T + c0 + tid) * H + h;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
       const int t = e / VT, c = e % VT;
       float acc = sm.Os[t * LDH + c];
       for (int s = 0; s <= t; ++s) acc += sm.Pm[t * kLdF + s] * sm.Rs[s * LDH + c];
-      if (t < nrows)
+      if (t < nrows && !(fusion & kModeNoOutput))
         Elem<OutT>::store(o, ((static_cast<int64_t>(b) * T + c0 + t) * H + h) * V + vt * VT + c, acc);
     }
     // h' = exp(G_n) h + K^T diag(exp(G_n - G)) Ubar

@@ -6,6 +6,12 @@
 
 namespace comba {
 
+// Library-internal modes of the chunk kernels, in FwdArgs::fusion above the
+// COMBA_FUSE_* bits (callers can never set them), used by the segment-parallel
+// forward: v read as zeros, no output written, initial state the identity
+// (then V == K).
+constexpr unsigned kModeZeroV = 1u << 16, kModeNoOutput = 1u << 17, kModeIdentityInit = 1u << 18;
+
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -20,13 +26,16 @@ struct FwdArgs {
   int in_dtype, out_dtype;    // COMBA_BF16 / COMBA_FP32
   void* o;
   float* sf;                  // may be null
-  unsigned fusion;            // COMBA_FUSE_* flags
+  unsigned fusion;            // COMBA_FUSE_* flags | kMode* bits
 };
 
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_fp32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_varlen_order(const int32_t* cu_seqlens, int N, int32_t* order, hipStream_t st);
+hipError_t launch_segment_bounds(int B, int T, int L, int S, int32_t* cu, hipStream_t st);
+hipError_t launch_segment_scan(const float* s0, const float* bst, const float* phi, float* X, float* sf, int B,
+                               int H, int K, int V, int S, hipStream_t st);
 
 // Grid for work units of NVT tiles each, dealt round-robin over the 8 XCDs so
 // that the tiles of one unit run on the same XCD (and share its L2).

@@ -1,0 +1,103 @@
+// Segment-parallel chunk forward for long sequences: the small kernels
+// around the chunk kernel.
+//
+// A sequence split into segments j = 0 .. S-1 of L tokens is run as S packed
+// sequences. The state map of a segment is affine in its initial state X
+// (Comba write-up, section "Comba架构：基于闭环控制理论": every step multiplies
+// the state by alpha_t I - beta_t k_t k_t^T on the right and adds beta_t v_t k_t^T):
+//     S_end = X Phi_j + b_j,   Phi_j = prod_t (alpha_t I - beta_t k_t k_t^T),
+// where b_j is the segment's final state from a zero state and Phi_j the final
+// state of a run with v = 0 from the identity (a K x K "state"). The chunk
+// kernel produces both; the scan below chains them, X_{j+1} = X_j Phi_j + b_j,
+// and a last chunk-kernel pass reruns every segment from its true X_j.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace comba {
+
+// cu[n] for segment n = b * S + j: b T + min(j L, T); cu[B S] = B T.
+__global__ __launch_bounds__(256) void segment_bounds_kernel(int B, int T, int L, int S, int32_t* __restrict__ cu) {
+  const int n = blockIdx.x * blockDim.x + threadIdx.x;
+  const int total = B * S;
+  if (n > total) return;
+  if (n == total) {
+    cu[n] = B * T;
+    return;
+  }
+  const int b = n / S, j = n % S;
+  cu[n] = b * T + min(j * L, T);
+}
+
+// One workgroup per (batch row b, head h, block of RB state rows). X rows
+// live in LDS; thread (c, i0) owns column c of RPT rows. For each segment:
+// store X_j as that segment's initial state, then X_{j+1} = X_j Phi_j + b_j in
+// fp32 (Phi_j column c read coalesced, the X row element broadcast from LDS).
+// After the last segment X_S is the sequence's final state.
+template <int K>
+__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ s0, const float* __restrict__ bst,
+                                                           const float* __restrict__ phi, float* __restrict__ X,
+                                                           float* __restrict__ sf, int H, int V, int S) {
+  constexpr int RB = 16, RG = 256 / K, RPT = RB / RG;
+  __shared__ float xs[RB][K];
+  const int nrb = V / RB;
+  const int rb = blockIdx.x % nrb, bh = blockIdx.x / nrb, h = bh % H, b = bh / H;
+  const int c = threadIdx.x % K, i0 = threadIdx.x / K;
+  float x[RPT];
+#pragma unroll
+  for (int r = 0; r < RPT; ++r) {
+    const int row = rb * RB + i0 + r * RG;
+    x[r] = s0 ? s0[((static_cast<int64_t>(b) * H + h) * V + row) * K + c] : 0.f;
+    xs[i0 + r * RG][c] = x[r];
+  }
+  __syncthreads();
+  for (int j = 0; j < S; ++j) {
+    const int64_t n = static_cast<int64_t>(b) * S + j;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = rb * RB + i0 + r * RG;
+      X[((n * H + h) * V + row) * K + c] = x[r];
+    }
+    const float* ph = phi + (n * H + h) * K * K + c;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = rb * RB + i0 + r * RG;
+      x[r] = bst[((n * H + h) * V + row) * K + c];
+    }
+    for (int m = 0; m < K; ++m) {
+      const float p = ph[static_cast<int64_t>(m) * K];
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) x[r] += xs[i0 + r * RG][m] * p;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) xs[i0 + r * RG][c] = x[r];
+    __syncthreads();
+  }
+  if (sf) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+      const int row = rb * RB + i0 + r * RG;
+      sf[((static_cast<int64_t>(b) * H + h) * V + row) * K + c] = x[r];
+    }
+  }
+}
+
+hipError_t launch_segment_bounds(int B, int T, int L, int S, int32_t* cu, hipStream_t st) {
+  const int n = B * S + 1;
+  segment_bounds_kernel<<<(n + 255) / 256, 256, 0, st>>>(B, T, L, S, cu);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_scan(const float* s0, const float* bst, const float* phi, float* X, float* sf, int B,
+                               int H, int K, int V, int S, hipStream_t st) {
+  const int grid = B * H * (V / 16);
+  if (K == 128)
+    segment_scan_kernel<128><<<grid, 256, 0, st>>>(s0, bst, phi, X, sf, H, V, S);
+  else
+    segment_scan_kernel<64><<<grid, 256, 0, st>>>(s0, bst, phi, X, sf, H, V, S);
+  return hipGetLastError();
+}
+
+}  // namespace comba

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define COMBA_ABI_VERSION 2
+#define COMBA_ABI_VERSION 3
 
 /* Status codes returned by every entry point. */
 enum {
@@ -179,6 +179,48 @@ int32_t comba_recurrent_step_fused(const void* q, const void* k, const void* v,
                                    int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
                                    int32_t in_dtype, int32_t out_dtype,
                                    void* o, float* final_state, uint32_t fusion, void* stream);
+
+/*
+ * Segment-parallel chunk forward for batches of few, long sequences
+ * (fixed-length batches only: no cu_seqlens). Same result as comba_chunk_fwd
+ * up to rounding order. The recurrence's state map over a stretch of tokens
+ * is affine in the state it starts from (Comba write-up, section
+ * "Comba架构：基于闭环控制理论": each step multiplies the state by
+ * alpha_t I - beta_t k_t k_t^T and adds beta_t v_t k_t^T), so every sequence is
+ * cut into S segments of L tokens (L a multiple of 64) that run in parallel:
+ *   1. each segment from a zero state gives its final state b_j;
+ *   2. each segment with v = 0 from the identity gives its K x K map Phi_j;
+ *   3. a scan X_{j+1} = X_j Phi_j + b_j (fp32), X_0 = initial_state, gives
+ *      every segment's true initial state and, as X_S, final_state;
+ *   4. each segment runs again from X_j and writes o.
+ * This is about three times the arithmetic of comba_chunk_fwd, spread over
+ * S times as many workgroups: it pays when B * H * ceil(V / 64) is well below
+ * the chip's 256 compute units.
+ *
+ * Arguments as comba_chunk_fwd (without cu_seqlens / num_seqs), plus:
+ *   num_segments  S per sequence; 0 chooses it: enough workgroups to fill 256
+ *                 compute units once, segments of at least 512 tokens.
+ *                 Capped at ceil(T / 64). When the plan has one segment the
+ *                 call is comba_chunk_fwd and uses no workspace.
+ *   workspace     device scratch of at least
+ *                 comba_chunk_fwd_segmented_workspace_size(B, T, H, K, V,
+ *                 num_segments) bytes, 256-byte aligned, not read before it is
+ *                 written; it holds the segment bounds, the b_j, Phi_j and X_j.
+ *   fusion        as for comba_chunk_fwd_fused, applied in every pass.
+ * Errors: as comba_chunk_fwd; COMBA_ERR_INVALID_ARG for num_segments < 0 or
+ * unknown fusion bits; COMBA_ERR_UNSUPPORTED when B * T exceeds 2^31 - 1.
+ * initial_state == final_state is allowed.
+ */
+size_t comba_chunk_fwd_segmented_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                                int32_t num_segments);
+
+int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v,
+                                  const float* alpha, const float* beta, const float* d,
+                                  const float* initial_state,
+                                  int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                  int32_t in_dtype, int32_t out_dtype,
+                                  void* o, float* final_state, int32_t num_segments,
+                                  void* workspace, size_t workspace_bytes, uint32_t fusion, void* stream);
 
 /*
  * Longest-first order of packed sequences (integer work, exact): writes into

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = comba.lib()
-    assert L.comba_abi_version() == 2
+    assert L.comba_abi_version() == 3
     assert api.status_string(0) == "COMBA_OK"
     assert api.status_string(-1) == "COMBA_ERR_INVALID_ARG"
     assert api.status_string(-2) == "COMBA_ERR_UNSUPPORTED"
@@ -72,6 +72,19 @@ def step(fusion=None, **kw):
     return L.comba_recurrent_step_fused(*a, fusion, None)
 
 
+def segmented(fusion=0, nseg=4, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, B=1, T=1000, H=2, K=64, V=64,
+                idt=0, odt=0, o=FAKE, sf=None, ws=FAKE, wsb=1 << 40)
+    args.update({k2: v2 for k2, v2 in kw.items() if k2 not in ("cu", "n")})
+    if "cu" in kw:  # no packed batches on this entry point: map the case onto an equivalent invalid one
+        args["B"] = 0
+    L = comba.lib()
+    return L.comba_chunk_fwd_segmented(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"],
+                                       args["s0"], args["B"], args["T"], args["H"], args["K"], args["V"],
+                                       args["idt"], args["odt"], args["o"], args["sf"], nseg, args["ws"],
+                                       args["wsb"], fusion, None)
+
+
 def chunk_fused(**kw):
     return chunk(fusion=api.COMBA_FUSE_GATE_LOGITS | api.COMBA_FUSE_QK_L2NORM, **kw)
 
@@ -80,7 +93,7 @@ def step_fused(**kw):
     return step(fusion=api.COMBA_FUSE_QK_L2NORM, **kw)
 
 
-@pytest.mark.parametrize("fn", [chunk, step, chunk_fused, step_fused])
+@pytest.mark.parametrize("fn", [chunk, step, chunk_fused, step_fused, segmented])
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
     (dict(beta=None), -1), (dict(d=None), -1), (dict(o=None), -1),
@@ -95,11 +108,30 @@ def test_invalid_arguments_are_rejected_before_launch(fn, kw, code):
     assert api.last_error() != ""
 
 
-@pytest.mark.parametrize("fn", [chunk, step])
-@pytest.mark.parametrize("fusion", [4, 8, 0x80000000, 0xFFFFFFFF])
+@pytest.mark.parametrize("fn", [chunk, step, segmented])
+@pytest.mark.parametrize("fusion", [4, 8, 1 << 16, 1 << 17, 1 << 18, 0x80000000, 0xFFFFFFFF])
 def test_unknown_fusion_bits_are_rejected(fn, fusion):
     assert fn(fusion=fusion) == api.COMBA_ERR_INVALID_ARG
     assert "fusion" in api.last_error()
+
+
+def test_segmented_plan_and_workspace():
+    ws = comba.segmented_workspace_size
+    # one 64K-token sequence of 16 heads: 32 workgroups, so 8 segments of 8192 tokens
+    assert ws(1, 65536, 16, 128, 128, 0) == 256 + 3 * 8 * 16 * 128 * 128 * 4
+    # the 1.3B layer already fills the chip: no segmentation, no workspace
+    assert ws(8, 4096, 16, 128, 128, 0) == 0
+    # explicit counts are capped at one chunk per segment: T = 100 allows 2
+    assert ws(1, 100, 2, 64, 64, 5) == ws(1, 100, 2, 64, 64, 2) > 0
+    assert ws(1, 100, 2, 64, 64, 1) == 0
+    # K != V: Phi is K x K, the states V x K
+    S = 4
+    assert ws(2, 4096, 3, 64, 128, S) == 256 + 2 * S * 3 * (2 * 128 * 64 + 64 * 64) * 4
+    # too small a workspace, negative counts, packed batches are not accepted
+    assert segmented(nseg=4, ws=FAKE, wsb=ws(1, 1000, 2, 64, 64, 4) - 1) == -3
+    assert segmented(nseg=4, ws=None, wsb=0) == -3
+    assert segmented(nseg=-1) == -1
+    assert segmented(B=2, T=(1 << 30)) == -2
 
 
 def test_workspace_rules():
