@@ -9,8 +9,9 @@ run and reported in GB/s under "decode". The same 1.3B-layer forward with
 input-side fusion (raw q/k normalised in the kernel, alpha/beta given as
 logits) is timed under "fused", beside the same preprocessing done by
 separate torch ops before an unfused call. The 64K-token single-sequence
-workload is timed plain and segment-parallel under "long_context" (context,
-not the metric). The fp64 CPU oracle is timed on
+workload is timed plain and segment-parallel under "long_context", and the
+1.3B layer with one q/k head shared by all value heads under "shared_qk"
+(context, not the metric). The fp64 CPU oracle is timed on
 the host cores on a bounded sample of the same workload ("cpu_baseline").
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -219,6 +220,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-shared-qk", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with a plain 256 MiB device copy (counter calibration runs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -345,6 +347,22 @@ def main():
                            "torch_preprocess_then_chunk_us": sms * 1e3,
                            "parity_sampled_o_rel_l2": oracle.rel_l2(fo[b:b + 1, :, h:h + 1], ro)}
         del tr
+
+    if not args.no_shared_qk:
+        # multi-value heads: one q / k head shared by the 16 value heads
+        si = make_inputs(w, qk_heads=1)
+        ts = device_inputs(si, torch, dev)
+
+        def sstep(_):
+            comba.chunk_fwd(ts["q"], ts["k"], ts["v"], ts["alpha"], ts["beta"], ts["d"], ts["s0"], out=o,
+                            final_state=sf)
+
+        qms, _ = time_loop(torch, sstep, max(args.steps // 2, 10), min(args.warmup, 50))
+        sbytes = nbytes - B * T * H * 2 * K * 2 * (H - 1) // H  # q, k read once per shared head
+        result["shared_qk"] = {"workload": "layer_1p3b with 1 q/k head for 16 value heads", "num_qk_heads": 1,
+                               "us_per_step": qms * 1e3, "tokens/s": B * T / (qms * 1e-3),
+                               "algorithmic_bytes": sbytes, "hbm_frac": sbytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del ts, si
 
     if not args.no_long:
         # one 64K-token sequence: 32 workgroups plain, segment-parallel fills the chip

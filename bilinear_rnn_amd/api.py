@@ -28,8 +28,9 @@ COMBA_FUSE_GATE_LOGITS = 1
 COMBA_FUSE_QK_L2NORM = 2
 
 EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
-            "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_chunk_fwd_fused",
-            "comba_recurrent_step", "comba_recurrent_step_fused", "comba_chunk_fwd_segmented_workspace_size",
+            "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_chunk_fwd_fused", "comba_chunk_fwd_ex",
+            "comba_recurrent_step", "comba_recurrent_step_fused", "comba_recurrent_step_ex",
+            "comba_chunk_fwd_segmented_workspace_size",
             "comba_chunk_fwd_segmented", "comba_varlen_order")
 
 
@@ -74,7 +75,13 @@ def lib() -> ctypes.CDLL:
         L.comba_recurrent_step_fused.restype = i32
         L.comba_chunk_fwd_segmented_workspace_size.argtypes = [i32] * 6
         L.comba_chunk_fwd_segmented_workspace_size.restype = sz
-        L.comba_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, i32,
+        L.comba_chunk_fwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                         i32, i32, vp, fp, vp, sz, ctypes.c_uint32, vp]
+        L.comba_chunk_fwd_ex.restype = i32
+        L.comba_recurrent_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32,
+                                              i32, i32, vp, fp, ctypes.c_uint32, vp]
+        L.comba_recurrent_step_ex.restype = i32
+        L.comba_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                 vp, fp, i32, vp, sz, ctypes.c_uint32, vp]
         L.comba_chunk_fwd_segmented.restype = i32
         L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
@@ -120,11 +127,13 @@ def _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype):
     if q.dtype not in _DT:
         raise ValueError(f"q must be bfloat16 or float32 (got {q.dtype})")
     if q.dim() != 4 or v.dim() != 4:
-        raise ValueError("q, k must be [B, T, H, K] and v [B, T, H, V]")
-    B, T, H, K = q.shape
-    V = v.shape[-1]
+        raise ValueError("q, k must be [B, T, Hqk, K] and v [B, T, H, V]")
+    B, T, Hk, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    if H % Hk != 0:
+        raise ValueError(f"the q/k head count {Hk} must divide the value head count {H}")
     _require(q, "q", q.dtype)
-    _require(k, "k", q.dtype, (B, T, H, K))
+    _require(k, "k", q.dtype, (B, T, Hk, K))
     _require(v, "v", q.dtype, (B, T, H, V))
     _require(alpha, "alpha", torch.float32, (B, T, H))
     _require(beta, "beta", torch.float32, (B, T, H))
@@ -139,7 +148,7 @@ def _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype):
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DT:
         raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
-    return B, T, H, K, V, N, out_dtype
+    return B, T, H, Hk, K, V, N, out_dtype
 
 
 def _fusion(gate_logits: bool, qk_l2norm: bool) -> int:
@@ -161,12 +170,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               segments: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunk-wise forward through ``comba_chunk_fwd``. Returns (o, final_state).
 
+    q and k may hold fewer heads than v (a divisor of H): consecutive value
+    heads then share one q / k head (``comba_chunk_fwd_ex``).
+
     ``gate_logits``: alpha and beta hold pre-sigmoid logits; ``qk_l2norm``: q
     and k are L2-normalised per head and token inside the kernel. Either flag
     routes the call through ``comba_chunk_fwd_fused``. ``segments`` (an int,
     0 = automatic; fixed-length batches only) routes it through the
     segment-parallel ``comba_chunk_fwd_segmented``."""
-    B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     L = lib()
     if out is None:
         out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
@@ -185,8 +197,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
         with torch.cuda.device(q.device):
             stream = torch.cuda.current_stream(q.device).cuda_stream
             _check(L.comba_chunk_fwd_segmented(
-                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state), B, T, H, K, V,
-                _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state), int(segments), _ptr(workspace),
+                _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state), B, T, H, Hk, K,
+                V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state), int(segments), _ptr(workspace),
                 0 if workspace is None else workspace.numel(), fusion, ctypes.c_void_p(stream)))
         return out, final_state
     nws = int(L.comba_chunk_fwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0, _DT[q.dtype]))
@@ -194,14 +206,16 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
-                _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
-                _DT[out_dtype], _ptr(out), _ptr(final_state), _ptr(workspace),
+        head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
+                _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H)
+        tail = (K, V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state), _ptr(workspace),
                 0 if workspace is None else workspace.numel())
-        if fusion:
-            _check(L.comba_chunk_fwd_fused(*args, fusion, ctypes.c_void_p(stream)))
+        if Hk != H:
+            _check(L.comba_chunk_fwd_ex(*head, Hk, *tail, fusion, ctypes.c_void_p(stream)))
+        elif fusion:
+            _check(L.comba_chunk_fwd_fused(*head, *tail, fusion, ctypes.c_void_p(stream)))
         else:
-            _check(L.comba_chunk_fwd(*args, ctypes.c_void_p(stream)))
+            _check(L.comba_chunk_fwd(*head, *tail, ctypes.c_void_p(stream)))
     return out, final_state
 
 
@@ -217,7 +231,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
     With ``in_place`` the state is updated in ``initial_state`` itself.
     ``gate_logits`` and ``qk_l2norm`` as in ``chunk_fwd`` (through
     ``comba_recurrent_step_fused``)."""
-    B, T, H, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     L = lib()
     if out is None:
         out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
@@ -233,13 +247,15 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
     fusion = _fusion(gate_logits, qk_l2norm)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        args = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
-                _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
-                _DT[out_dtype], _ptr(out), _ptr(final_state))
-        if fusion:
-            _check(L.comba_recurrent_step_fused(*args, fusion, ctypes.c_void_p(stream)))
+        head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
+                _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H)
+        tail = (K, V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state))
+        if Hk != H:
+            _check(L.comba_recurrent_step_ex(*head, Hk, *tail, fusion, ctypes.c_void_p(stream)))
+        elif fusion:
+            _check(L.comba_recurrent_step_fused(*head, *tail, fusion, ctypes.c_void_p(stream)))
         else:
-            _check(L.comba_recurrent_step(*args, ctypes.c_void_p(stream)))
+            _check(L.comba_recurrent_step(*head, *tail, ctypes.c_void_p(stream)))
     return out, final_state
 
 

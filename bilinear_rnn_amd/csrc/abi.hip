@@ -29,7 +29,7 @@ bool supported_dim(int32_t x) { return x == 64 || x == 128; }
 // Common argument checks; fills a with everything but the workspace.
 int32_t check_args(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                    const float* d, const float* s0, const int32_t* cu, int32_t num_seqs, int32_t B,
-                   int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
+                   int32_t T, int32_t H, int32_t Hk, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
                    void* o, float* sf, comba::FwdArgs& a) {
   if (!q || !k || !v || !alpha || !beta || !d || !o)
     return fail(COMBA_ERR_INVALID_ARG, "q, k, v, alpha, beta, d and o must be non-NULL");
@@ -37,6 +37,8 @@ int32_t check_args(const void* q, const void* k, const void* v, const float* alp
     return fail(COMBA_ERR_INVALID_ARG, "in_dtype and out_dtype must be COMBA_BF16 or COMBA_FP32");
   if (B < 1 || H < 1 || K < 1 || V < 1)
     return fail(COMBA_ERR_INVALID_ARG, "B, H, K and V must be >= 1");
+  if (Hk < 1 || H % Hk != 0)
+    return fail(COMBA_ERR_INVALID_ARG, "num_qk_heads must be >= 1 and divide H");
   if (cu) {
     if (B != 1) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens requires B == 1");
     if (num_seqs < 1) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens requires num_seqs >= 1");
@@ -58,7 +60,7 @@ int32_t check_args(const void* q, const void* k, const void* v, const float* alp
     if (s0b < sfb + bytes && sfb < s0b + bytes)
       return fail(COMBA_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
   }
-  a = comba::FwdArgs{q, k, v, alpha, beta, d, s0, cu, nullptr, static_cast<int>(N), B, T, H, K, V,
+  a = comba::FwdArgs{q, k, v, alpha, beta, d, s0, cu, nullptr, static_cast<int>(N), B, T, H, K, V, Hk,
                      in_dtype, out_dtype, o, sf, 0u};
   return COMBA_OK;
 }
@@ -102,12 +104,12 @@ constexpr uint32_t kKnownFusion = COMBA_FUSE_GATE_LOGITS | COMBA_FUSE_QK_L2NORM;
 
 int32_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                        const float* d, const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
-                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                       int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t K, int32_t V, int32_t in_dtype,
                        int32_t out_dtype, void* o, float* final_state, void* workspace, size_t workspace_bytes,
                        uint32_t fusion, void* stream) {
   if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
   comba::FwdArgs a;
-  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, Hk, K, V,
                           in_dtype, out_dtype, o, final_state, a);
   if (rc != COMBA_OK) return rc;
   a.fusion = fusion;
@@ -127,11 +129,11 @@ int32_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float*
 
 int32_t recurrent_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
                        const float* d, const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
-                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                       int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t K, int32_t V, int32_t in_dtype,
                        int32_t out_dtype, void* o, float* final_state, uint32_t fusion, void* stream) {
   if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
   comba::FwdArgs a;
-  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V,
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, Hk, K, V,
                           in_dtype, out_dtype, o, final_state, a);
   if (rc != COMBA_OK) return rc;
   a.fusion = fusion;
@@ -146,7 +148,7 @@ COMBA_API int32_t comba_chunk_fwd(const void* q, const void* k, const void* v, c
                                   int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
                                   void* o, float* final_state, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
                         out_dtype, o, final_state, workspace, workspace_bytes, 0u, stream);
 }
 
@@ -156,8 +158,18 @@ COMBA_API int32_t comba_chunk_fwd_fused(const void* q, const void* k, const void
                                         int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
                                         void* o, float* final_state, void* workspace, size_t workspace_bytes,
                                         uint32_t fusion, void* stream) {
-  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
                         out_dtype, o, final_state, workspace, workspace_bytes, fusion, stream);
+}
+
+COMBA_API int32_t comba_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+                                     const float* beta, const float* d, const float* initial_state,
+                                     const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                                     int32_t num_qk_heads, int32_t K, int32_t V, int32_t in_dtype,
+                                     int32_t out_dtype, void* o, float* final_state, void* workspace,
+                                     size_t workspace_bytes, uint32_t fusion, void* stream) {
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, num_qk_heads, K, V,
+                        in_dtype, out_dtype, o, final_state, workspace, workspace_bytes, fusion, stream);
 }
 
 COMBA_API int32_t comba_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
@@ -165,7 +177,7 @@ COMBA_API int32_t comba_recurrent_step(const void* q, const void* k, const void*
                                        const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
                                        int32_t H, int32_t K, int32_t V, int32_t in_dtype,
                                        int32_t out_dtype, void* o, float* final_state, void* stream) {
-  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
                         out_dtype, o, final_state, 0u, stream);
 }
 
@@ -175,8 +187,18 @@ COMBA_API int32_t comba_recurrent_step_fused(const void* q, const void* k, const
                                              int32_t H, int32_t K, int32_t V, int32_t in_dtype,
                                              int32_t out_dtype, void* o, float* final_state, uint32_t fusion,
                                              void* stream) {
-  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype,
+  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
                         out_dtype, o, final_state, fusion, stream);
+}
+
+COMBA_API int32_t comba_recurrent_step_ex(const void* q, const void* k, const void* v, const float* alpha,
+                                          const float* beta, const float* d, const float* initial_state,
+                                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                          int32_t H, int32_t num_qk_heads, int32_t K, int32_t V, int32_t in_dtype,
+                                          int32_t out_dtype, void* o, float* final_state, uint32_t fusion,
+                                          void* stream) {
+  return recurrent_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, num_qk_heads, K, V,
+                        in_dtype, out_dtype, o, final_state, fusion, stream);
 }
 
 namespace {
@@ -231,22 +253,23 @@ COMBA_API size_t comba_chunk_fwd_segmented_workspace_size(int32_t B, int32_t T, 
 
 COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v, const float* alpha,
                                             const float* beta, const float* d, const float* initial_state,
-                                            int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                            int32_t B, int32_t T, int32_t H, int32_t num_qk_heads, int32_t K,
+                                            int32_t V,
                                             int32_t in_dtype, int32_t out_dtype, void* o, float* final_state,
                                             int32_t num_segments, void* workspace, size_t workspace_bytes,
                                             uint32_t fusion, void* stream) {
   if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
   if (num_segments < 0) return fail(COMBA_ERR_INVALID_ARG, "num_segments must be >= 0 (0: automatic)");
   comba::FwdArgs a;
-  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, nullptr, 0, B, T, H, K, V, in_dtype, out_dtype,
-                          o, final_state, a);
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, nullptr, 0, B, T, H, num_qk_heads, K, V,
+                          in_dtype, out_dtype, o, final_state, a);
   if (rc != COMBA_OK) return rc;
   if (static_cast<int64_t>(B) * T > INT_MAX)
     return fail(COMBA_ERR_UNSUPPORTED, "B * T above 2^31 - 1 tokens");
   const SegPlan p = plan_segments(B, T, H, V, num_segments);
   if (p.S <= 1)
-    return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, nullptr, 0, B, T, H, K, V, in_dtype, out_dtype, o,
-                          final_state, nullptr, 0, fusion, stream);
+    return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, nullptr, 0, B, T, H, num_qk_heads, K, V, in_dtype,
+                          out_dtype, o, final_state, nullptr, 0, fusion, stream);
   const int NS = B * p.S;
   if (static_cast<int64_t>(NS) * H * 2 > INT_MAX / 16)
     return fail(COMBA_ERR_UNSUPPORTED, "too many (segment, head) pairs for one launch");

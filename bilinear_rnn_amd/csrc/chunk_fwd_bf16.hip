@@ -545,7 +545,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ order, int T, int H, int N, OutT* __restrict__ o,
+    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
     float* __restrict__ sf, unsigned fusion) {
   static_assert(VT == 64, "four consumer wavefronts of 16 channels");
   constexpr int NVT = V / VT;
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   int unit, vt;
   if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
-  const int h = unit % H;
+  const int h = unit % H, hk = h / (H / Hk);
   int n = unit / H;
   if (order) n = __builtin_amdgcn_readfirstlane(order[n]);
   int b, t0, t1;
@@ -603,7 +603,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < QPT; ++j) {
       const int piece = ptid + j * 256, row = piece / KP, c8 = piece % KP;
-      qkoff[j] = (row * H * K + c8 * 8) * 2;
+      qkoff[j] = (row * Hk * K + c8 * 8) * 2;
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -612,13 +612,14 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     }
     auto fetch = [&](int c0) {
       const int nrows = min(64, t1 - c0);
-      const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;  // token c0, head h
+      const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;      // token c0, value head h
+      const int64_t tqk0 = (static_cast<int64_t>(b) * T + c0) * Hk + hk;    // token c0, its q / k head
       const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(const_cast<u16*>(q + tok0 * K)), static_cast<short>(0),
-          __builtin_amdgcn_readfirstlane(nrows * H * K * 2), kBufferWord3);
+          uniform_ptr(const_cast<u16*>(q + tqk0 * K)), static_cast<short>(0),
+          __builtin_amdgcn_readfirstlane(nrows * Hk * K * 2), kBufferWord3);
       const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-          uniform_ptr(const_cast<u16*>(k + tok0 * K)), static_cast<short>(0),
-          __builtin_amdgcn_readfirstlane(nrows * H * K * 2), kBufferWord3);
+          uniform_ptr(const_cast<u16*>(k + tqk0 * K)), static_cast<short>(0),
+          __builtin_amdgcn_readfirstlane(nrows * Hk * K * 2), kBufferWord3);
       const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
           uniform_ptr(const_cast<u16*>(v + tok0 * V + vt * VT)), static_cast<short>(0),
           __builtin_amdgcn_readfirstlane((fusion & kModeZeroV) ? 0 : nrows * H * V * 2), kBufferWord3);
@@ -984,7 +985,7 @@ static hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t st) {
   const int units = a.N * a.H;
   chunk_fwd_bf16_kernel<K, V, VT, OutT, NORM><<<xcd_grid(units, NVT), 512, 0, st>>>(
       static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.alpha,
-      a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
+      a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
   return hipGetLastError();
 }
 

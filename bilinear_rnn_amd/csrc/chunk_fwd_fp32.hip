@@ -30,14 +30,14 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ order, int T, int H, int N, OutT* __restrict__ o,
+    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
     float* __restrict__ sf, unsigned fusion) {
   constexpr int NT = 256, VT = SmemF32<K>::VT, LDH = SmemF32<K>::LDH, NVT = V / VT, LQ = K + 1;
   __shared__ SmemF32<K> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   int unit, vt;
   if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
-  const int h = unit % H;
+  const int h = unit % H, hk = h / (H / Hk);
   int n = unit / H;
   if (order) n = order[n];
   int b, t0, t1;
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     __syncthreads();
     for (int e = tid; e < 64 * K; e += NT) {
       const int row = e / K, c = e % K, t = c0 + row;
-      const int64_t off = ((static_cast<int64_t>(b) * T + t) * H + h) * K + c;
+      const int64_t off = ((static_cast<int64_t>(b) * T + t) * Hk + hk) * K + c;
       sm.Qs[row * LQ + c] = row < nrows ? q[off] : 0.f;
       sm.Ks[row * LQ + c] = row < nrows ? k[off] : 0.f;
     }
@@ -170,7 +170,7 @@ static hipError_t launch_f32_t(const FwdArgs& a, hipStream_t st) {
   constexpr int NVT = V / SmemF32<K>::VT;
   chunk_fwd_fp32_kernel<K, V, OutT><<<xcd_grid(a.N * a.H, NVT), 256, 0, st>>>(
       static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
+      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
   return hipGetLastError();
 }
 

@@ -23,6 +23,7 @@ struct FwdArgs {
   const int32_t* cu_seqlens;  // may be null
   const int32_t* order;       // longest-first sequence order, may be null
   int N, B, T, H, K, V;
+  int Hk;                     // q / k heads (H % Hk == 0): value head h reads q / k head h / (H / Hk)
   int in_dtype, out_dtype;    // COMBA_BF16 / COMBA_FP32
   void* o;
   float* sf;                  // may be null

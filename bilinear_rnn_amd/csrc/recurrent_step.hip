@@ -48,14 +48,14 @@ template <int K, int V, int VB, typename InT, typename OutT>
 __global__ __launch_bounds__(256) void recurrent_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
-    const float* s0, const int32_t* __restrict__ cu_seqlens, int T, int H,
+    const float* s0, const int32_t* __restrict__ cu_seqlens, int T, int H, int Hk,
     OutT* __restrict__ o, float* sf, unsigned fusion) {
   constexpr int F4 = K / 64;   // 16-byte pieces per lane and row
   constexpr int RPP = 16;       // rows per pass: 4 per wavefront
   constexpr int NP = VB / RPP;  // passes
   constexpr int NB = V / VB;    // row blocks per (sequence, head)
   const int vb = blockIdx.x % NB;
-  const int h = (blockIdx.x / NB) % H;
+  const int h = (blockIdx.x / NB) % H, hk = h / (H / Hk);
   const int n = blockIdx.x / (NB * H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int rw = lane >> 4, j = lane & 15;
@@ -75,13 +75,14 @@ __global__ __launch_bounds__(256) void recurrent_kernel(
   const float dh = d[h];
 
   for (int t = t0; t < t1; ++t) {
-    const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;
+    const int64_t tok = (static_cast<int64_t>(b) * T + t) * H + h;     // value head h
+    const int64_t tqk = (static_cast<int64_t>(b) * T + t) * Hk + hk;   // its q / k head
     float kk[F4][4], qt[F4][4];
     float kq = 0.f;
 #pragma unroll
     for (int f = 0; f < F4; ++f) {
-      Load4<InT>::get(k, tok * K + 4 * j + 64 * f, kk[f]);
-      Load4<InT>::get(q, tok * K + 4 * j + 64 * f, qt[f]);
+      Load4<InT>::get(k, tqk * K + 4 * j + 64 * f, kk[f]);
+      Load4<InT>::get(q, tqk * K + 4 * j + 64 * f, qt[f]);
     }
     if (fusion & kFuseQkL2Norm) {  // q, k / sqrt(sum of squares + eps), in float32
       float sk = 0.f, sq = 0.f;
@@ -157,7 +158,7 @@ static hipError_t launch_rec_t(const FwdArgs& a, hipStream_t st) {
   const int grid = a.N * a.H * (V / VB);
   recurrent_kernel<K, V, VB, InT, OutT><<<grid, 256, 0, st>>>(
       static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v),
-      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.T, a.H, static_cast<OutT*>(a.o), a.sf, a.fusion);
+      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.T, a.H, a.Hk, static_cast<OutT*>(a.o), a.sf, a.fusion);
   return hipGetLastError();
 }
 

@@ -104,8 +104,8 @@ class Inputs:
     """One batch. Floating tensors are float32 numpy arrays holding exactly the
     values the device receives (bf16 workloads are already rounded);
     ``*_bits`` carry the bf16 bit patterns for the device copy."""
-    q: np.ndarray                   # [B, T, H, K]
-    k: np.ndarray                   # [B, T, H, K]
+    q: np.ndarray                   # [B, T, Hqk, K] (Hqk = H unless q / k heads are shared)
+    k: np.ndarray                   # [B, T, Hqk, K]
     v: np.ndarray                   # [B, T, H, V]
     alpha: np.ndarray               # [B, T, H]
     beta: np.ndarray                # [B, T, H]
@@ -126,8 +126,12 @@ class Inputs:
 def make_inputs(w: Workload, *, B: Optional[int] = None, T: Optional[int] = None,
                 H: Optional[int] = None, num_seqs: Optional[int] = None,
                 seed: Optional[int] = None, s0_std: Optional[float] = None,
-                lengths: Optional[np.ndarray] = None, raw: bool = False) -> Inputs:
-    """Draw the inputs of workload ``w``; keyword overrides shrink it for tests."""
+                lengths: Optional[np.ndarray] = None, raw: bool = False,
+                qk_heads: Optional[int] = None) -> Inputs:
+    """Draw the inputs of workload ``w``; keyword overrides shrink it for tests.
+
+    ``qk_heads`` (a divisor of H) draws q and k with that many heads, shared by
+    consecutive value heads; v, alpha, beta, d and the state keep H heads."""
     B = w.B if B is None else B
     T = w.T if T is None else T
     H = w.H if H is None else H
@@ -147,8 +151,10 @@ def make_inputs(w: Workload, *, B: Optional[int] = None, T: Optional[int] = None
         B, T, nseq = 1, int(cu[-1]), len(lengths)
 
     K, V = w.K, w.V
-    q = rng.standard_normal((B, T, H, K), dtype=np.float32)
-    k = rng.standard_normal((B, T, H, K), dtype=np.float32)
+    Hk = H if qk_heads is None else qk_heads
+    assert H % Hk == 0
+    q = rng.standard_normal((B, T, Hk, K), dtype=np.float32)
+    k = rng.standard_normal((B, T, Hk, K), dtype=np.float32)
     v = rng.standard_normal((B, T, H, V), dtype=np.float32)
     a_logit = rng.standard_normal((B, T, H), dtype=np.float32) * np.float32(0.5) + np.float32(w.alpha_mu)
     b_logit = rng.standard_normal((B, T, H), dtype=np.float32)

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define COMBA_ABI_VERSION 3
+#define COMBA_ABI_VERSION 4
 
 /* Status codes returned by every entry point. */
 enum {
@@ -181,6 +181,35 @@ int32_t comba_recurrent_step_fused(const void* q, const void* k, const void* v,
                                    void* o, float* final_state, uint32_t fusion, void* stream);
 
 /*
+ * Shared q / k heads (the Comba write-up, section "硬件高效的分块并行计算",
+ * last paragraph: the Mamba-form models share a query and key of dimension
+ * 128 across value heads, like multi-value attention; the GLA/KDA blog,
+ * section 4.2: grouped value attention). q and k hold num_qk_heads heads,
+ * [B, T, num_qk_heads, K]; v, o, alpha, beta, d and the states keep H value
+ * heads, and value head h reads q / k head h / (H / num_qk_heads)
+ * (consecutive value heads share one q / k head). num_qk_heads must divide
+ * H; num_qk_heads == H is the plain layout. Otherwise as comba_chunk_fwd_fused
+ * and comba_recurrent_step_fused. COMBA_FUSE_QK_L2NORM normalises each
+ * shared q / k row.
+ */
+int32_t comba_chunk_fwd_ex(const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* d,
+                           const float* initial_state,
+                           const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t B, int32_t T, int32_t H, int32_t num_qk_heads, int32_t K, int32_t V,
+                           int32_t in_dtype, int32_t out_dtype,
+                           void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, uint32_t fusion, void* stream);
+
+int32_t comba_recurrent_step_ex(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* d,
+                                const float* initial_state,
+                                const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t B, int32_t T, int32_t H, int32_t num_qk_heads, int32_t K, int32_t V,
+                                int32_t in_dtype, int32_t out_dtype,
+                                void* o, float* final_state, uint32_t fusion, void* stream);
+
+/*
  * Segment-parallel chunk forward for batches of few, long sequences
  * (fixed-length batches only: no cu_seqlens). Same result as comba_chunk_fwd
  * up to rounding order. The recurrence's state map over a stretch of tokens
@@ -197,7 +226,7 @@ int32_t comba_recurrent_step_fused(const void* q, const void* k, const void* v,
  * S times as many workgroups: it pays when B * H * ceil(V / 64) is well below
  * the chip's 256 compute units.
  *
- * Arguments as comba_chunk_fwd (without cu_seqlens / num_seqs), plus:
+ * Arguments as comba_chunk_fwd_ex (without cu_seqlens / num_seqs), plus:
  *   num_segments  S per sequence; 0 chooses it: enough workgroups to fill 256
  *                 compute units once, segments of at least 512 tokens.
  *                 Capped at ceil(T / 64). When the plan has one segment the
@@ -217,7 +246,7 @@ size_t comba_chunk_fwd_segmented_workspace_size(int32_t B, int32_t T, int32_t H,
 int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                   const float* alpha, const float* beta, const float* d,
                                   const float* initial_state,
-                                  int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                  int32_t B, int32_t T, int32_t H, int32_t num_qk_heads, int32_t K, int32_t V,
                                   int32_t in_dtype, int32_t out_dtype,
                                   void* o, float* final_state, int32_t num_segments,
                                   void* workspace, size_t workspace_bytes, uint32_t fusion, void* stream);

@@ -136,6 +136,22 @@ def comba_forward_chunked(q, k, v, alpha, beta, d, s0=None, cu_seqlens=None,
     return o, s_final
 
 
+def expand_shared_qk(q, k, H: int):
+    """q, k with Hqk heads shared by H value heads -> one q, k head per value head.
+
+    The Comba write-up (section "硬件高效的分块并行计算", last paragraph) has its
+    Mamba-form models share one query and key across value heads, like
+    multi-value attention. Value head h reads q / k head h // (H // Hqk):
+    consecutive value heads share a head. With Hqk == H this is the identity.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    Hk = q.shape[2]
+    if H % Hk != 0:
+        raise ValueError("the q/k head count must divide H")
+    return np.repeat(q, H // Hk, axis=2), np.repeat(k, H // Hk, axis=2)
+
+
 L2NORM_EPS = 1e-6
 
 

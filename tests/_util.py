@@ -33,6 +33,8 @@ def oracle_of(inp, heads=None, seqs=None, nthreads=0, gate_logits=None, qk_l2nor
     q, k, v, a, b, d, s0 = inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, inp.s0
     gate_logits = inp.raw if gate_logits is None else gate_logits
     qk_l2norm = inp.raw if qk_l2norm is None else qk_l2norm
+    if q.shape[2] != v.shape[2]:  # q / k heads shared by several value heads
+        q, k = oracle.expand_shared_qk(q, k, v.shape[2])
     cu = inp.cu_seqlens
     if seqs is not None:
         assert cu is None

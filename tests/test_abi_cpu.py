@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = comba.lib()
-    assert L.comba_abi_version() == 3
+    assert L.comba_abi_version() == 4
     assert api.status_string(0) == "COMBA_OK"
     assert api.status_string(-1) == "COMBA_ERR_INVALID_ARG"
     assert api.status_string(-2) == "COMBA_ERR_UNSUPPORTED"
@@ -80,8 +80,9 @@ def segmented(fusion=0, nseg=4, **kw):
         args["B"] = 0
     L = comba.lib()
     return L.comba_chunk_fwd_segmented(args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"],
-                                       args["s0"], args["B"], args["T"], args["H"], args["K"], args["V"],
-                                       args["idt"], args["odt"], args["o"], args["sf"], nseg, args["ws"],
+                                       args["s0"], args["B"], args["T"], args["H"], args.get("Hk", args["H"]),
+                                       args["K"], args["V"], args["idt"], args["odt"], args["o"], args["sf"],
+                                       nseg, args["ws"],
                                        args["wsb"], fusion, None)
 
 
@@ -132,6 +133,36 @@ def test_segmented_plan_and_workspace():
     assert segmented(nseg=4, ws=None, wsb=0) == -3
     assert segmented(nseg=-1) == -1
     assert segmented(B=2, T=(1 << 30)) == -2
+
+
+def _ex(fn_name, Hk, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=16, H=4, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None)
+    args.update(kw)
+    a = (args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"], args["s0"], args["cu"],
+         args["n"], args["B"], args["T"], args["H"], Hk, args["K"], args["V"], args["idt"], args["odt"],
+         args["o"], args["sf"])
+    L = comba.lib()
+    if fn_name == "chunk":
+        return L.comba_chunk_fwd_ex(*a, None, 0, 0, None)
+    return L.comba_recurrent_step_ex(*a, 0, None)
+
+
+@pytest.mark.parametrize("fn_name", ["chunk", "step"])
+@pytest.mark.parametrize("Hk", [0, -1, 3, 8])
+def test_qk_heads_must_divide_value_heads(fn_name, Hk):
+    assert _ex(fn_name, Hk) == api.COMBA_ERR_INVALID_ARG
+    assert "num_qk_heads" in api.last_error()
+
+
+@pytest.mark.parametrize("fn_name", ["chunk", "step"])
+def test_qk_heads_other_errors_still_reported(fn_name):
+    assert _ex(fn_name, 2, q=None) == api.COMBA_ERR_INVALID_ARG
+    assert _ex(fn_name, 2, K=96) == api.COMBA_ERR_UNSUPPORTED
+
+
+def test_segmented_qk_heads_checked():
+    assert segmented(Hk=3, H=4) == api.COMBA_ERR_INVALID_ARG
 
 
 def test_workspace_rules():

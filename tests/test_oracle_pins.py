@@ -387,3 +387,32 @@ def test_fused_inputs_make_the_forward_scale_invariant_in_q_and_k():
                            np.maximum(beta, 1e-3), d, S0)
     for x, y in zip(ref, direct):
         assert rel_l2(x, y) < 1e-6
+
+
+# --- q / k heads shared by several value heads -----------------------------------------
+
+def test_shared_qk_expansion_groups_consecutive_value_heads():
+    rng = np.random.default_rng(51)
+    B, T, H, Hk, K, V = 1, 9, 6, 2, 4, 3
+    q = rng.standard_normal((B, T, Hk, K))
+    k = rng.standard_normal((B, T, Hk, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, V))
+    alpha = rng.uniform(0.7, 1.0, (B, T, H))
+    beta = rng.uniform(0.0, 1.0, (B, T, H))
+    d = rng.uniform(-1, 1, (H,))
+    qe, ke = oracle.expand_shared_qk(q, k, H)
+    o, s = comba_forward(qe, ke, v, alpha, beta, d)
+    # each value head, run alone with the q / k head of its group (h // 3)
+    for h in range(H):
+        g = h // (H // Hk)
+        oh, sh = comba_forward(q[:, :, g:g + 1], k[:, :, g:g + 1], v[:, :, h:h + 1], alpha[:, :, h:h + 1],
+                               beta[:, :, h:h + 1], d[h:h + 1])
+        np.testing.assert_allclose(o[:, :, h:h + 1], oh, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(s[:, h:h + 1], sh, rtol=1e-13, atol=1e-13)
+    # one q / k head per value head is the plain layout
+    q6, k6 = oracle.expand_shared_qk(qe, ke, H)
+    np.testing.assert_array_equal(q6, qe)
+    np.testing.assert_array_equal(k6, ke)
+    with pytest.raises(ValueError):
+        oracle.expand_shared_qk(q[:, :, :1].repeat(4, axis=2), k[:, :, :1].repeat(4, axis=2), H)
