@@ -20,7 +20,7 @@ from typing import Optional
 
 import numpy as np
 
-from .reference import comba_forward, comba_forward_chunked, expand_shared_qk, fused_inputs, rel_l2  # noqa: F401
+from .reference import comba_backward, comba_forward, comba_forward_chunked, expand_shared_qk, fused_inputs, rel_l2  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "comba_oracle.c")

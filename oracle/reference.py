@@ -136,6 +136,74 @@ def comba_forward_chunked(q, k, v, alpha, beta, d, s0=None, cu_seqlens=None,
     return o, s_final
 
 
+def comba_backward(q, k, v, alpha, beta, d, do, s0=None, dsf=None, cu_seqlens=None):
+    """Gradients of the token recurrence of :func:`comba_forward`, in fp64.
+
+    Reverse-mode differentiation of the definition, one token at a time and
+    backwards, for a loss L with dL/do = ``do`` [B, T, H, V] and dL/dS_final =
+    ``dsf`` [N, H, V, K] (None: 0). Per head, with S_t the V x K state, a_t =
+    S_{t-1} k_t, u_t = v_t - a_t, S_t = alpha_t S_{t-1} + beta_t u_t k_t^T,
+    qt_t = q_t - d k_t and o_t = S_t qt_t, and X the running dL/dS_t:
+
+        X     += do_t qt_t^T                 (o_t reads S_t)
+        dqt    = S_t^T do_t   ->  dq_t = dqt, dk_t -= d dqt, dd -= dqt . k_t
+        dalpha_t = <X, S_{t-1}>,   dbeta_t = u_t . (X k_t)
+        du     = beta_t X k_t     ->  dv_t = du, da = -du
+        dk_t  += beta_t X^T u_t + S_{t-1}^T da
+        X      = alpha_t X + da k_t^T        (dL/dS_{t-1})
+
+    and dS_0 is X after the first token. The states S_{t-1} are kept from a
+    forward pass over the sequence.
+
+    Returns a dict of float64 arrays: dq, dk, dv, dalpha, dbeta ([B, T, H, ...]),
+    dd [H] (summed over the batch) and ds0 [N, H, V, K].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    alpha = np.asarray(alpha, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    d = np.asarray(d, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    N = B if cu_seqlens is None else len(cu_seqlens) - 1
+    g = {name: np.zeros_like(x) for name, x in (("dq", q), ("dk", k), ("dv", v), ("dalpha", alpha),
+                                                  ("dbeta", beta))}
+    g["dd"] = np.zeros((H,))
+    g["ds0"] = np.zeros((N, H, V, K))
+    for n, b, t0, t1 in _segments(B, T, cu_seqlens):
+        S = np.zeros((H, V, K)) if s0 is None else np.array(s0[n], dtype=np.float64)
+        states = [S]
+        for t in range(t0, t1):  # forward, keeping every state
+            kk = k[b, t]
+            u = v[b, t] - np.einsum("hvk,hk->hv", S, kk)
+            S = alpha[b, t][:, None, None] * S + beta[b, t][:, None, None] * u[:, :, None] * kk[:, None, :]
+            states.append(S)
+        X = np.zeros((H, V, K)) if dsf is None else np.array(dsf[n], dtype=np.float64)
+        for t in range(t1 - 1, t0 - 1, -1):
+            S_prev, S_t = states[t - t0], states[t - t0 + 1]
+            kk, qv, al, be = k[b, t], q[b, t], alpha[b, t], beta[b, t]
+            qt = qv - d[:, None] * kk
+            dot = do[b, t]                                           # [H, V]
+            X = X + dot[:, :, None] * qt[:, None, :]
+            dqt = np.einsum("hvk,hv->hk", S_t, dot)
+            g["dq"][b, t] += dqt
+            g["dk"][b, t] -= d[:, None] * dqt
+            g["dd"] -= np.einsum("hk,hk->h", dqt, kk)
+            u = v[b, t] - np.einsum("hvk,hk->hv", S_prev, kk)
+            Xk = np.einsum("hvk,hk->hv", X, kk)
+            g["dalpha"][b, t] += np.einsum("hvk,hvk->h", X, S_prev)
+            g["dbeta"][b, t] += np.einsum("hv,hv->h", u, Xk)
+            du = be[:, None] * Xk
+            g["dv"][b, t] += du
+            da = -du
+            g["dk"][b, t] += be[:, None] * np.einsum("hvk,hv->hk", X, u) + np.einsum("hvk,hv->hk", S_prev, da)
+            X = al[:, None, None] * X + da[:, :, None] * kk[:, None, :]
+        g["ds0"][n] = X
+    return g
+
+
 def expand_shared_qk(q, k, H: int):
     """q, k with Hqk heads shared by H value heads -> one q, k head per value head.
 

@@ -41,6 +41,14 @@ MUTATIONS = {
     "l2norm_k_by_q_norm": ("k = k / np.sqrt(np.sum(k * k, axis=-1",
                            "k = k / np.sqrt(np.sum(q * q, axis=-1"),
     "sigmoid_sign": ("alpha = 1.0 / (1.0 + np.exp(-alpha))", "alpha = 1.0 / (1.0 + np.exp(alpha))"),
+    # backward
+    "bwd_no_feedback_term": ("X = al[:, None, None] * X + da[:, :, None] * kk[:, None, :]",
+                             "X = al[:, None, None] * X"),
+    "bwd_dalpha_from_new_state": ('g["dalpha"][b, t] += np.einsum("hvk,hvk->h", X, S_prev)',
+                                  'g["dalpha"][b, t] += np.einsum("hvk,hvk->h", X, S_t)'),
+    "bwd_dk_write_sign": ('g["dk"][b, t] += be[:, None] * np.einsum("hvk,hv->hk", X, u) +',
+                          'g["dk"][b, t] -= be[:, None] * np.einsum("hvk,hv->hk", X, u) -'),
+    "bwd_no_correction_in_dk": ('g["dk"][b, t] -= d[:, None] * dqt', 'g["dk"][b, t] -= 0 * dqt'),
     # shared q / k heads
     "shared_qk_interleaved": ("return np.repeat(q, H // Hk, axis=2), np.repeat(k, H // Hk, axis=2)",
                               "return np.tile(q, (1, 1, H // Hk, 1)), np.tile(k, (1, 1, H // Hk, 1))"),
@@ -58,7 +66,7 @@ def _run_pins_on_copy(tmp_path, before=None, after=None):
         ref.write_text(src.replace(before, after))
     env = dict(os.environ, PYTHONDONTWRITEBYTECODE="1")
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           "-k", "numpy or chunk or fused or shared", "tests/test_oracle_pins.py"],
+                           "-k", "numpy or chunk or fused or shared or backward", "tests/test_oracle_pins.py"],
                           cwd=tmp_path, env=env, capture_output=True, text=True, timeout=600)
 
 

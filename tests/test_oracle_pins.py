@@ -416,3 +416,60 @@ def test_shared_qk_expansion_groups_consecutive_value_heads():
     np.testing.assert_array_equal(k6, ke)
     with pytest.raises(ValueError):
         oracle.expand_shared_qk(q[:, :, :1].repeat(4, axis=2), k[:, :, :1].repeat(4, axis=2), H)
+
+
+# --- backward --------------------------------------------------------------------------
+
+def _loss(q, k, v, alpha, beta, d, s0, cu, Wo, Ws):
+    o, s = comba_forward(q, k, v, alpha, beta, d, s0, cu)
+    return float(np.sum(o * Wo) + np.sum(s * Ws))
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_backward_matches_central_differences(packed):
+    """Every gradient of the backward oracle against central differences of
+    the forward oracle, for L = <o, Wo> + <S_final, Ws> with random weights."""
+    rng = np.random.default_rng(61 + packed)
+    if packed:
+        B, T, H, K, V = 1, 9, 2, 3, 2
+        cu = np.array([0, 4, 4, 9])
+        N = 3
+    else:
+        B, T, H, K, V = 2, 5, 2, 3, 2
+        cu = None
+        N = B
+    x = dict(q=rng.standard_normal((B, T, H, K)), k=rng.standard_normal((B, T, H, K)) * 0.6,
+             v=rng.standard_normal((B, T, H, V)), alpha=rng.uniform(0.5, 1.0, (B, T, H)),
+             beta=rng.uniform(0.1, 1.0, (B, T, H)), d=rng.uniform(-1, 1, (H,)),
+             s0=rng.standard_normal((N, H, V, K)) * 0.5)
+    Wo = rng.standard_normal((B, T, H, V))
+    Ws = rng.standard_normal((N, H, V, K))
+    g = oracle.comba_backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["d"], Wo, x["s0"], Ws, cu)
+    names = dict(q="dq", k="dk", v="dv", alpha="dalpha", beta="dbeta", d="dd", s0="ds0")
+    eps = 1e-6
+    for name, gname in names.items():
+        fd = np.zeros_like(x[name])
+        for idx in np.ndindex(x[name].shape):
+            xp = {kk: vv.copy() for kk, vv in x.items()}
+            xm = {kk: vv.copy() for kk, vv in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd[idx] = (_loss(**xp, cu=cu, Wo=Wo, Ws=Ws) - _loss(**xm, cu=cu, Wo=Wo, Ws=Ws)) / (2 * eps)
+        np.testing.assert_allclose(g[gname], fd, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_linear_in_output_weights():
+    """The gradients are linear in (do, dS_final): a second independent
+    property, and the zero cotangent gives zero gradients."""
+    q, k, v, alpha, beta, d, S0 = small_case(63, B=1, T=11, H=2, K=4, V=3)
+    rng = np.random.default_rng(64)
+    do1, do2 = rng.standard_normal((2,) + v.shape)
+    ds1 = rng.standard_normal(S0.shape)
+    g1 = oracle.comba_backward(q, k, v, alpha, beta, d, do1, S0, ds1)
+    g2 = oracle.comba_backward(q, k, v, alpha, beta, d, do2, S0, None)
+    g12 = oracle.comba_backward(q, k, v, alpha, beta, d, 2 * do1 - do2, S0, 2 * ds1)
+    for key in g1:
+        np.testing.assert_allclose(g12[key], 2 * g1[key] - g2[key], rtol=1e-10, atol=1e-12)
+    g0 = oracle.comba_backward(q, k, v, alpha, beta, d, 0 * do1, S0, None)
+    for key in g0:
+        assert np.all(g0[key] == 0)
