@@ -173,12 +173,12 @@ def comba_backward(q, k, v, alpha, beta, d, do, s0=None, dsf=None, cu_seqlens=No
     g["dd"] = np.zeros((H,))
     g["ds0"] = np.zeros((N, H, V, K))
     for n, b, t0, t1 in _segments(B, T, cu_seqlens):
-        S = np.zeros((H, V, K)) if s0 is None else np.array(s0[n], dtype=np.float64)
+        S = np.zeros((H, V, K)) if s0 is None else np.asarray(s0[n], dtype=np.float64).copy()
         states = [S]
         for t in range(t0, t1):  # forward, keeping every state
-            kk = k[b, t]
-            u = v[b, t] - np.einsum("hvk,hk->hv", S, kk)
-            S = alpha[b, t][:, None, None] * S + beta[b, t][:, None, None] * u[:, :, None] * kk[:, None, :]
+            kt = k[b, t]
+            ut = v[b, t] - np.einsum("hvk,hk->hv", S, kt)
+            S = S * alpha[b, t][:, None, None] + (beta[b, t][:, None] * ut)[:, :, None] * kt[:, None, :]
             states.append(S)
         X = np.zeros((H, V, K)) if dsf is None else np.array(dsf[n], dtype=np.float64)
         for t in range(t1 - 1, t0 - 1, -1):
@@ -191,14 +191,14 @@ def comba_backward(q, k, v, alpha, beta, d, do, s0=None, dsf=None, cu_seqlens=No
             g["dq"][b, t] += dqt
             g["dk"][b, t] -= d[:, None] * dqt
             g["dd"] -= np.einsum("hk,hk->h", dqt, kk)
-            u = v[b, t] - np.einsum("hvk,hk->hv", S_prev, kk)
+            ur = v[b, t] - np.einsum("hvk,hk->hv", S_prev, kk)
             Xk = np.einsum("hvk,hk->hv", X, kk)
             g["dalpha"][b, t] += np.einsum("hvk,hvk->h", X, S_prev)
-            g["dbeta"][b, t] += np.einsum("hv,hv->h", u, Xk)
+            g["dbeta"][b, t] += np.einsum("hv,hv->h", ur, Xk)
             du = be[:, None] * Xk
             g["dv"][b, t] += du
             da = -du
-            g["dk"][b, t] += be[:, None] * np.einsum("hvk,hv->hk", X, u) + np.einsum("hvk,hv->hk", S_prev, da)
+            g["dk"][b, t] += be[:, None] * np.einsum("hvk,hv->hk", X, ur) + np.einsum("hvk,hv->hk", S_prev, da)
             X = al[:, None, None] * X + da[:, :, None] * kk[:, None, :]
         g["ds0"][n] = X
     return g

@@ -46,8 +46,8 @@ MUTATIONS = {
                              "X = al[:, None, None] * X"),
     "bwd_dalpha_from_new_state": ('g["dalpha"][b, t] += np.einsum("hvk,hvk->h", X, S_prev)',
                                   'g["dalpha"][b, t] += np.einsum("hvk,hvk->h", X, S_t)'),
-    "bwd_dk_write_sign": ('g["dk"][b, t] += be[:, None] * np.einsum("hvk,hv->hk", X, u) +',
-                          'g["dk"][b, t] -= be[:, None] * np.einsum("hvk,hv->hk", X, u) -'),
+    "bwd_dk_write_sign": ('g["dk"][b, t] += be[:, None] * np.einsum("hvk,hv->hk", X, ur) +',
+                          'g["dk"][b, t] -= be[:, None] * np.einsum("hvk,hv->hk", X, ur) -'),
     "bwd_no_correction_in_dk": ('g["dk"][b, t] -= d[:, None] * dqt', 'g["dk"][b, t] -= 0 * dqt'),
     # shared q / k heads
     "shared_qk_interleaved": ("return np.repeat(q, H // Hk, axis=2), np.repeat(k, H // Hk, axis=2)",
