@@ -10,8 +10,8 @@ input-side fusion (raw q/k normalised in the kernel, alpha/beta given as
 logits) is timed under "fused", beside the same preprocessing done by
 separate torch ops before an unfused call. The 64K-token single-sequence
 workload is timed plain and segment-parallel under "long_context", and the
-1.3B layer with one q/k head shared by all value heads under "shared_qk"
-(context, not the metric). The fp64 CPU oracle is timed on
+1.3B layer with one q/k head shared by all value heads under "shared_qk", and
+the layer's chunk backward under "backward" (context, not the metric). The fp64 CPU oracle is timed on
 the host cores on a bounded sample of the same workload ("cpu_baseline").
 
 Prints one JSON line. Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -221,6 +221,7 @@ def main():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-shared-qk", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="finish with a plain 256 MiB device copy (counter calibration runs)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -363,6 +364,24 @@ def main():
                                "us_per_step": qms * 1e3, "tokens/s": B * T / (qms * 1e-3),
                                "algorithmic_bytes": sbytes, "hbm_frac": sbytes / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         del ts, si
+
+    if not args.no_backward:
+        # training path: gradients of the same layer for seeded cotangents
+        g = torch.Generator(device=dev)
+        g.manual_seed(1234)
+        do_ = torch.randn((B, T, H, V), generator=g, device=dev).to(torch.bfloat16)
+        dsf_ = torch.randn((B, H, V, K), generator=g, device=dev)
+        bws = torch.empty((comba.bwd_workspace_size(B, T, H, K, V),), dtype=torch.uint8, device=dev)
+
+        def bstep(_):
+            comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], do_, t["s0"], None, dsf_,
+                            workspace=bws)
+
+        bms, _ = time_loop(torch, bstep, max(args.steps // 20, 3), 2)
+        result["backward"] = {"workload": "layer_1p3b, chunk backward (dq, dk, dv, dalpha, dbeta, dd, dS0)",
+                              "us_per_step": bms * 1e3, "tokens/s": B * T / (bms * 1e-3),
+                              "workspace_bytes": bws.numel()}
+        del bws, do_, dsf_
 
     if not args.no_long:
         # one 64K-token sequence: 32 workgroups plain, segment-parallel fills the chip

@@ -5,8 +5,8 @@ a bilinear RNN with a scalar-plus-low-rank state transition and output
 correction, as hand-written HIP kernels behind a C ABI (include/comba.h).
 This package is the thin Python binding over that library.
 """
-from .api import (CombaError, chunk_fwd, lib, library_path, recurrent_step,  # noqa: F401
-                  segmented_workspace_size, varlen_order, workspace_size)
+from .api import (CombaError, bwd_workspace_size, chunk_bwd, chunk_fwd, lib, library_path,  # noqa: F401
+                  recurrent_step, segmented_workspace_size, varlen_order, workspace_size)
 
-__all__ = ["chunk_fwd", "recurrent_step", "varlen_order", "workspace_size", "segmented_workspace_size",
+__all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "varlen_order", "workspace_size", "segmented_workspace_size",
            "CombaError"]

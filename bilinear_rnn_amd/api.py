@@ -31,7 +31,8 @@ EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_chunk_fwd_fused", "comba_chunk_fwd_ex",
             "comba_recurrent_step", "comba_recurrent_step_fused", "comba_recurrent_step_ex",
             "comba_chunk_fwd_segmented_workspace_size",
-            "comba_chunk_fwd_segmented", "comba_varlen_order")
+            "comba_chunk_fwd_segmented", "comba_chunk_bwd_workspace_size", "comba_chunk_bwd",
+            "comba_varlen_order")
 
 
 class CombaError(RuntimeError):
@@ -84,6 +85,11 @@ def lib() -> ctypes.CDLL:
         L.comba_chunk_fwd_segmented.argtypes = [vp, vp, vp, fp, fp, fp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
                                                 vp, fp, i32, vp, sz, ctypes.c_uint32, vp]
         L.comba_chunk_fwd_segmented.restype = i32
+        L.comba_chunk_bwd_workspace_size.argtypes = [i32] * 6
+        L.comba_chunk_bwd_workspace_size.restype = sz
+        L.comba_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32, vp, fp,
+                                      fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+        L.comba_chunk_bwd.restype = i32
         L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
         L.comba_varlen_order.restype = i32
         _lib = L
@@ -257,6 +263,43 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
         else:
             _check(L.comba_recurrent_step(*head, *tail, ctypes.c_void_p(stream)))
     return out, final_state
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+              d: torch.Tensor, do: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None,
+              need_initial_state_grad: bool = True,
+              workspace: Optional[torch.Tensor] = None) -> dict:
+    """Gradients through ``comba_chunk_bwd`` for dL/do = ``do`` and dL/dS_final =
+    ``d_final_state`` (None: 0). Returns a dict of fp32 tensors dq, dk, dv,
+    dalpha, dbeta, dd and (unless disabled) dinitial_state."""
+    B, T, H, Hk, K, V, N, _ = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, None)
+    if Hk != H:
+        raise ValueError("the backward takes one q / k head per value head")
+    _require(do, "do", q.dtype, (B, T, H, V))
+    if d_final_state is not None:
+        _require(d_final_state, "d_final_state", torch.float32, (N, H, V, K))
+    L = lib()
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g = dict(dq=torch.empty((B, T, H, K), **f32), dk=torch.empty((B, T, H, K), **f32),
+             dv=torch.empty((B, T, H, V), **f32), dalpha=torch.empty((B, T, H), **f32),
+             dbeta=torch.empty((B, T, H), **f32), dd=torch.empty((H,), **f32))
+    g["dinitial_state"] = torch.empty((N, H, V, K), **f32) if need_initial_state_grad else None
+    nws = int(L.comba_chunk_bwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0))
+    if workspace is None or workspace.numel() < nws:
+        workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(L.comba_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
+                                 _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
+                                 _ptr(do), _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                                 _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dd"]), _ptr(g["dinitial_state"]),
+                                 _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream)))
+    return g
+
+
+def bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0) -> int:
+    return int(lib().comba_chunk_bwd_workspace_size(B, T, H, K, V, num_seqs))
 
 
 def segmented_workspace_size(B: int, T: int, H: int, K: int, V: int, segments: int = 0) -> int:

@@ -320,6 +320,68 @@ COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const 
   return launched(launch(p3));
 }
 
+namespace {
+
+struct BwdWorkspace {
+  size_t hck, dhck, dd, total;
+};
+
+BwdWorkspace bwd_workspace(int64_t nslots, int32_t H, int32_t K, int32_t V) {
+  BwdWorkspace w;
+  const size_t state = align_up(static_cast<size_t>(nslots) * H * V * K * 4);
+  w.hck = 0;
+  w.dhck = state;
+  w.dd = 2 * state;
+  w.total = w.dd + align_up(static_cast<size_t>(nslots) * H * 4);
+  return w;
+}
+
+}  // namespace
+
+COMBA_API size_t comba_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                                int32_t num_seqs) {
+  if (B < 1 || T < 0 || H < 1 || K < 1 || V < 1) return 0;
+  const bool packed = num_seqs > 0;
+  return bwd_workspace(comba::chunk_slots(packed, B, T, packed ? num_seqs : B), H, K, V).total;
+}
+
+COMBA_API int32_t comba_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* d, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                                  int32_t K, int32_t V, int32_t in_dtype, const void* d_o,
+                                  const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha,
+                                  float* dbeta, float* dd, float* d_initial_state, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!d_o || !dq || !dk || !dv || !dalpha || !dbeta || !dd)
+    return fail(COMBA_ERR_INVALID_ARG, "d_o, dq, dk, dv, dalpha, dbeta and dd must be non-NULL");
+  comba::FwdArgs a;
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
+                          in_dtype, const_cast<void*>(d_o), nullptr, a);
+  if (rc != COMBA_OK) return rc;
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t nslots = comba::chunk_slots(packed, B, T, a.N);
+  if (nslots * H > INT_MAX) return fail(COMBA_ERR_UNSUPPORTED, "too many (chunk, head) pairs for one launch");
+  const BwdWorkspace w = bwd_workspace(nslots, H, K, V);
+  if (!workspace || workspace_bytes < w.total)
+    return fail(COMBA_ERR_WORKSPACE, "workspace is NULL or smaller than comba_chunk_bwd_workspace_size()");
+  char* ws = static_cast<char*>(workspace);
+  float* hck = reinterpret_cast<float*>(ws + w.hck);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // forward pass that keeps every chunk's incoming state (no output)
+  comba::FwdArgs f = a;
+  f.o = hck;  // never written: no-output mode
+  f.sf = nullptr;
+  f.order = nullptr;
+  f.fusion = comba::kModeNoOutput;
+  f.hck = hck;
+  rc = launched(in_dtype == COMBA_BF16 ? comba::launch_chunk_bf16(f, st) : comba::launch_chunk_fp32(f, st));
+  if (rc != COMBA_OK) return rc;
+  comba::BwdArgs g{q, k, v, alpha, beta, d, d_o, cu_seqlens, a.N, a.B, a.T, H, K, V, in_dtype, d_final_state,
+                   hck, reinterpret_cast<float*>(ws + w.dhck), reinterpret_cast<float*>(ws + w.dd),
+                   dq, dk, dv, dalpha, dbeta, dd, d_initial_state};
+  return launched(comba::launch_chunk_bwd(g, st));
+}
+
 COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,
                                      void* stream) {
   if (!cu_seqlens || !order) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens and order must be non-NULL");

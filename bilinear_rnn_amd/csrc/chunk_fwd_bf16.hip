@@ -546,7 +546,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
-    float* __restrict__ sf, unsigned fusion) {
+    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck) {
   static_assert(VT == 64, "four consumer wavefronts of 16 channels");
   constexpr int NVT = V / VT;
   __shared__ SmemV3<K, VT> sm;
@@ -768,6 +768,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         const int c0 = t0 + c * 64;
         const int nrows = min(64, t1 - c0);
         const int64_t obase = ((static_cast<int64_t>(b) * T + c0) * H + h) * V;  // row c0, head h
+        if (hck) {  // keep the chunk's incoming state (for the backward)
+          float* dst = hck + ((chunk_slot(cu_seqlens != nullptr, t0, n, c, T) * H + h) * V + vcol) * K + 4 * g;
+#pragma unroll
+          for (int kb = 0; kb < K / 16; ++kb) *reinterpret_cast<f32x4*>(dst + 16 * kb) = hs[kb];
+        }
 
         // The body is software-pipelined by hand: every stage issues the LDS
         // reads of the next one before its own matrix products, and
@@ -985,7 +990,7 @@ static hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t st) {
   const int units = a.N * a.H;
   chunk_fwd_bf16_kernel<K, V, VT, OutT, NORM><<<xcd_grid(units, NVT), 512, 0, st>>>(
       static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.alpha,
-      a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
+      a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion, a.hck);
   return hipGetLastError();
 }
 

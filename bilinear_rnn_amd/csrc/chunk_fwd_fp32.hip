@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
-    float* __restrict__ sf, unsigned fusion) {
+    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck) {
   constexpr int NT = 256, VT = SmemF32<K>::VT, LDH = SmemF32<K>::LDH, NVT = V / VT, LQ = K + 1;
   __shared__ SmemF32<K> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -56,6 +56,13 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     const int c0 = t0 + ci * 64;
     const int nrows = min(64, t1 - c0);
     __syncthreads();
+    if (hck) {  // keep the chunk's incoming state (for the backward)
+      float* dst = hck + ((chunk_slot(cu_seqlens != nullptr, t0, n, ci, T) * H + h) * V + vt * VT) * K;
+      for (int e = tid; e < K * VT; e += NT) {
+        const int kk = e % K, c = e / K;
+        dst[static_cast<int64_t>(c) * K + kk] = sm.Hs[kk * LDH + c];
+      }
+    }
     for (int e = tid; e < 64 * K; e += NT) {
       const int row = e / K, c = e % K, t = c0 + row;
       const int64_t off = ((static_cast<int64_t>(b) * T + t) * Hk + hk) * K + c;
@@ -170,7 +177,8 @@ static hipError_t launch_f32_t(const FwdArgs& a, hipStream_t st) {
   constexpr int NVT = V / SmemF32<K>::VT;
   chunk_fwd_fp32_kernel<K, V, OutT><<<xcd_grid(a.N * a.H, NVT), 256, 0, st>>>(
       static_cast<const float*>(a.q), static_cast<const float*>(a.k), static_cast<const float*>(a.v),
-      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion);
+      a.alpha, a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion,
+      a.hck);
   return hipGetLastError();
 }
 

@@ -28,9 +28,45 @@ struct FwdArgs {
   void* o;
   float* sf;                  // may be null
   unsigned fusion;            // COMBA_FUSE_* flags | kMode* bits
+  float* hck = nullptr;       // incoming state of every chunk, [slots, H, V, K] (backward); may be null
+};
+
+// Index of chunk c of sequence n (first token t0) in per-chunk buffers: n * ceil(T / 64) + c
+// for fixed-length batches; t0 / 64 + n + c for packed ones (unique because sequence starts
+// increase), fewer than T / 64 + N + 1 slots in all.
+__host__ __device__ inline int64_t chunk_slot(bool packed, int t0, int n, int c, int T) {
+  return packed ? static_cast<int64_t>(t0 / 64) + n + c : static_cast<int64_t>(n) * ((T + 63) / 64) + c;
+}
+__host__ __device__ inline int64_t chunk_slots(bool packed, int B, int T, int N) {
+  return packed ? static_cast<int64_t>(T / 64) + N + 1 : static_cast<int64_t>(B) * ((T + 63) / 64);
+}
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* d;
+  const void* dO;             // dL/do, in_dtype, [B, T, H, V]
+  const int32_t* cu_seqlens;  // may be null
+  int N, B, T, H, K, V;
+  int in_dtype;               // COMBA_BF16 / COMBA_FP32
+  const float* dsf;           // dL/dS_final [N, H, V, K], may be null
+  float* hck;                 // chunk incoming states [slots, H, V, K] (from the forward pass)
+  float* dhck;                // chunk outgoing-state gradients [slots, H, V, K]
+  float* dd_part;             // [slots, H]
+  float* dq;                  // [B, T, H, K] fp32
+  float* dk;
+  float* dv;                  // [B, T, H, V] fp32
+  float* dalpha;              // [B, T, H] fp32
+  float* dbeta;
+  float* dd;                  // [H] fp32
+  float* ds0;                 // [N, H, V, K] fp32, may be null
 };
 
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t st);
+hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_fp32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_varlen_order(const int32_t* cu_seqlens, int N, int32_t* order, hipStream_t st);

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define COMBA_ABI_VERSION 4
+#define COMBA_ABI_VERSION 5
 
 /* Status codes returned by every entry point. */
 enum {
@@ -250,6 +250,36 @@ int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v,
                                   int32_t in_dtype, int32_t out_dtype,
                                   void* o, float* final_state, int32_t num_segments,
                                   void* workspace, size_t workspace_bytes, uint32_t fusion, void* stream);
+
+/*
+ * Chunk-wise backward (the training path; the write-up, section
+ * "硬件高效的分块并行计算", notes that the backward either reuses the
+ * cached chunk inverse and chunk states or recomputes them): gradients of a
+ * loss L for given d_o = dL/do [B, T, H, V] (in_dtype) and d_final_state =
+ * dL/dS_final [N, H, V, K] (fp32; NULL means 0). Inputs as comba_chunk_fwd
+ * (one q / k head per value head, no fusion; the output dtype is not an
+ * input). Outputs, all fp32, written in full:
+ *   dq, dk [B, T, H, K]; dv [B, T, H, V]; dalpha, dbeta [B, T, H];
+ *   dd [H] (summed over the batch and the tokens);
+ *   d_initial_state [N, H, V, K] (may be NULL: not written).
+ * The call recomputes the forward, keeping every chunk's incoming state, then
+ * runs a reverse scan over the chunks and a chunk-parallel gradient pass.
+ * It needs a device workspace of at least comba_chunk_bwd_workspace_size(B,
+ * T, H, K, V, num_seqs) bytes (two fp32 states per chunk and head: about 1 GiB
+ * for B = 8, T = 4096, H = 16, K = V = 128), 256-byte aligned.
+ * Errors: as comba_chunk_fwd, COMBA_ERR_INVALID_ARG for a NULL d_o or
+ * gradient output, COMBA_ERR_WORKSPACE for a short workspace.
+ */
+size_t comba_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs);
+
+int32_t comba_chunk_bwd(const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const float* d,
+                        const float* initial_state,
+                        const int32_t* cu_seqlens, int32_t num_seqs,
+                        int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                        int32_t in_dtype, const void* d_o, const float* d_final_state,
+                        float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dd,
+                        float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Longest-first order of packed sequences (integer work, exact): writes into

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = comba.lib()
-    assert L.comba_abi_version() == 4
+    assert L.comba_abi_version() == 5
     assert api.status_string(0) == "COMBA_OK"
     assert api.status_string(-1) == "COMBA_ERR_INVALID_ARG"
     assert api.status_string(-2) == "COMBA_ERR_UNSUPPORTED"
@@ -163,6 +163,37 @@ def test_qk_heads_other_errors_still_reported(fn_name):
 
 def test_segmented_qk_heads_checked():
     assert segmented(Hk=3, H=4) == api.COMBA_ERR_INVALID_ARG
+
+
+def bwd(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=16, H=2, K=64, V=64, idt=0, do=FAKE, dsf=None, dq=FAKE, dk=FAKE, dv=FAKE, da=FAKE,
+                db=FAKE, dd=FAKE, ds0=None, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    return comba.lib().comba_chunk_bwd(
+        args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"], args["s0"], args["cu"], args["n"],
+        args["B"], args["T"], args["H"], args["K"], args["V"], args["idt"], args["do"], args["dsf"], args["dq"],
+        args["dk"], args["dv"], args["da"], args["db"], args["dd"], args["ds0"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(do=None), -1), (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1), (dict(da=None), -1),
+    (dict(db=None), -1), (dict(dd=None), -1), (dict(q=None), -1), (dict(T=0), -1), (dict(idt=3), -1),
+    (dict(K=96), -2), (dict(cu=FAKE, n=0), -1), (dict(ws=None, wsb=0), -3), (dict(wsb=100), -3),
+])
+def test_backward_rejects_bad_arguments(kw, code):
+    assert bwd(**kw) == code
+    assert api.last_error() != ""
+
+
+def test_backward_workspace_size():
+    ws = comba.bwd_workspace_size
+    # two fp32 states per chunk and head plus one float per chunk and head
+    state = 8 * 64 * 16 * 128 * 128 * 4
+    assert ws(8, 4096, 16, 128, 128) == 2 * state + 8 * 64 * 16 * 4
+    # packed: T / 64 + N + 1 slots
+    slots = 1000 // 64 + 5 + 1
+    assert ws(1, 1000, 2, 64, 64, 5) == 2 * slots * 2 * 64 * 64 * 4 + ((slots * 2 * 4 + 255) // 256) * 256
 
 
 def test_workspace_rules():
