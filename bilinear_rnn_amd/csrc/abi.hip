@@ -323,15 +323,19 @@ COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const 
 namespace {
 
 struct BwdWorkspace {
-  size_t hck, dhck, dd, total;
+  size_t hck, dhck, tm, pm, kk, dd, total;
 };
 
 BwdWorkspace bwd_workspace(int64_t nslots, int32_t H, int32_t K, int32_t V) {
   BwdWorkspace w;
   const size_t state = align_up(static_cast<size_t>(nslots) * H * V * K * 4);
+  const size_t mat = align_up(static_cast<size_t>(nslots) * H * 64 * 64 * 4);
   w.hck = 0;
   w.dhck = state;
-  w.dd = 2 * state;
+  w.tm = 2 * state;
+  w.pm = w.tm + mat;
+  w.kk = w.pm + mat;
+  w.dd = w.kk + mat;
   w.total = w.dd + align_up(static_cast<size_t>(nslots) * H * 4);
   return w;
 }
@@ -378,7 +382,8 @@ COMBA_API int32_t comba_chunk_bwd(const void* q, const void* k, const void* v, c
   if (rc != COMBA_OK) return rc;
   comba::BwdArgs g{q, k, v, alpha, beta, d, d_o, cu_seqlens, a.N, a.B, a.T, H, K, V, in_dtype, d_final_state,
                    hck, reinterpret_cast<float*>(ws + w.dhck), reinterpret_cast<float*>(ws + w.dd),
-                   dq, dk, dv, dalpha, dbeta, dd, d_initial_state};
+                   reinterpret_cast<float*>(ws + w.tm), reinterpret_cast<float*>(ws + w.pm),
+                   reinterpret_cast<float*>(ws + w.kk), dq, dk, dv, dalpha, dbeta, dd, d_initial_state};
   return launched(comba::launch_chunk_bwd(g, st));
 }
 

@@ -24,15 +24,20 @@
 // An fp64 prototype of exactly these formulas matches the reverse-mode oracle
 // of the token recurrence to 1e-15.
 //
-// Three launches after a forward pass that stores every chunk's incoming
-// state (the chunk kernels' checkpoint option):
+// Launches after a forward pass that stores every chunk's incoming state (the
+// chunk kernels' checkpoint option):
+//   chunk_bwd_prep_kernel  one workgroup per (chunk, head), all chunks at once:
+//                          Tinv, P and k_t.k_s of the chunk, stored;
 //   chunk_bwd_dh_kernel    reverse scan over chunks, one workgroup per
 //                          (sequence, head, 32 value channels): stores each
 //                          chunk's outgoing-state gradient dh, writes dS_0;
-//   chunk_bwd_grad_kernel  one workgroup per (chunk, head), all chunks at once:
-//                          every per-token gradient and a partial of dd;
+//   chunk_bwd_grad_kernel  one workgroup per (chunk, head): every per-token
+//                          gradient and a partial of dd;
 //   dd_reduce_kernel       dd per head, summed over chunks in a fixed order.
-// All arithmetic is fp32 on the vector units.
+// All arithmetic is fp32 on the vector units. Each thread owns a small block
+// of outputs and reads its operands as 16-byte LDS vectors from layouts chosen
+// per product (rows, or transposed copies), so that every LDS read feeds
+// several multiply-adds.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,223 +50,21 @@ namespace {
 
 constexpr int kDhVT = 32;  // value channels per workgroup of the reverse scan
 constexpr int kGrVT = 8;   // value channels per tile of the gradient kernel
+constexpr int kLdT = 68;   // row stride of 64-wide fp32 tiles (16-byte aligned rows)
 
 template <typename InT>
 __device__ __forceinline__ float ld(const InT* p, int64_t i) {
   return Elem<InT>::load(p, i);
 }
 
-// q~ = q - d k and k of the chunk's rows (zeros past the end), fp32, row stride K + 1.
-template <int K, typename InT>
-__device__ __forceinline__ void stage_qk(const InT* q, const InT* k, float (*Qt)[K + 1], float (*Kc)[K + 1],
-                                         int64_t tok0, int H, int nrows, float dh, int tid, int nt) {
-  for (int e = tid; e < 64 * K; e += nt) {
-    const int row = e / K, c = e % K;
-    float kv = 0.f, qv = 0.f;
-    if (row < nrows) {
-      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + c;
-      kv = ld(k, off);
-      qv = ld(q, off);
-    }
-    Kc[row][c] = kv;
-    Qt[row][c] = qv - dh * kv;
-  }
-}
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ __forceinline__ float hsum(f32x4 x) { return (x[0] + x[1]) + (x[2] + x[3]); }
 
-// A (strictly lower, full 64 x 64 with zeros elsewhere) from staged k rows.
-template <int K>
-__device__ __forceinline__ void form_A(const float (*Kc)[K + 1], const ChunkGates& gt, float* Am, int tid, int nt) {
-  for (int e = tid; e < 64 * 64; e += nt) {
-    const int t = e >> 6, s = e & 63;
-    float a = 0.f;
-    if (s < t) {
-      float kk = 0.f;
-      #pragma unroll 8
-      for (int c = 0; c < K; ++c) kk += Kc[t][c] * Kc[s][c];
-      a = gt.beta[t] * expf(gt.Gx[t] - gt.G[s]) * kk;
-    }
-    Am[t * kLdF + s] = a;
-  }
-}
-
-// P (lower with diagonal, full 64 x 64 with zeros elsewhere).
-template <int K>
-__device__ __forceinline__ void form_P(const float (*Qt)[K + 1], const float (*Kc)[K + 1], const ChunkGates& gt,
-                                       float* Pm, int tid, int nt) {
-  for (int e = tid; e < 64 * 64; e += nt) {
-    const int t = e >> 6, s = e & 63;
-    float p = 0.f;
-    if (s <= t) {
-      float qk = 0.f;
-      #pragma unroll 8
-      for (int c = 0; c < K; ++c) qk += Qt[t][c] * Kc[s][c];
-      p = qk * expf(fminf(gt.G[t] - gt.G[s], 0.f));
-    }
-    Pm[t * kLdF + s] = p;
-  }
-}
-
-template <int K>
-struct SmemDh {
-  float Kc[64][K + 1];
-  float Qt[64][K + 1];
-  float Tm[64 * kLdF];
-  float Pm[64 * kLdF];  // A, then P
-  float Ys[768];
-  float dh[K][kDhVT + 1];
-  float dO[64][kDhVT + 1];
-  float dU[64][kDhVT + 1];  // dUbar, then dR
-  ChunkGates gt;
-};
-
-// Reverse scan over the chunks of one (sequence, head, value tile).
-template <int K, int V, typename InT>
-__global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
-    const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ dsf,
-    float* __restrict__ dhck, float* __restrict__ ds0) {
-  constexpr int NT = 256, VT = kDhVT, NVT = V / VT;
-  __shared__ SmemDh<K> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int unit, vt;
-  if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
-  const int h = unit % H, n = unit / H;
-  int b, t0, t1;
-  sequence_range(cu_seqlens, n, T, b, t0, t1);
-  const float dh_ = d[h];
-  const int nch = (t1 - t0 + 63) / 64;
-  const bool packed = cu_seqlens != nullptr;
-  const int64_t srow = (static_cast<int64_t>(n) * H + h) * V + vt * VT;  // state row of channel 0 of the tile
-
-  for (int e = tid; e < K * VT; e += NT) {
-    const int kk = e % K, c = e / K;
-    sm.dh[kk][c] = dsf ? dsf[(srow + c) * K + kk] : 0.f;
-  }
-  for (int ci = nch - 1; ci >= 0; --ci) {
-    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
-    __syncthreads();
-    stage_qk<K>(q, k, sm.Qt, sm.Kc, tok0, H, nrows, dh_, tid, NT);
-    for (int e = tid; e < 64 * VT; e += NT) {
-      const int row = e / VT, c = e % VT;
-      sm.dO[row][c] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + c) : 0.f;
-    }
-    if (tid < 64) {
-      sm.gt.raw_a[tid] = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
-      sm.gt.raw_b[tid] = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
-    }
-    // the gradient of this chunk's outgoing state, for the gradient kernel
-    {
-      float* dst = dhck + (chunk_slot(packed, t0, n, ci, T) * H + h) * V * K + static_cast<int64_t>(vt) * VT * K;
-      for (int e = tid; e < K * VT; e += NT) {
-        const int kk = e % K, c = e / K;
-        dst[static_cast<int64_t>(c) * K + kk] = sm.dh[kk][c];
-      }
-    }
-    __syncthreads();
-    if (wave == 0) chunk_gates(sm.gt, lane, nrows);
-    __syncthreads();
-    form_A<K>(sm.Kc, sm.gt, sm.Pm, tid, NT);
-    __syncthreads();
-    unit_lower_inverse64<NT>(sm.Pm, sm.Tm, sm.Ys, tid);
-    form_P<K>(sm.Qt, sm.Kc, sm.gt, sm.Pm, tid, NT);
-    __syncthreads();
-    // dUbar = P^T dO + diag(e^(Gn - G)) K dh
-    for (int e = tid; e < 64 * VT; e += NT) {
-      const int t = e / VT, c = e % VT;
-      float acc = 0.f;
-      for (int t2 = t; t2 < 64; ++t2) acc += sm.Pm[t2 * kLdF + t] * sm.dO[t2][c];
-      float kd = 0.f;
-      #pragma unroll 8
-      for (int kk = 0; kk < K; ++kk) kd += sm.Kc[t][kk] * sm.dh[kk][c];
-      sm.dU[t][c] = acc + sm.gt.EGnG[t] * kd;
-    }
-    __syncthreads();
-    // dR = Tinv^T dUbar
-    float r[64 * VT / NT];
-#pragma unroll
-    for (int j = 0; j < 64 * VT / NT; ++j) {
-      const int e = tid + j * NT, s = e / VT, c = e % VT;
-      float acc = 0.f;
-      for (int t = s; t < 64; ++t) acc += sm.Tm[t * kLdF + s] * sm.dU[t][c];
-      r[j] = acc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < 64 * VT / NT; ++j) {
-      const int e = tid + j * NT;
-      sm.dU[e / VT][e % VT] = r[j];
-    }
-    __syncthreads();
-    // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR
-    const float eGn = sm.gt.EG[63];
-    float nd[K * VT / NT];
-#pragma unroll
-    for (int j = 0; j < K * VT / NT; ++j) {
-      const int e = tid + j * NT, kk = e % K, c = e / K;
-      float acc = eGn * sm.dh[kk][c];
-      for (int t = 0; t < 64; ++t)
-        acc += sm.Qt[t][kk] * (sm.gt.EG[t] * sm.dO[t][c]) - sm.Kc[t][kk] * (sm.gt.bEGx[t] * sm.dU[t][c]);
-      nd[j] = acc;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < K * VT / NT; ++j) {
-      const int e = tid + j * NT;
-      sm.dh[e % K][e / K] = nd[j];
-    }
-  }
-  __syncthreads();
-  if (ds0) {
-    for (int e = tid; e < K * VT; e += NT) {
-      const int kk = e % K, c = e / K;
-      ds0[(srow + c) * K + kk] = sm.dh[kk][c];
-    }
-  }
-}
-
-template <int K>
-struct SmemGrad {
-  float Kc[64][K + 1];
-  float Qt[64][K + 1];
-  float Tm[64 * kLdF];  // Tinv, then k_t.k_s, then X = W (.) KK
-  float Pm[64 * kLdF];  // P, then dP (.) P
-  float dA[64 * kLdF];  // A, then dA, then W = dA (.) E
-  float dP[64 * kLdF];  // dP, then dP (.) M
-  union {
-    float Ys[768];  // inverse scratch (before the value tiles)
-    struct {
-      float hc[K][kGrVT + 1];
-      float dh[K][kGrVT + 1];
-    } st;
-  } u;
-  float dO[64][kGrVT + 1];
-  float U[64][kGrVT + 1];   // R, then Ubar
-  float dR[64][kGrVT + 1];  // dUbar, then dR
-  ChunkGates gt;
-  float vec[8][64];  // per-token sums over the value channels / rows / columns
-  float red[16];
-};
-
-// Gradients of one (chunk, head).
-template <int K, int V, typename InT>
-__global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
-    const InT* __restrict__ dO, const int32_t* __restrict__ cu_seqlens, int T, int H, int N, int64_t nslots,
-    const float* __restrict__ hck, const float* __restrict__ dhck, float* __restrict__ dq, float* __restrict__ dk,
-    float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta, float* __restrict__ dd_part) {
-  constexpr int NT = 512, VT = kGrVT, NTILE = V / VT, CK = 64 * K / NT;
-  __shared__ SmemGrad<K> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = blockIdx.x % H;
-  const int64_t slot = blockIdx.x / H;
-  if (slot >= nslots) return;
-  // chunk of this slot
-  const bool packed = cu_seqlens != nullptr;
-  int n, c, b, t0, t1;
-  if (packed) {
+// The chunk of a slot (see chunk_slot). Returns false for a slot between packed sequences.
+__device__ __forceinline__ bool slot_chunk(const int32_t* cu_seqlens, int64_t slot, int T, int N, int& n, int& c,
+                                           int& b, int& t0, int& t1) {
+  if (cu_seqlens) {
     int lo = 0, hi = N - 1;  // largest n with t0(n) / 64 + n <= slot
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -278,117 +81,406 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     c = static_cast<int>(slot % nch);
     sequence_range(cu_seqlens, n, T, b, t0, t1);
   }
-  const int c0 = t0 + 64 * c;
-  const bool valid = c >= 0 && c0 < t1;
-  if (!valid) {  // a slot between packed sequences: no chunk
+  return c >= 0 && t0 + 64 * c < t1;
+}
+
+// q~ = q - d k and k of the chunk's rows (zeros past the end), fp32 rows of stride LD.
+template <int K, int LD, typename InT>
+__device__ __forceinline__ void stage_rows(const InT* q, const InT* k, float* Qt, float* Kc, int64_t tok0, int H,
+                                           int nrows, float dh, int tid, int nt) {
+  for (int e = tid; e < 64 * K; e += nt) {
+    const int row = e / K, c = e % K;
+    float kv = 0.f, qv = 0.f;
+    if (row < nrows) {
+      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + c;
+      kv = ld(k, off);
+      qv = ld(q, off);
+    }
+    Kc[row * LD + c] = kv;
+    Qt[row * LD + c] = qv - dh * kv;
+  }
+}
+
+__device__ __forceinline__ void stage_gates(ChunkGates& gt, const float* alpha, const float* beta, int64_t tok0,
+                                            int H, int nrows, int tid) {
+  if (tid < 64) {
+    gt.raw_a[tid] = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
+    gt.raw_b[tid] = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
+  }
+}
+
+// ---- prep: Tinv, P and k_t.k_s of every chunk -------------------------------------------
+
+template <int K>
+struct SmemPrep {
+  float QtT[K][kLdT];  // q~ transposed: [key channel][token]
+  float KT[K][kLdT];
+  float Am[64 * kLdF];
+  float Tm[64 * kLdF];
+  float Ys[768];
+  ChunkGates gt;
+};
+
+template <int K, typename InT>
+__global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const float* __restrict__ d, const int32_t* __restrict__ cu_seqlens, int T,
+    int H, int N, int64_t nslots, float* __restrict__ Tg, float* __restrict__ Pg, float* __restrict__ KKg) {
+  constexpr int NT = 256;
+  __shared__ SmemPrep<K> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x % H;
+  const int64_t slot = blockIdx.x / H;
+  if (slot >= nslots) return;
+  int n, c, b, t0, t1;
+  if (!slot_chunk(cu_seqlens, slot, T, N, n, c, b, t0, t1)) return;
+  const int c0 = t0 + 64 * c, nrows = min(64, t1 - c0);
+  const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+  const float dh = d[h];
+  for (int e = tid; e < 64 * K; e += NT) {
+    const int row = e / K, cc = e % K;
+    float kv = 0.f, qv = 0.f;
+    if (row < nrows) {
+      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
+      kv = ld(k, off);
+      qv = ld(q, off);
+    }
+    sm.KT[cc][row] = kv;
+    sm.QtT[cc][row] = qv - dh * kv;
+  }
+  stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
+  __syncthreads();
+  if (wave == 0) chunk_gates(sm.gt, lane, nrows);
+  __syncthreads();
+  // 4 x 4 block of (t, s) per thread: k_t.k_s and q~_t.k_s
+  const int tb = 4 * (tid >> 4), sb = 4 * (tid & 15);
+  f32x4 kk[4], qk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kk[i] = qk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int cc = 0; cc < K; ++cc) {
+    const f32x4 kt = ld4(&sm.KT[cc][tb]), ks = ld4(&sm.KT[cc][sb]), qt = ld4(&sm.QtT[cc][tb]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      kk[i] += kt[i] * ks;
+      qk[i] += qt[i] * ks;
+    }
+  }
+  const int64_t mb = (slot * H + h) * 64 * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = tb + i;
+    f32x4 a, p;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = sb + j;
+      a[j] = s < t ? sm.gt.beta[t] * expf(sm.gt.Gx[t] - sm.gt.G[s]) * kk[i][j] : 0.f;
+      p[j] = s <= t ? qk[i][j] * expf(fminf(sm.gt.G[t] - sm.gt.G[s], 0.f)) : 0.f;
+    }
+    st4(&sm.Am[t * kLdF + sb], a);
+    st4(&Pg[mb + t * 64 + sb], p);
+    st4(&KKg[mb + t * 64 + sb], kk[i]);
+  }
+  __syncthreads();
+  unit_lower_inverse64<NT>(sm.Am, sm.Tm, sm.Ys, tid);
+  for (int e = tid; e < 64 * 64; e += NT) {
+    const int t = e >> 6, s = e & 63;
+    Tg[mb + e] = s <= t ? sm.Tm[t * kLdF + s] : 0.f;
+  }
+}
+
+// ---- reverse scan of dh --------------------------------------------------------------------
+
+template <int K>
+struct SmemDh {
+  float Qt[64][K + 4];
+  float Kc[64][K + 4];
+  float Tm[64][kLdT];
+  float Pm[64][kLdT];
+  float dh[K][kDhVT + 4];
+  float dO[64][kDhVT + 4];
+  float dU[64][kDhVT + 4];  // dUbar, then dR
+  ChunkGates gt;
+};
+
+template <int K, int V, typename InT>
+__global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
+    const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
+    const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0) {
+  constexpr int NT = 256, VT = kDhVT, NVT = V / VT, LQ = K + 4;
+  __shared__ SmemDh<K> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int unit, vt;
+  if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
+  const int h = unit % H, n = unit / H;
+  int b, t0, t1;
+  sequence_range(cu_seqlens, n, T, b, t0, t1);
+  const float dh_ = d[h];
+  const int nch = (t1 - t0 + 63) / 64;
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t srow = (static_cast<int64_t>(n) * H + h) * V + vt * VT;  // state row of channel 0 of the tile
+  // thread blocks: (token pair, channel quad) for dUbar and dR; (key quad, channel quad) for dh,
+  // the latter for threads with kq < K (whole wavefronts)
+  const int tp = 2 * (tid >> 3), vq = 4 * (tid & 7);
+  const int kq = 4 * (tid >> 3);
+  const bool kact = kq < K;
+
+  for (int e = tid; e < K * VT; e += NT) {
+    const int kk = e % K, cc = e / K;
+    sm.dh[kk][cc] = dsf ? dsf[(srow + cc) * K + kk] : 0.f;
+  }
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+    const int64_t slot = chunk_slot(packed, t0, n, ci, T);
+    const int64_t mb = (slot * H + h) * 64 * 64;
+    __syncthreads();
+    stage_rows<K, LQ>(q, k, &sm.Qt[0][0], &sm.Kc[0][0], tok0, H, nrows, dh_, tid, NT);
+    for (int e = tid; e < 64 * VT; e += NT) {
+      const int row = e / VT, cc = e % VT;
+      sm.dO[row][cc] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + cc) : 0.f;
+    }
+    for (int e = tid; e < 64 * 16; e += NT) {
+      const int row = e >> 4, c4 = 4 * (e & 15);
+      st4(&sm.Tm[row][c4], ld4(&Tg[mb + row * 64 + c4]));
+      st4(&sm.Pm[row][c4], ld4(&Pg[mb + row * 64 + c4]));
+    }
+    stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
+    // the gradient of this chunk's outgoing state, for the gradient kernel ([channel][key])
+    if (kact) {
+      float* dst = dhck + (slot * H + h) * V * K + static_cast<int64_t>(vt) * VT * K;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = sm.dh[kq + i][vq + j];
+        st4(dst + static_cast<int64_t>(vq + j) * K + kq, x);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) chunk_gates(sm.gt, lane, nrows);
+    __syncthreads();
+    // dUbar = P^T dO + diag(e^(Gn - G)) K dh  (rows tp, tp+1; channels vq..vq+3)
+    {
+      f32x4 a0{0.f, 0.f, 0.f, 0.f}, a1{0.f, 0.f, 0.f, 0.f};
+      for (int t2 = tp; t2 < 64; ++t2) {
+        const f32x4 o = ld4(&sm.dO[t2][vq]);
+        a0 += sm.Pm[t2][tp] * o;
+        a1 += sm.Pm[t2][tp + 1] * o;
+      }
+      f32x4 k0{0.f, 0.f, 0.f, 0.f}, k1{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+      for (int kk = 0; kk < K; kk += 4) {
+        const f32x4 r0 = ld4(&sm.Kc[tp][kk]), r1 = ld4(&sm.Kc[tp + 1][kk]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 dv = ld4(&sm.dh[kk + i][vq]);
+          k0 += r0[i] * dv;
+          k1 += r1[i] * dv;
+        }
+      }
+      st4(&sm.dU[tp][vq], a0 + sm.gt.EGnG[tp] * k0);
+      st4(&sm.dU[tp + 1][vq], a1 + sm.gt.EGnG[tp + 1] * k1);
+    }
+    __syncthreads();
+    // dR = Tinv^T dUbar
+    f32x4 r0{0.f, 0.f, 0.f, 0.f}, r1{0.f, 0.f, 0.f, 0.f};
+    for (int t2 = tp; t2 < 64; ++t2) {
+      const f32x4 u = ld4(&sm.dU[t2][vq]);
+      r0 += sm.Tm[t2][tp] * u;
+      r1 += sm.Tm[t2][tp + 1] * u;
+    }
+    __syncthreads();
+    st4(&sm.dU[tp][vq], r0);
+    st4(&sm.dU[tp + 1][vq], r1);
+    __syncthreads();
+    // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR   (keys kq..kq+3, channels vq..vq+3)
+    f32x4 acc[4];
+    if (kact) {
+      const float eGn = sm.gt.EG[63];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = eGn * ld4(&sm.dh[kq + i][vq]);
+#pragma unroll 2
+      for (int t = 0; t < 64; ++t) {
+        const f32x4 qr = ld4(&sm.Qt[t][kq]), kr = ld4(&sm.Kc[t][kq]);
+        const f32x4 o = sm.gt.EG[t] * ld4(&sm.dO[t][vq]), r = sm.gt.bEGx[t] * ld4(&sm.dU[t][vq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += qr[i] * o - kr[i] * r;
+      }
+    }
+    __syncthreads();
+    if (kact) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st4(&sm.dh[kq + i][vq], acc[i]);
+    }
+  }
+  __syncthreads();
+  if (ds0) {
+    for (int e = tid; e < K * VT; e += NT) {
+      const int kk = e % K, cc = e / K;
+      ds0[(srow + cc) * K + kk] = sm.dh[kk][cc];
+    }
+  }
+}
+
+// ---- per-chunk gradients ------------------------------------------------------------------
+
+template <int K>
+struct SmemGrad {
+  float Qt[64][K + 4];
+  float Kc[64][K + 4];
+  float Tm[64][kLdT];        // Tinv, then dP (.) M
+  float TT[64][kLdT];        // Tinv^T, then W = dA (.) E
+  float PT[64][kLdT];        // P^T, then (dP (.) P)^T
+  float X4[64][kLdT];        // X = W (.) k_t.k_s
+  float hT[kGrVT][K + 4];    // state tile, [channel][key]
+  float dhT[kGrVT][K + 4];
+  float dOT[kGrVT][kLdT];    // [channel][token]
+  float UT[kGrVT][kLdT];     // R, then Ubar
+  float dRT[kGrVT][kLdT];    // dUbar, then dR
+  ChunkGates gt;
+  float vec[8][64];
+  float red[16];
+};
+
+template <int K, int V, typename InT>
+__global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
+    const InT* __restrict__ dO, const int32_t* __restrict__ cu_seqlens, int T, int H, int N, int64_t nslots,
+    const float* __restrict__ hck, const float* __restrict__ dhck, const float* __restrict__ Tg,
+    const float* __restrict__ Pg, const float* __restrict__ KKg, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta, float* __restrict__ dd_part) {
+  constexpr int NT = 512, VT = kGrVT, NTILE = V / VT, LQ = K + 4;
+  constexpr int TB = 64 * K / (4 * NT);  // token rows per thread in the 64 x K blocks (4 keys each)
+  constexpr int NKQ = K / 4;
+  __shared__ SmemGrad<K> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x % H;
+  const int64_t slot = blockIdx.x / H;
+  if (slot >= nslots) return;
+  int n, c, b, t0, t1;
+  if (!slot_chunk(cu_seqlens, slot, T, N, n, c, b, t0, t1)) {
     if (tid == 0) dd_part[slot * H + h] = 0.f;
     return;
   }
-  const int nrows = min(64, t1 - c0);
+  const int c0 = t0 + 64 * c, nrows = min(64, t1 - c0);
   const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
   const float dh_ = d[h];
   const float* hsrc = hck + (slot * H + h) * V * K;
   const float* dhsrc = dhck + (slot * H + h) * V * K;
+  const int64_t mb = (slot * H + h) * 64 * 64;
 
-  stage_qk<K>(q, k, sm.Qt, sm.Kc, tok0, H, nrows, dh_, tid, NT);
-  if (tid < 64) {
-    sm.gt.raw_a[tid] = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
-    sm.gt.raw_b[tid] = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
+  stage_rows<K, LQ>(q, k, &sm.Qt[0][0], &sm.Kc[0][0], tok0, H, nrows, dh_, tid, NT);
+  for (int e = tid; e < 64 * 16; e += NT) {
+    const int row = e >> 4, c4 = 4 * (e & 15);
+    const f32x4 tv = ld4(&Tg[mb + row * 64 + c4]), pv = ld4(&Pg[mb + row * 64 + c4]);
+    st4(&sm.Tm[row][c4], tv);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sm.TT[c4 + j][row] = tv[j];
+      sm.PT[c4 + j][row] = pv[j];
+    }
   }
+  stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
   __syncthreads();
   if (wave == 0) chunk_gates(sm.gt, lane, nrows);
   __syncthreads();
-  form_A<K>(sm.Kc, sm.gt, sm.dA, tid, NT);
-  __syncthreads();
-  unit_lower_inverse64<NT>(sm.dA, sm.Tm, sm.u.Ys, tid);
-  form_P<K>(sm.Qt, sm.Kc, sm.gt, sm.Pm, tid, NT);
-  __syncthreads();
 
-  // this thread's (row, channel) in a value tile, its 8 entries of the 64 x 64
-  // accumulators and its CK entries of the 64 x K ones
+  // (token, channel) of a value tile
   const int tr = tid >> 3, tv = tid & 7;
   const float be_t = sm.gt.beta[tr], b1_t = sm.gt.bEGx[tr], eGnG_t = sm.gt.EGnG[tr], eGx_t = expf(sm.gt.Gx[tr]);
-  float accA[8], accP[8], accQ[CK], accK[CK];
+  // 64 x K blocks: TB token rows x 4 keys
+  const int bt = TB * (tid / NKQ), bk = 4 * (tid % NKQ);
+  f32x4 accQ[TB], accK[TB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) accA[i] = accP[i] = 0.f;
+  for (int i = 0; i < TB; ++i) accQ[i] = accK[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // 64 x 64 blocks: 2 token rows x 4 columns
+  const int at = 2 * (tid >> 4), as = 4 * (tid & 15);
+  f32x4 accA[2], accP[2];
 #pragma unroll
-  for (int i = 0; i < CK; ++i) accQ[i] = accK[i] = 0.f;
+  for (int i = 0; i < 2; ++i) accA[i] = accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float sQh = 0.f, sbR = 0.f, sKhdR = 0.f, st2 = 0.f, shdh = 0.f;
 
   for (int jt = 0; jt < NTILE; ++jt) {
     const int v0 = jt * VT;
     __syncthreads();
-    for (int e = tid; e < K * VT; e += NT) {
-      const int kk = e % K, cc = e / K;
-      const float hv = hsrc[static_cast<int64_t>(v0 + cc) * K + kk];
-      const float dv_ = dhsrc[static_cast<int64_t>(v0 + cc) * K + kk];
-      sm.u.st.hc[kk][cc] = hv;
-      sm.u.st.dh[kk][cc] = dv_;
-      shdh += hv * dv_;
+    for (int e = tid; e < K * VT / 4; e += NT) {
+      const int c4 = 4 * (e % NKQ), cc = e / NKQ;
+      const f32x4 hv = ld4(hsrc + static_cast<int64_t>(v0 + cc) * K + c4);
+      const f32x4 dv_ = ld4(dhsrc + static_cast<int64_t>(v0 + cc) * K + c4);
+      st4(&sm.hT[cc][c4], hv);
+      st4(&sm.dhT[cc][c4], dv_);
+      shdh += hsum(hv * dv_);
     }
-    {
-      const float x = tr < nrows ? ld(dO, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
-      sm.dO[tr][tv] = x;
-    }
+    sm.dOT[tv][tr] = tr < nrows ? ld(dO, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
     __syncthreads();
-    float kh = 0.f, qh = 0.f, kdh = 0.f;
-    #pragma unroll 8
-    for (int kk = 0; kk < K; ++kk) {
-      const float kv = sm.Kc[tr][kk];
-      kh += kv * sm.u.st.hc[kk][tv];
-      qh += sm.Qt[tr][kk] * sm.u.st.hc[kk][tv];
-      kdh += kv * sm.u.st.dh[kk][tv];
+    float kh, qh, kdh;
+    {
+      f32x4 a{0.f, 0.f, 0.f, 0.f}, bq{0.f, 0.f, 0.f, 0.f}, cd{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int kk = 0; kk < K; kk += 4) {
+        const f32x4 kr = ld4(&sm.Kc[tr][kk]), hv = ld4(&sm.hT[tv][kk]);
+        a += kr * hv;
+        bq += ld4(&sm.Qt[tr][kk]) * hv;
+        cd += kr * ld4(&sm.dhT[tv][kk]);
+      }
+      kh = hsum(a);
+      qh = hsum(bq);
+      kdh = hsum(cd);
     }
     const float vv = tr < nrows ? ld(v, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
-    sm.U[tr][tv] = be_t * vv - b1_t * kh;  // R
+    sm.UT[tv][tr] = be_t * vv - b1_t * kh;  // R
     __syncthreads();
-    float ub = 0.f;  // Ubar = Tinv R
-    for (int s = 0; s <= tr; ++s) ub += sm.Tm[tr * kLdF + s] * sm.U[s][tv];
-    float du = eGnG_t * kdh;  // dUbar = P^T dO + diag(e^(Gn - G)) K dh
-    for (int t2 = tr; t2 < 64; ++t2) du += sm.Pm[t2 * kLdF + tr] * sm.dO[t2][tv];
+    float ub, du;
+    {
+      f32x4 a{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s <= tr; s += 4) a += ld4(&sm.Tm[tr][s]) * ld4(&sm.UT[tv][s]);  // Tinv is 0 above the diagonal
+      ub = hsum(a);
+      f32x4 p{0.f, 0.f, 0.f, 0.f};
+      for (int t2 = tr & ~3; t2 < 64; t2 += 4) p += ld4(&sm.PT[tr][t2]) * ld4(&sm.dOT[tv][t2]);  // P^T is 0 below
+      du = eGnG_t * kdh + hsum(p);
+    }
     __syncthreads();
-    sm.U[tr][tv] = ub;
-    sm.dR[tr][tv] = du;
+    sm.UT[tv][tr] = ub;
+    sm.dRT[tv][tr] = du;
     __syncthreads();
-    float dr = 0.f;  // dR = Tinv^T dUbar
-    for (int t2 = tr; t2 < 64; ++t2) dr += sm.Tm[t2 * kLdF + tr] * sm.dR[t2][tv];
+    float dr;
+    {
+      f32x4 a{0.f, 0.f, 0.f, 0.f};
+      for (int t2 = tr & ~3; t2 < 64; t2 += 4) a += ld4(&sm.TT[tr][t2]) * ld4(&sm.dRT[tv][t2]);
+      dr = hsum(a);
+    }
     __syncthreads();
-    sm.dR[tr][tv] = dr;
+    sm.dRT[tv][tr] = dr;
     if (tr < nrows) dv[(tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv] = be_t * dr;
-    // this (row, channel)'s terms of the sums over the value channels
-    sQh += qh * sm.dO[tr][tv];
+    sQh += qh * sm.dOT[tv][tr];
     sbR += dr * (vv - eGx_t * kh);
     sKhdR += kh * dr;
     st2 += kdh * ub;
     __syncthreads();
-    // dA -= dR Ubar^T (s < t), dP += dO Ubar^T (s <= t)
+    // dA -= dR Ubar^T, dP += dO Ubar^T (masked at the end)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e2 = tid + i * NT, t = e2 >> 6, s = e2 & 63;
-      float xa = 0.f, xp = 0.f;
+    for (int cc = 0; cc < VT; ++cc) {
+      const f32x4 us = ld4(&sm.UT[cc][as]);
 #pragma unroll
-      for (int cc = 0; cc < VT; ++cc) {
-        const float us = sm.U[s][cc];
-        xa += sm.dR[t][cc] * us;
-        xp += sm.dO[t][cc] * us;
+      for (int i = 0; i < 2; ++i) {
+        accA[i] -= sm.dRT[cc][at + i] * us;
+        accP[i] += sm.dOT[cc][at + i] * us;
       }
-      if (s < t) accA[i] -= xa;
-      if (s <= t) accP[i] += xp;
     }
     // dQt += dO h^T;  dK += -diag(b1) dR h^T + diag(e^(Gn - G)) Ubar dh^T
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int e3 = tid + i * NT, t = e3 / K, kk = e3 % K;
-      const float b1 = sm.gt.bEGx[t], eg = sm.gt.EGnG[t];
-      float xq = 0.f, xk = 0.f;
+    for (int cc = 0; cc < VT; ++cc) {
+      const f32x4 hv = ld4(&sm.hT[cc][bk]), dv_ = ld4(&sm.dhT[cc][bk]);
 #pragma unroll
-      for (int cc = 0; cc < VT; ++cc) {
-        const float hv = sm.u.st.hc[kk][cc];
-        xq += sm.dO[t][cc] * hv;
-        xk += eg * sm.U[t][cc] * sm.u.st.dh[kk][cc] - b1 * sm.dR[t][cc] * hv;
+      for (int i = 0; i < TB; ++i) {
+        const int t = bt + i;
+        accQ[i] += sm.dOT[cc][t] * hv;
+        accK[i] += (sm.gt.EGnG[t] * sm.UT[cc][t]) * dv_ - (sm.gt.bEGx[t] * sm.dRT[cc][t]) * hv;
       }
-      accQ[i] += xq;
-      accK[i] += xk;
     }
   }
   __syncthreads();
@@ -410,40 +502,35 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) shdh += __shfl_xor(shdh, m, kWave);
   if (lane == 0) sm.red[wave] = shdh;
-  // k_t . k_s (Tinv is no longer needed), dA, dP
-  for (int e = tid; e < 64 * 64; e += NT) {
-    const int t = e >> 6, s = e & 63;
-    float kk = 0.f;
-    #pragma unroll 8
-    for (int cc = 0; cc < K; ++cc) kk += sm.Kc[t][cc] * sm.Kc[s][cc];
-    sm.Tm[t * kLdF + s] = kk;
-  }
+  // dP (.) M -> Tm, W = dA (.) E -> TT, (dP (.) P)^T -> PT, X = W (.) KK -> X4
+  // (each thread rewrites only the entries of its own 2 x 4 block)
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e2 = tid + i * NT, t = e2 >> 6, s = e2 & 63;
-    sm.dA[t * kLdF + s] = accA[i];
-    sm.dP[t * kLdF + s] = accP[i];
-  }
-  __syncthreads();
-  // dP (.) P, dP (.) M, W = dA (.) E, X = W (.) KK
+  for (int i = 0; i < 2; ++i) {
+    const int t = at + i;
+    const f32x4 kkv = ld4(&KKg[mb + t * 64 + as]);
+    f32x4 pm, w, x;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e2 = tid + i * NT, t = e2 >> 6, s = e2 & 63, o = t * kLdF + s;
-    const float M = s <= t ? expf(fminf(sm.gt.G[t] - sm.gt.G[s], 0.f)) : 0.f;
-    const float E = s < t ? expf(fminf(sm.gt.Gx[t] - sm.gt.G[s], 0.f)) : 0.f;
-    const float dpv = sm.dP[o], w = sm.dA[o] * E;
-    sm.Pm[o] = dpv * sm.Pm[o];
-    sm.dP[o] = dpv * M;
-    sm.dA[o] = w;
-    sm.Tm[o] = w * sm.Tm[o];
+    for (int j = 0; j < 4; ++j) {
+      const int s = as + j;
+      const float M = s <= t ? expf(fminf(sm.gt.G[t] - sm.gt.G[s], 0.f)) : 0.f;
+      const float E = s < t ? expf(fminf(sm.gt.Gx[t] - sm.gt.G[s], 0.f)) : 0.f;
+      const float dpv = s <= t ? accP[i][j] : 0.f, dav = s < t ? accA[i][j] : 0.f;
+      pm[j] = dpv * M;
+      w[j] = dav * E;
+      x[j] = w[j] * kkv[j];
+      sm.PT[s][t] = dpv * sm.PT[s][t];
+    }
+    st4(&sm.Tm[t][as], pm);
+    st4(&sm.TT[t][as], w);
+    st4(&sm.X4[t][as], x);
   }
   __syncthreads();
   // row and column sums (fixed order)
   if (tid < 64) {
     float rp = 0.f, rx = 0.f;
     for (int s = 0; s < 64; ++s) {
-      rp += sm.Pm[tid * kLdF + s];
-      rx += sm.Tm[tid * kLdF + s];
+      rp += sm.PT[s][tid];
+      rx += sm.X4[tid][s];
     }
     sm.vec[4][tid] = rp;
     sm.vec[5][tid] = rx;
@@ -451,29 +538,42 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     const int s = tid - 64;
     float cp = 0.f, cx = 0.f;
     for (int t = 0; t < 64; ++t) {
-      cp += sm.Pm[t * kLdF + s];
-      cx += sm.gt.beta[t] * sm.Tm[t * kLdF + s];
+      cp += sm.PT[s][t];
+      cx += sm.gt.beta[t] * sm.X4[t][s];
     }
     sm.vec[6][s] = cp;
     sm.vec[7][s] = cx;
   }
-  // dq, dk and this thread's part of dd
+  // dq, dk (rows bt.., keys bk..bk+3) and this thread's part of dd
+  f32x4 xq[TB], xk[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    xq[i] = sm.gt.EG[bt + i] * accQ[i];
+    xk[i] = accK[i];
+  }
+  for (int s = 0; s < 64; ++s) {
+    const f32x4 ks = ld4(&sm.Kc[s][bk]), qs = ld4(&sm.Qt[s][bk]);
+    const float bs = sm.gt.beta[s];
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      const int t = bt + i;
+      // row t of (dP (.) M) K and of diag(beta) W K (zero above the diagonal)
+      xq[i] += sm.Tm[t][s] * ks;
+      xk[i] += (sm.gt.beta[t] * sm.TT[t][s]) * ks;
+      // column t of (dP (.) M)^T Qt and of W^T diag(beta) K
+      xk[i] += sm.Tm[s][t] * qs + (sm.TT[s][t] * bs) * ks;
+    }
+  }
   float ddp = 0.f;
 #pragma unroll
-  for (int i = 0; i < CK; ++i) {
-    const int e3 = tid + i * NT, t = e3 / K, kk = e3 % K;
-    float xq = sm.gt.EG[t] * accQ[i];
-    for (int s = 0; s <= t; ++s) xq += sm.dP[t * kLdF + s] * sm.Kc[s][kk];
-    float xk = accK[i] - dh_ * xq;
-    const float be = sm.gt.beta[t];
-    for (int t2 = t; t2 < 64; ++t2) xk += sm.dP[t2 * kLdF + t] * sm.Qt[t2][kk];
-    for (int s = 0; s < t; ++s) xk += be * sm.dA[t * kLdF + s] * sm.Kc[s][kk];
-    for (int t2 = t + 1; t2 < 64; ++t2) xk += sm.dA[t2 * kLdF + t] * sm.gt.beta[t2] * sm.Kc[t2][kk];
-    ddp -= xq * sm.Kc[t][kk];
+  for (int i = 0; i < TB; ++i) {
+    const int t = bt + i;
+    xk[i] -= dh_ * xq[i];
+    ddp -= hsum(xq[i] * ld4(&sm.Kc[t][bk]));
     if (t < nrows) {
-      const int64_t off = (tok0 + static_cast<int64_t>(t) * H) * K + kk;
-      dq[off] = xq;
-      dk[off] = xk;
+      const int64_t off = (tok0 + static_cast<int64_t>(t) * H) * K + bk;
+      st4(dq + off, xq[i]);
+      st4(dk + off, xk[i]);
     }
   }
 #pragma unroll
@@ -513,30 +613,40 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   }
 }
 
-__global__ void dd_reduce_kernel(const float* __restrict__ dd_part, int64_t nslots, int H, float* __restrict__ dd) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
+// dd per head: one 64-thread block per head sums the chunks in a fixed order
+// (strided partial sums, then a fixed butterfly).
+__global__ __launch_bounds__(64) void dd_reduce_kernel(const float* __restrict__ dd_part, int64_t nslots, int H,
+                                                       float* __restrict__ dd) {
+  const int h = blockIdx.x, lane = threadIdx.x;
   float s = 0.f;
-  for (int64_t i = 0; i < nslots; ++i) s += dd_part[i * H + h];
-  dd[h] = s;
+  for (int64_t i = lane; i < nslots; i += 64) s += dd_part[i * H + h];
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, kWave);
+  if (lane == 0) dd[h] = s;
 }
 
 template <int K, int V, typename InT>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const bool packed = a.cu_seqlens != nullptr;
   const int64_t nslots = chunk_slots(packed, a.B, a.T, a.N);
-  chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 256, 0, st>>>(
-      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.alpha, a.beta, a.d,
-      static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, a.dsf, a.dhck, a.ds0);
+  const unsigned grid = static_cast<unsigned>(nslots * a.H);
+  chunk_bwd_prep_kernel<K, InT><<<grid, 256, 0, st>>>(
+      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.alpha, a.beta, a.d, a.cu_seqlens, a.T, a.H, a.N,
+      nslots, a.Tg, a.Pg, a.KKg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  chunk_bwd_grad_kernel<K, V, InT><<<static_cast<unsigned>(nslots * a.H), 512, 0, st>>>(
-      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v), a.alpha, a.beta,
-      a.d, static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.dq, a.dk, a.dv,
-      a.dalpha, a.dbeta, a.dd_part);
+  chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 256, 0, st>>>(
+      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.alpha, a.beta, a.d,
+      static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.dsf, a.dhck, a.ds0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dd_reduce_kernel<<<(a.H + 63) / 64, 64, 0, st>>>(a.dd_part, nslots, a.H, a.dd);
+  chunk_bwd_grad_kernel<K, V, InT><<<grid, 512, 0, st>>>(
+      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v), a.alpha, a.beta,
+      a.d, static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg,
+      a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dd_part);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dd_reduce_kernel<<<a.H, 64, 0, st>>>(a.dd_part, nslots, a.H, a.dd);
   return hipGetLastError();
 }
 

@@ -56,6 +56,9 @@ struct BwdArgs {
   float* hck;                 // chunk incoming states [slots, H, V, K] (from the forward pass)
   float* dhck;                // chunk outgoing-state gradients [slots, H, V, K]
   float* dd_part;             // [slots, H]
+  float* Tg;                  // per chunk and head: Tinv, P and k_t.k_s, fp32 64 x 64 each
+  float* Pg;
+  float* KKg;
   float* dq;                  // [B, T, H, K] fp32
   float* dk;
   float* dv;                  // [B, T, H, V] fp32

@@ -262,11 +262,12 @@ int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v,
  *   dq, dk [B, T, H, K]; dv [B, T, H, V]; dalpha, dbeta [B, T, H];
  *   dd [H] (summed over the batch and the tokens);
  *   d_initial_state [N, H, V, K] (may be NULL: not written).
- * The call recomputes the forward, keeping every chunk's incoming state, then
- * runs a reverse scan over the chunks and a chunk-parallel gradient pass.
- * It needs a device workspace of at least comba_chunk_bwd_workspace_size(B,
- * T, H, K, V, num_seqs) bytes (two fp32 states per chunk and head: about 1 GiB
- * for B = 8, T = 4096, H = 16, K = V = 128), 256-byte aligned.
+ * The call recomputes the forward, keeping every chunk's incoming state,
+ * forms each chunk's inverse and score matrices, then runs a reverse scan over
+ * the chunks and a chunk-parallel gradient pass. It needs a device workspace
+ * of at least comba_chunk_bwd_workspace_size(B, T, H, K, V, num_seqs) bytes
+ * (per chunk and head two fp32 states and three fp32 64 x 64 matrices: about
+ * 1.4 GiB for B = 8, T = 4096, H = 16, K = V = 128), 256-byte aligned.
  * Errors: as comba_chunk_fwd, COMBA_ERR_INVALID_ARG for a NULL d_o or
  * gradient output, COMBA_ERR_WORKSPACE for a short workspace.
  */

@@ -188,12 +188,12 @@ def test_backward_rejects_bad_arguments(kw, code):
 
 def test_backward_workspace_size():
     ws = comba.bwd_workspace_size
-    # two fp32 states per chunk and head plus one float per chunk and head
-    state = 8 * 64 * 16 * 128 * 128 * 4
-    assert ws(8, 4096, 16, 128, 128) == 2 * state + 8 * 64 * 16 * 4
+    # per chunk and head: two fp32 states, three fp32 64 x 64 matrices, one float
+    pairs = 8 * 64 * 16
+    assert ws(8, 4096, 16, 128, 128) == pairs * (2 * 128 * 128 * 4 + 3 * 64 * 64 * 4 + 4)
     # packed: T / 64 + N + 1 slots
-    slots = 1000 // 64 + 5 + 1
-    assert ws(1, 1000, 2, 64, 64, 5) == 2 * slots * 2 * 64 * 64 * 4 + ((slots * 2 * 4 + 255) // 256) * 256
+    pairs = (1000 // 64 + 5 + 1) * 2
+    assert ws(1, 1000, 2, 64, 64, 5) == pairs * (2 * 64 * 64 * 4 + 3 * 64 * 64 * 4) + ((pairs * 4 + 255) // 256) * 256
 
 
 def test_workspace_rules():
