@@ -29,7 +29,8 @@
 //   chunk_bwd_prep_kernel  one workgroup per (chunk, head), all chunks at once:
 //                          Tinv, P and k_t.k_s of the chunk, stored;
 //   chunk_bwd_dh_kernel    reverse scan over chunks, one workgroup per
-//                          (sequence, head, 32 value channels): stores each
+//                          (sequence, head, 32 value channels), next chunk
+//                          prefetched into registers: stores each
 //                          chunk's outgoing-state gradient dh, writes dS_0;
 //   chunk_bwd_grad_kernel  one workgroup per (chunk, head): every per-token
 //                          gradient and a partial of dd;
@@ -204,12 +205,13 @@ struct SmemDh {
 };
 
 template <int K, int V, typename InT>
-__global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
+__global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
     const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0) {
-  constexpr int NT = 256, VT = kDhVT, NVT = V / VT, LQ = K + 4;
+  constexpr int NT = 512, VT = kDhVT, NVT = V / VT;
+  constexpr int QPT = 64 * K / NT, OPT = 64 * VT / NT, MPT = 64 * 16 / NT;  // staged elements per thread
   __shared__ SmemDh<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int unit, vt;
@@ -221,99 +223,125 @@ __global__ __launch_bounds__(256) void chunk_bwd_dh_kernel(
   const int nch = (t1 - t0 + 63) / 64;
   const bool packed = cu_seqlens != nullptr;
   const int64_t srow = (static_cast<int64_t>(n) * H + h) * V + vt * VT;  // state row of channel 0 of the tile
-  // thread blocks: (token pair, channel quad) for dUbar and dR; (key quad, channel quad) for dh,
-  // the latter for threads with kq < K (whole wavefronts)
-  const int tp = 2 * (tid >> 3), vq = 4 * (tid & 7);
-  const int kq = 4 * (tid >> 3);
-  const bool kact = kq < K;
+  // thread blocks: (token, channel quad) for dUbar and dR; (key pair, channel quad) for dh,
+  // the latter for threads with kp < K (whole wavefronts)
+  const int tr = tid >> 3, vq = 4 * (tid & 7);
+  const int kp = 2 * (tid >> 3);
+  const bool kact = kp < K;
+
+  // the next chunk's operands, loaded one chunk ahead into registers
+  float rq[QPT], rk[QPT], ro[OPT], ra = 1.f, rb = 0.f;
+  f32x4 rt[MPT], rp[MPT];
+  auto fetch = [&](int ci) {
+    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+    const int64_t mb = (chunk_slot(packed, t0, n, ci, T) * H + h) * 64 * 64;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = tid + j * NT, row = e / K, cc = e % K;
+      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
+      rq[j] = row < nrows ? ld(q, off) : 0.f;
+      rk[j] = row < nrows ? ld(k, off) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int e = tid + j * NT, row = e / VT, cc = e % VT;
+      ro[j] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + cc) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < MPT; ++j) {
+      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+      rt[j] = ld4(&Tg[mb + row * 64 + c4]);
+      rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+    }
+    if (tid < 64) {
+      ra = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
+      rb = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
+    }
+  };
 
   for (int e = tid; e < K * VT; e += NT) {
     const int kk = e % K, cc = e / K;
     sm.dh[kk][cc] = dsf ? dsf[(srow + cc) * K + kk] : 0.f;
   }
+  if (nch > 0) fetch(nch - 1);
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
     const int64_t slot = chunk_slot(packed, t0, n, ci, T);
-    const int64_t mb = (slot * H + h) * 64 * 64;
     __syncthreads();
-    stage_rows<K, LQ>(q, k, &sm.Qt[0][0], &sm.Kc[0][0], tok0, H, nrows, dh_, tid, NT);
-    for (int e = tid; e < 64 * VT; e += NT) {
-      const int row = e / VT, cc = e % VT;
-      sm.dO[row][cc] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + cc) : 0.f;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = tid + j * NT, row = e / K, cc = e % K;
+      sm.Kc[row][cc] = rk[j];
+      sm.Qt[row][cc] = rq[j] - dh_ * rk[j];
     }
-    for (int e = tid; e < 64 * 16; e += NT) {
-      const int row = e >> 4, c4 = 4 * (e & 15);
-      st4(&sm.Tm[row][c4], ld4(&Tg[mb + row * 64 + c4]));
-      st4(&sm.Pm[row][c4], ld4(&Pg[mb + row * 64 + c4]));
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int e = tid + j * NT;
+      sm.dO[e / VT][e % VT] = ro[j];
     }
-    stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
+#pragma unroll
+    for (int j = 0; j < MPT; ++j) {
+      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+      st4(&sm.Tm[row][c4], rt[j]);
+      st4(&sm.Pm[row][c4], rp[j]);
+    }
+    if (tid < 64) {
+      sm.gt.raw_a[tid] = ra;
+      sm.gt.raw_b[tid] = rb;
+    }
     // the gradient of this chunk's outgoing state, for the gradient kernel ([channel][key])
     if (kact) {
       float* dst = dhck + (slot * H + h) * V * K + static_cast<int64_t>(vt) * VT * K;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        f32x4 x;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = sm.dh[kq + i][vq + j];
-        st4(dst + static_cast<int64_t>(vq + j) * K + kq, x);
+        float* row = dst + static_cast<int64_t>(vq + j) * K + kp;
+        row[0] = sm.dh[kp][vq + j];
+        row[1] = sm.dh[kp + 1][vq + j];
       }
     }
     __syncthreads();
+    if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
     if (wave == 0) chunk_gates(sm.gt, lane, nrows);
     __syncthreads();
-    // dUbar = P^T dO + diag(e^(Gn - G)) K dh  (rows tp, tp+1; channels vq..vq+3)
+    // dUbar = P^T dO + diag(e^(Gn - G)) K dh  (row tr, channels vq..vq+3)
     {
-      f32x4 a0{0.f, 0.f, 0.f, 0.f}, a1{0.f, 0.f, 0.f, 0.f};
-      for (int t2 = tp; t2 < 64; ++t2) {
-        const f32x4 o = ld4(&sm.dO[t2][vq]);
-        a0 += sm.Pm[t2][tp] * o;
-        a1 += sm.Pm[t2][tp + 1] * o;
-      }
-      f32x4 k0{0.f, 0.f, 0.f, 0.f}, k1{0.f, 0.f, 0.f, 0.f};
+      f32x4 a{0.f, 0.f, 0.f, 0.f};
+      for (int t2 = tr; t2 < 64; ++t2) a += sm.Pm[t2][tr] * ld4(&sm.dO[t2][vq]);
+      f32x4 kd{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
       for (int kk = 0; kk < K; kk += 4) {
-        const f32x4 r0 = ld4(&sm.Kc[tp][kk]), r1 = ld4(&sm.Kc[tp + 1][kk]);
+        const f32x4 r = ld4(&sm.Kc[tr][kk]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const f32x4 dv = ld4(&sm.dh[kk + i][vq]);
-          k0 += r0[i] * dv;
-          k1 += r1[i] * dv;
-        }
+        for (int i = 0; i < 4; ++i) kd += r[i] * ld4(&sm.dh[kk + i][vq]);
       }
-      st4(&sm.dU[tp][vq], a0 + sm.gt.EGnG[tp] * k0);
-      st4(&sm.dU[tp + 1][vq], a1 + sm.gt.EGnG[tp + 1] * k1);
+      st4(&sm.dU[tr][vq], a + sm.gt.EGnG[tr] * kd);
     }
     __syncthreads();
     // dR = Tinv^T dUbar
-    f32x4 r0{0.f, 0.f, 0.f, 0.f}, r1{0.f, 0.f, 0.f, 0.f};
-    for (int t2 = tp; t2 < 64; ++t2) {
-      const f32x4 u = ld4(&sm.dU[t2][vq]);
-      r0 += sm.Tm[t2][tp] * u;
-      r1 += sm.Tm[t2][tp + 1] * u;
-    }
+    f32x4 r{0.f, 0.f, 0.f, 0.f};
+    for (int t2 = tr; t2 < 64; ++t2) r += sm.Tm[t2][tr] * ld4(&sm.dU[t2][vq]);
     __syncthreads();
-    st4(&sm.dU[tp][vq], r0);
-    st4(&sm.dU[tp + 1][vq], r1);
+    st4(&sm.dU[tr][vq], r);
     __syncthreads();
-    // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR   (keys kq..kq+3, channels vq..vq+3)
-    f32x4 acc[4];
+    // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR   (keys kp, kp+1; channels vq..vq+3)
+    f32x4 acc0, acc1;
     if (kact) {
       const float eGn = sm.gt.EG[63];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = eGn * ld4(&sm.dh[kq + i][vq]);
-#pragma unroll 2
+      acc0 = eGn * ld4(&sm.dh[kp][vq]);
+      acc1 = eGn * ld4(&sm.dh[kp + 1][vq]);
+#pragma unroll 4
       for (int t = 0; t < 64; ++t) {
-        const f32x4 qr = ld4(&sm.Qt[t][kq]), kr = ld4(&sm.Kc[t][kq]);
-        const f32x4 o = sm.gt.EG[t] * ld4(&sm.dO[t][vq]), r = sm.gt.bEGx[t] * ld4(&sm.dU[t][vq]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += qr[i] * o - kr[i] * r;
+        const float q0 = sm.Qt[t][kp], q1 = sm.Qt[t][kp + 1], k0 = sm.Kc[t][kp], k1 = sm.Kc[t][kp + 1];
+        const f32x4 o = sm.gt.EG[t] * ld4(&sm.dO[t][vq]), rr = sm.gt.bEGx[t] * ld4(&sm.dU[t][vq]);
+        acc0 += q0 * o - k0 * rr;
+        acc1 += q1 * o - k1 * rr;
       }
     }
     __syncthreads();
     if (kact) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st4(&sm.dh[kq + i][vq], acc[i]);
+      st4(&sm.dh[kp][vq], acc0);
+      st4(&sm.dh[kp + 1][vq], acc1);
     }
   }
   __syncthreads();
@@ -635,7 +663,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       nslots, a.Tg, a.Pg, a.KKg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 256, 0, st>>>(
+  chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 512, 0, st>>>(
       static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.alpha, a.beta, a.d,
       static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.dsf, a.dhck, a.ds0);
   e = hipGetLastError();
