@@ -58,12 +58,15 @@ def chunk_fwd_algorithmic(B, T, H, K, V, with_s0=True):
     return nbytes, flops
 
 
+# the sources the counted chunk-forward kernel is compiled from
+FWD_SOURCES = ("chunk_fwd_bf16.hip", "chunk_common.h", "device_common.h", "launch.h")
+
+
 def kernel_source_hash():
     csrc = os.path.join(ROOT, "bilinear_rnn_amd", "csrc")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(csrc)):
-        if f.startswith(("chunk_", "device_common")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    for f in FWD_SOURCES:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
