@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -113,7 +115,7 @@ __device__ __forceinline__ void stage_gates(ChunkGates& gt, const float* alpha, 
 // ---- prep: Tinv, P and k_t.k_s of every chunk -------------------------------------------
 
 template <int K>
-struct SmemPrep {
+struct SmemPrepValu {
   float QtT[K][kLdT];  // q~ transposed: [key channel][token]
   float KT[K][kLdT];
   float Am[64 * kLdF];
@@ -122,13 +124,30 @@ struct SmemPrep {
   ChunkGates gt;
 };
 
+struct SmemPrepMfma {
+  float Am[64 * kLdF];
+  float Tm[64 * kLdF];
+  float Ys[768];
+  ChunkGates gt;
+};
+
+// A (to LDS, for the inverse), P and k_t.k_s (to the per-chunk buffers) of one entry.
+__device__ __forceinline__ void prep_entry(const ChunkGates& gt, int t, int s, float kk, float qtk, float* Am,
+                                           float* Pg, float* KKg) {
+  Am[t * kLdF + s] = s < t ? gt.beta[t] * expf(gt.Gx[t] - gt.G[s]) * kk : 0.f;
+  Pg[t * 64 + s] = s <= t ? qtk * expf(fminf(gt.G[t] - gt.G[s], 0.f)) : 0.f;
+  KKg[t * 64 + s] = kk;
+}
+
 template <int K, typename InT>
 __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ d, const int32_t* __restrict__ cu_seqlens, int T,
     int H, int N, int64_t nslots, float* __restrict__ Tg, float* __restrict__ Pg, float* __restrict__ KKg) {
   constexpr int NT = 256;
-  __shared__ SmemPrep<K> sm;
+  constexpr bool kMfma = sizeof(InT) == 2;  // bf16 q / k: exact matrix-core operands
+  using Smem = typename std::conditional<kMfma, SmemPrepMfma, SmemPrepValu<K>>::type;
+  __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x % H;
   const int64_t slot = blockIdx.x / H;
@@ -138,55 +157,87 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
   const int c0 = t0 + 64 * c, nrows = min(64, t1 - c0);
   const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
   const float dh = d[h];
-  for (int e = tid; e < 64 * K; e += NT) {
-    const int row = e / K, cc = e % K;
-    float kv = 0.f, qv = 0.f;
-    if (row < nrows) {
-      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
-      kv = ld(k, off);
-      qv = ld(q, off);
+  const int64_t mb = (slot * H + h) * 64 * 64;
+  if constexpr (!kMfma) {
+    for (int e = tid; e < 64 * K; e += NT) {
+      const int row = e / K, cc = e % K;
+      float kv = 0.f, qv = 0.f;
+      if (row < nrows) {
+        const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
+        kv = ld(k, off);
+        qv = ld(q, off);
+      }
+      sm.KT[cc][row] = kv;
+      sm.QtT[cc][row] = qv - dh * kv;
     }
-    sm.KT[cc][row] = kv;
-    sm.QtT[cc][row] = qv - dh * kv;
   }
   stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
   __syncthreads();
   if (wave == 0) chunk_gates(sm.gt, lane, nrows);
   __syncthreads();
-  // 4 x 4 block of (t, s) per thread: k_t.k_s and q~_t.k_s
-  const int tb = 4 * (tid >> 4), sb = 4 * (tid & 15);
-  f32x4 kk[4], qk[4];
+  if constexpr (kMfma) {
+    // wavefront w: token rows 16 w .. 16 w + 15 against all 64 columns. Lane l
+    // supplies row (l % 16) of a block and the 8 keys 32 j + 8 (l / 16) + 0..7
+    // (the same keys for both operands), loaded straight from HBM; the
+    // accumulator gives rows 4 (l / 16) + i of column (l % 16).
+    const int l16 = lane & 15, g = lane >> 4, rb = wave;
+    const bf16x8 zero8 = {};
+    f32x4 akk[4], aqk[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kk[i] = qk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < 4; ++cb) akk[cb] = aqk[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ra = 16 * rb + l16;
+    const u16* kb_ = reinterpret_cast<const u16*>(k);
+    const u16* qb_ = reinterpret_cast<const u16*>(q);
+#pragma unroll
+    for (int j = 0; j < K / 32; ++j) {
+      const int kofs = 32 * j + 8 * g;
+      const bf16x8 ak = ra < nrows ? *reinterpret_cast<const bf16x8*>(kb_ + (tok0 + static_cast<int64_t>(ra) * H) * K + kofs)
+                                   : zero8;
+      const bf16x8 aq = ra < nrows ? *reinterpret_cast<const bf16x8*>(qb_ + (tok0 + static_cast<int64_t>(ra) * H) * K + kofs)
+                                   : zero8;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int rcol = 16 * cb + l16;
+        const bf16x8 bk = rcol < nrows
+                              ? *reinterpret_cast<const bf16x8*>(kb_ + (tok0 + static_cast<int64_t>(rcol) * H) * K + kofs)
+                              : zero8;
+        akk[cb] = mfma16x16x32(ak, bk, akk[cb]);
+        aqk[cb] = mfma16x16x32(aq, bk, aqk[cb]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * rb + 4 * g + i, s_ = 16 * cb + l16;
+        prep_entry(sm.gt, t, s_, akk[cb][i], aqk[cb][i] - dh * akk[cb][i], sm.Am, Pg + mb, KKg + mb);
+      }
+    }
+  } else {
+    // 4 x 4 block of (t, s) per thread: k_t.k_s and q~_t.k_s
+    const int tb = 4 * (tid >> 4), sb = 4 * (tid & 15);
+    f32x4 kk[4], qk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kk[i] = qk[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int cc = 0; cc < K; ++cc) {
-    const f32x4 kt = ld4(&sm.KT[cc][tb]), ks = ld4(&sm.KT[cc][sb]), qt = ld4(&sm.QtT[cc][tb]);
+    for (int cc = 0; cc < K; ++cc) {
+      const f32x4 kt = ld4(&sm.KT[cc][tb]), ks = ld4(&sm.KT[cc][sb]), qt = ld4(&sm.QtT[cc][tb]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      kk[i] += kt[i] * ks;
-      qk[i] += qt[i] * ks;
+      for (int i = 0; i < 4; ++i) {
+        kk[i] += kt[i] * ks;
+        qk[i] += qt[i] * ks;
+      }
     }
-  }
-  const int64_t mb = (slot * H + h) * 64 * 64;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = tb + i;
-    f32x4 a, p;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = sb + j;
-      a[j] = s < t ? sm.gt.beta[t] * expf(sm.gt.Gx[t] - sm.gt.G[s]) * kk[i][j] : 0.f;
-      p[j] = s <= t ? qk[i][j] * expf(fminf(sm.gt.G[t] - sm.gt.G[s], 0.f)) : 0.f;
-    }
-    st4(&sm.Am[t * kLdF + sb], a);
-    st4(&Pg[mb + t * 64 + sb], p);
-    st4(&KKg[mb + t * 64 + sb], kk[i]);
+      for (int j = 0; j < 4; ++j) prep_entry(sm.gt, tb + i, sb + j, kk[i][j], qk[i][j], sm.Am, Pg + mb, KKg + mb);
   }
   __syncthreads();
   unit_lower_inverse64<NT>(sm.Am, sm.Tm, sm.Ys, tid);
   for (int e = tid; e < 64 * 64; e += NT) {
-    const int t = e >> 6, s = e & 63;
-    Tg[mb + e] = s <= t ? sm.Tm[t * kLdF + s] : 0.f;
+    const int t = e >> 6, s_ = e & 63;
+    Tg[mb + e] = s_ <= t ? sm.Tm[t * kLdF + s_] : 0.f;
   }
 }
 
@@ -430,7 +481,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   f32x4 accA[2], accP[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) accA[i] = accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sQh = 0.f, sbR = 0.f, sKhdR = 0.f, st2 = 0.f, shdh = 0.f;
+  float sbR = 0.f, sKhdR = 0.f, st2 = 0.f, shdh = 0.f;
 
   for (int jt = 0; jt < NTILE; ++jt) {
     const int v0 = jt * VT;
@@ -445,18 +496,16 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     }
     sm.dOT[tv][tr] = tr < nrows ? ld(dO, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
     __syncthreads();
-    float kh, qh, kdh;
+    float kh, kdh;
     {
-      f32x4 a{0.f, 0.f, 0.f, 0.f}, bq{0.f, 0.f, 0.f, 0.f}, cd{0.f, 0.f, 0.f, 0.f};
+      f32x4 a{0.f, 0.f, 0.f, 0.f}, cd{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
       for (int kk = 0; kk < K; kk += 4) {
-        const f32x4 kr = ld4(&sm.Kc[tr][kk]), hv = ld4(&sm.hT[tv][kk]);
-        a += kr * hv;
-        bq += ld4(&sm.Qt[tr][kk]) * hv;
+        const f32x4 kr = ld4(&sm.Kc[tr][kk]);
+        a += kr * ld4(&sm.hT[tv][kk]);
         cd += kr * ld4(&sm.dhT[tv][kk]);
       }
       kh = hsum(a);
-      qh = hsum(bq);
       kdh = hsum(cd);
     }
     const float vv = tr < nrows ? ld(v, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
@@ -484,7 +533,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     __syncthreads();
     sm.dRT[tv][tr] = dr;
     if (tr < nrows) dv[(tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv] = be_t * dr;
-    sQh += qh * sm.dOT[tv][tr];
     sbR += dr * (vv - eGx_t * kh);
     sKhdR += kh * dr;
     st2 += kdh * ub;
@@ -516,16 +564,23 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   // per-token sums over the 8 channel lanes of a row; <h, dh> over the block
 #pragma unroll
   for (int m = 1; m < 8; m <<= 1) {
-    sQh += __shfl_xor(sQh, m, kWave);
     sbR += __shfl_xor(sbR, m, kWave);
     sKhdR += __shfl_xor(sKhdR, m, kWave);
     st2 += __shfl_xor(st2, m, kWave);
   }
   if (tv == 0) {
-    sm.vec[0][tr] = sQh;
     sm.vec[1][tr] = sbR;
     sm.vec[2][tr] = sKhdR;
     sm.vec[3][tr] = st2;
+  }
+  // sum over channels of (Qt h)_t . dO_t = sum over keys of Qt_t . (dO h^T)_t, from the
+  // accumulated dO h^T: the NKQ consecutive lanes of a row block hold its keys
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    float x = hsum(ld4(&sm.Qt[bt + i][bk]) * accQ[i]);
+#pragma unroll
+    for (int m = 1; m < NKQ; m <<= 1) x += __shfl_xor(x, m, kWave);
+    if (tid % NKQ == 0) sm.vec[0][bt + i] = x;
   }
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) shdh += __shfl_xor(shdh, m, kWave);
