@@ -52,7 +52,6 @@ namespace comba {
 namespace {
 
 constexpr int kDhVT = 32;  // value channels per workgroup of the reverse scan
-constexpr int kGrVT = 8;   // value channels per tile of the gradient kernel
 constexpr int kLdT = 68;   // row stride of 64-wide fp32 tiles (16-byte aligned rows)
 
 template <typename InT>
@@ -406,24 +405,47 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
 
 // ---- per-chunk gradients ------------------------------------------------------------------
 
+// D += A (16 x 4) B (4 x 16) in fp32 on the matrix cores. Lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; D holds rows 4 (l / 16) + i of
+// column (l % 16).
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+constexpr int kGrVT = 16;  // value channels per tile of the gradient kernel
+constexpr int kLdV = kGrVT + 4;
+
 template <int K>
 struct SmemGrad {
   float Qt[64][K + 4];
   float Kc[64][K + 4];
-  float Tm[64][kLdT];        // Tinv, then dP (.) M
-  float TT[64][kLdT];        // Tinv^T, then W = dA (.) E
-  float PT[64][kLdT];        // P^T, then (dP (.) P)^T
-  float X4[64][kLdT];        // X = W (.) k_t.k_s
-  float hT[kGrVT][K + 4];    // state tile, [channel][key]
-  float dhT[kGrVT][K + 4];
-  float dOT[kGrVT][kLdT];    // [channel][token]
-  float UT[kGrVT][kLdT];     // R, then Ubar
-  float dRT[kGrVT][kLdT];    // dUbar, then dR
+  float Tm[64][kLdT];  // Tinv, then dP (.) M
+  float Pm[64][kLdT];  // P, then dP (.) P
+  union {
+    struct {
+      float S[kGrVT][K + 4];   // state tile, [channel][key]
+      float dS[kGrVT][K + 4];  // outgoing-state gradient tile
+      float dO[64][kLdV];      // [token][channel]
+      float R[64][kLdV];
+      float U[64][kLdV];       // Ubar
+      float dU[64][kLdV];      // dUbar, then dR
+    } t;
+    struct {
+      float W[64][kLdT];  // dA (.) E
+      float X[64][kLdT];  // W (.) k_t.k_s
+    } p;
+  } u;
   ChunkGates gt;
-  float vec[8][64];
+  float vec[10][64];
   float red[16];
 };
 
+// Gradients of one (chunk, head). Wavefront w owns token block tb = w % 4
+// (rows 16 tb ..) and, with half hw = w / 4, the 16 x 16 blocks (tb, key
+// block KBW hw + c) of the 64 x K accumulators and (tb, 2 hw + c) of the
+// 64 x 64 ones. Per value tile, the hw = 0 waves form K h, R, Ubar and dR of
+// their token block and the hw = 1 waves K dh and dUbar; then every wave
+// accumulates its blocks of dO h^T, Ubar dh^T, dR h^T, dR Ubar^T, dO Ubar^T.
 template <int K, int V, typename InT>
 __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
@@ -432,9 +454,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     const float* __restrict__ hck, const float* __restrict__ dhck, const float* __restrict__ Tg,
     const float* __restrict__ Pg, const float* __restrict__ KKg, float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta, float* __restrict__ dd_part) {
-  constexpr int NT = 512, VT = kGrVT, NTILE = V / VT, LQ = K + 4;
-  constexpr int TB = 64 * K / (4 * NT);  // token rows per thread in the 64 x K blocks (4 keys each)
-  constexpr int NKQ = K / 4;
+  constexpr int NT = 512, VT = kGrVT, NTILE = V / VT, LQ = K + 4, KB = K / 16, KBW = KB / 2;
   __shared__ SmemGrad<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x % H;
@@ -455,208 +475,236 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   stage_rows<K, LQ>(q, k, &sm.Qt[0][0], &sm.Kc[0][0], tok0, H, nrows, dh_, tid, NT);
   for (int e = tid; e < 64 * 16; e += NT) {
     const int row = e >> 4, c4 = 4 * (e & 15);
-    const f32x4 tv = ld4(&Tg[mb + row * 64 + c4]), pv = ld4(&Pg[mb + row * 64 + c4]);
-    st4(&sm.Tm[row][c4], tv);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sm.TT[c4 + j][row] = tv[j];
-      sm.PT[c4 + j][row] = pv[j];
-    }
+    st4(&sm.Tm[row][c4], ld4(&Tg[mb + row * 64 + c4]));
+    st4(&sm.Pm[row][c4], ld4(&Pg[mb + row * 64 + c4]));
   }
   stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
   __syncthreads();
   if (wave == 0) chunk_gates(sm.gt, lane, nrows);
   __syncthreads();
 
-  // (token, channel) of a value tile
-  const int tr = tid >> 3, tv = tid & 7;
-  const float be_t = sm.gt.beta[tr], b1_t = sm.gt.bEGx[tr], eGnG_t = sm.gt.EGnG[tr], eGx_t = expf(sm.gt.Gx[tr]);
-  // 64 x K blocks: TB token rows x 4 keys
-  const int bt = TB * (tid / NKQ), bk = 4 * (tid % NKQ);
-  f32x4 accQ[TB], accK[TB];
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const int tb = wave & 3, hw = wave >> 2;
+  const int ta = 16 * tb + l16;  // token row this lane supplies to A operands
+  f32x4 accQ[KBW], accK[KBW], accA[2], accP[2];
 #pragma unroll
-  for (int i = 0; i < TB; ++i) accQ[i] = accK[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // 64 x 64 blocks: 2 token rows x 4 columns
-  const int at = 2 * (tid >> 4), as = 4 * (tid & 15);
-  f32x4 accA[2], accP[2];
+  for (int i = 0; i < KBW; ++i) accQ[i] = accK[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 2; ++i) accA[i] = accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float sbR = 0.f, sKhdR = 0.f, st2 = 0.f, shdh = 0.f;
+  // per-lane sums over the tile channels, for the accumulator rows 16 tb + 4 l4 + i
+  float sbR[4] = {0.f, 0.f, 0.f, 0.f}, sKhdR[4] = {0.f, 0.f, 0.f, 0.f}, st2[4] = {0.f, 0.f, 0.f, 0.f};
+  float shdh = 0.f;
 
   for (int jt = 0; jt < NTILE; ++jt) {
     const int v0 = jt * VT;
     __syncthreads();
-    for (int e = tid; e < K * VT / 4; e += NT) {
-      const int c4 = 4 * (e % NKQ), cc = e / NKQ;
-      const f32x4 hv = ld4(hsrc + static_cast<int64_t>(v0 + cc) * K + c4);
-      const f32x4 dv_ = ld4(dhsrc + static_cast<int64_t>(v0 + cc) * K + c4);
-      st4(&sm.hT[cc][c4], hv);
-      st4(&sm.dhT[cc][c4], dv_);
+    for (int e = tid; e < VT * K / 4; e += NT) {
+      const int row = e / (K / 4), c4 = 4 * (e % (K / 4));
+      const f32x4 hv = ld4(hsrc + static_cast<int64_t>(v0 + row) * K + c4);
+      const f32x4 dv_ = ld4(dhsrc + static_cast<int64_t>(v0 + row) * K + c4);
+      st4(&sm.u.t.S[row][c4], hv);
+      st4(&sm.u.t.dS[row][c4], dv_);
       shdh += hsum(hv * dv_);
     }
-    sm.dOT[tv][tr] = tr < nrows ? ld(dO, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
-    __syncthreads();
-    float kh, kdh;
-    {
-      f32x4 a{0.f, 0.f, 0.f, 0.f}, cd{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int kk = 0; kk < K; kk += 4) {
-        const f32x4 kr = ld4(&sm.Kc[tr][kk]);
-        a += kr * ld4(&sm.hT[tv][kk]);
-        cd += kr * ld4(&sm.dhT[tv][kk]);
-      }
-      kh = hsum(a);
-      kdh = hsum(cd);
-    }
-    const float vv = tr < nrows ? ld(v, (tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv) : 0.f;
-    sm.UT[tv][tr] = be_t * vv - b1_t * kh;  // R
-    __syncthreads();
-    float ub, du;
-    {
-      f32x4 a{0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s <= tr; s += 4) a += ld4(&sm.Tm[tr][s]) * ld4(&sm.UT[tv][s]);  // Tinv is 0 above the diagonal
-      ub = hsum(a);
-      f32x4 p{0.f, 0.f, 0.f, 0.f};
-      for (int t2 = tr & ~3; t2 < 64; t2 += 4) p += ld4(&sm.PT[tr][t2]) * ld4(&sm.dOT[tv][t2]);  // P^T is 0 below
-      du = eGnG_t * kdh + hsum(p);
+    for (int e = tid; e < 64 * VT; e += NT) {
+      const int t = e / VT, cc = e % VT;
+      sm.u.t.dO[t][cc] = t < nrows ? ld(dO, (tok0 + static_cast<int64_t>(t) * H) * V + v0 + cc) : 0.f;
     }
     __syncthreads();
-    sm.UT[tv][tr] = ub;
-    sm.dRT[tv][tr] = du;
-    __syncthreads();
-    float dr;
+    // K h (hw = 0) or K dh (hw = 1) for token block tb; B[k][v] = X[v][k]
+    f32x4 kx{0.f, 0.f, 0.f, 0.f};
     {
-      f32x4 a{0.f, 0.f, 0.f, 0.f};
-      for (int t2 = tr & ~3; t2 < 64; t2 += 4) a += ld4(&sm.TT[tr][t2]) * ld4(&sm.dRT[tv][t2]);
-      dr = hsum(a);
+      const float(*X)[K + 4] = hw == 0 ? sm.u.t.S : sm.u.t.dS;
+#pragma unroll 8
+      for (int j = 0; j < K / 4; ++j) kx = mma4(sm.Kc[ta][4 * j + l4], X[l16][4 * j + l4], kx);
     }
-    __syncthreads();
-    sm.dRT[tv][tr] = dr;
-    if (tr < nrows) dv[(tok0 + static_cast<int64_t>(tr) * H) * V + v0 + tv] = be_t * dr;
-    sbR += dr * (vv - eGx_t * kh);
-    sKhdR += kh * dr;
-    st2 += kdh * ub;
-    __syncthreads();
-    // dA -= dR Ubar^T, dP += dO Ubar^T (masked at the end)
+    float vv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (hw == 0) {
 #pragma unroll
-    for (int cc = 0; cc < VT; ++cc) {
-      const f32x4 us = ld4(&sm.UT[cc][as]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        accA[i] -= sm.dRT[cc][at + i] * us;
-        accP[i] += sm.dOT[cc][at + i] * us;
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tb + 4 * l4 + i;
+        vv[i] = t < nrows ? ld(v, (tok0 + static_cast<int64_t>(t) * H) * V + v0 + l16) : 0.f;
+        sm.u.t.R[t][l16] = sm.gt.beta[t] * vv[i] - sm.gt.bEGx[t] * kx[i];
       }
     }
-    // dQt += dO h^T;  dK += -diag(b1) dR h^T + diag(e^(Gn - G)) Ubar dh^T
+    __syncthreads();
+    if (hw == 0) {
+      // Ubar = Tinv R (Tinv is zero above the diagonal)
+      f32x4 u{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < 4 * (tb + 1); ++j) u = mma4(sm.Tm[ta][4 * j + l4], sm.u.t.R[4 * j + l4][l16], u);
 #pragma unroll
-    for (int cc = 0; cc < VT; ++cc) {
-      const f32x4 hv = ld4(&sm.hT[cc][bk]), dv_ = ld4(&sm.dhT[cc][bk]);
+      for (int i = 0; i < 4; ++i) sm.u.t.U[16 * tb + 4 * l4 + i][l16] = u[i];
+    } else {
+      // dUbar = P^T dO + diag(e^(Gn - G)) K dh; A[t][t'] = P[t'][t], zero for t' < t
+      f32x4 du;
 #pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        const int t = bt + i;
-        accQ[i] += sm.dOT[cc][t] * hv;
-        accK[i] += (sm.gt.EGnG[t] * sm.UT[cc][t]) * dv_ - (sm.gt.bEGx[t] * sm.dRT[cc][t]) * hv;
+      for (int i = 0; i < 4; ++i) du[i] = sm.gt.EGnG[16 * tb + 4 * l4 + i] * kx[i];
+      for (int j = 4 * tb; j < 16; ++j) du = mma4(sm.Pm[4 * j + l4][ta], sm.u.t.dO[4 * j + l4][l16], du);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.u.t.dU[16 * tb + 4 * l4 + i][l16] = du[i];
+    }
+    __syncthreads();
+    f32x4 dr{0.f, 0.f, 0.f, 0.f};
+    if (hw == 0) {
+      // dR = Tinv^T dUbar
+      for (int j = 4 * tb; j < 16; ++j) dr = mma4(sm.Tm[4 * j + l4][ta], sm.u.t.dU[4 * j + l4][l16], dr);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st2[i] += kx[i] * sm.u.t.U[16 * tb + 4 * l4 + i][l16];
+    }
+    __syncthreads();
+    if (hw == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * tb + 4 * l4 + i;
+        sm.u.t.dU[t][l16] = dr[i];
+        if (t < nrows) dv[(tok0 + static_cast<int64_t>(t) * H) * V + v0 + l16] = sm.gt.beta[t] * dr[i];
+        sbR[i] += dr[i] * (vv[i] - expf(sm.gt.Gx[t]) * kx[i]);
+        sKhdR[i] += kx[i] * dr[i];
+      }
+    }
+    __syncthreads();
+    // accumulators over the tile's channels (reduction index 4 j + l4)
+#pragma unroll
+    for (int j = 0; j < VT / 4; ++j) {
+      const int vc = 4 * j + l4;
+      const float aO = sm.u.t.dO[ta][vc];
+      const float aR = sm.u.t.dU[ta][vc];  // dR
+      const float aU = sm.gt.EGnG[ta] * sm.u.t.U[ta][vc];
+      const float aRb = -sm.gt.bEGx[ta] * aR;
+#pragma unroll
+      for (int cb = 0; cb < KBW; ++cb) {
+        const int kcol = 16 * (KBW * hw + cb) + l16;
+        const float bS = sm.u.t.S[vc][kcol], bdS = sm.u.t.dS[vc][kcol];
+        accQ[cb] = mma4(aO, bS, accQ[cb]);
+        accK[cb] = mma4(aU, bdS, accK[cb]);
+        accK[cb] = mma4(aRb, bS, accK[cb]);
+      }
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const float bU = sm.u.t.U[16 * (2 * hw + cb) + l16][vc];  // B[v][s] = Ubar[s][v]
+        accA[cb] = mma4(-aR, bU, accA[cb]);
+        accP[cb] = mma4(aO, bU, accP[cb]);
       }
     }
   }
   __syncthreads();
 
-  // per-token sums over the 8 channel lanes of a row; <h, dh> over the block
+  // sums over channels: reduce over the 16 lanes of a row group
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
-    sbR += __shfl_xor(sbR, m, kWave);
-    sKhdR += __shfl_xor(sKhdR, m, kWave);
-    st2 += __shfl_xor(st2, m, kWave);
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      sbR[i] += __shfl_xor(sbR[i], m, kWave);
+      sKhdR[i] += __shfl_xor(sKhdR[i], m, kWave);
+      st2[i] += __shfl_xor(st2[i], m, kWave);
+    }
   }
-  if (tv == 0) {
-    sm.vec[1][tr] = sbR;
-    sm.vec[2][tr] = sKhdR;
-    sm.vec[3][tr] = st2;
+  if (l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * l4 + i;
+      if (hw == 0) {
+        sm.vec[1][t] = sbR[i];
+        sm.vec[2][t] = sKhdR[i];
+      } else {
+        sm.vec[3][t] = st2[i];
+      }
+    }
   }
-  // sum over channels of (Qt h)_t . dO_t = sum over keys of Qt_t . (dO h^T)_t, from the
-  // accumulated dO h^T: the NKQ consecutive lanes of a row block hold its keys
+  // sum over channels of (Qt h)_t . dO_t = sum over keys of Qt_t . (dO h^T)_t, per wave half
 #pragma unroll
-  for (int i = 0; i < TB; ++i) {
-    float x = hsum(ld4(&sm.Qt[bt + i][bk]) * accQ[i]);
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * tb + 4 * l4 + i;
+    float x = 0.f;
 #pragma unroll
-    for (int m = 1; m < NKQ; m <<= 1) x += __shfl_xor(x, m, kWave);
-    if (tid % NKQ == 0) sm.vec[0][bt + i] = x;
+    for (int cb = 0; cb < KBW; ++cb) x += sm.Qt[t][16 * (KBW * hw + cb) + l16] * accQ[cb][i];
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, kWave);
+    if (l16 == 0) sm.vec[8 + hw][t] = x;
   }
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) shdh += __shfl_xor(shdh, m, kWave);
   if (lane == 0) sm.red[wave] = shdh;
-  // dP (.) M -> Tm, W = dA (.) E -> TT, (dP (.) P)^T -> PT, X = W (.) KK -> X4
-  // (each thread rewrites only the entries of its own 2 x 4 block)
+  // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cb)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int t = at + i;
-    const f32x4 kkv = ld4(&KKg[mb + t * 64 + as]);
-    f32x4 pm, w, x;
+  for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = as + j;
-      const float M = s <= t ? expf(fminf(sm.gt.G[t] - sm.gt.G[s], 0.f)) : 0.f;
-      const float E = s < t ? expf(fminf(sm.gt.Gx[t] - sm.gt.G[s], 0.f)) : 0.f;
-      const float dpv = s <= t ? accP[i][j] : 0.f, dav = s < t ? accA[i][j] : 0.f;
-      pm[j] = dpv * M;
-      w[j] = dav * E;
-      x[j] = w[j] * kkv[j];
-      sm.PT[s][t] = dpv * sm.PT[s][t];
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * l4 + i, s_ = 16 * (2 * hw + cb) + l16;
+      const float M = s_ <= t ? expf(fminf(sm.gt.G[t] - sm.gt.G[s_], 0.f)) : 0.f;
+      const float E = s_ < t ? expf(fminf(sm.gt.Gx[t] - sm.gt.G[s_], 0.f)) : 0.f;
+      const float dpv = s_ <= t ? accP[cb][i] : 0.f, dav = s_ < t ? accA[cb][i] : 0.f;
+      const float w = dav * E;
+      sm.Pm[t][s_] = dpv * sm.Pm[t][s_];  // dP (.) P
+      sm.Tm[t][s_] = dpv * M;             // dP (.) M
+      sm.u.p.W[t][s_] = w;
+      sm.u.p.X[t][s_] = w * KKg[mb + t * 64 + s_];
     }
-    st4(&sm.Tm[t][as], pm);
-    st4(&sm.TT[t][as], w);
-    st4(&sm.X4[t][as], x);
   }
   __syncthreads();
   // row and column sums (fixed order)
   if (tid < 64) {
     float rp = 0.f, rx = 0.f;
-    for (int s = 0; s < 64; ++s) {
-      rp += sm.PT[s][tid];
-      rx += sm.X4[tid][s];
+    for (int s_ = 0; s_ < 64; ++s_) {
+      rp += sm.Pm[tid][s_];
+      rx += sm.u.p.X[tid][s_];
     }
     sm.vec[4][tid] = rp;
     sm.vec[5][tid] = rx;
   } else if (tid < 128) {
-    const int s = tid - 64;
+    const int s_ = tid - 64;
     float cp = 0.f, cx = 0.f;
     for (int t = 0; t < 64; ++t) {
-      cp += sm.PT[s][t];
-      cx += sm.gt.beta[t] * sm.X4[t][s];
+      cp += sm.Pm[t][s_];
+      cx += sm.gt.beta[t] * sm.u.p.X[t][s_];
     }
-    sm.vec[6][s] = cp;
-    sm.vec[7][s] = cx;
+    sm.vec[6][s_] = cp;
+    sm.vec[7][s_] = cx;
   }
-  // dq, dk (rows bt.., keys bk..bk+3) and this thread's part of dd
-  f32x4 xq[TB], xk[TB];
+  // dq, dk of the blocks (tb, KBW hw + cb)
+  f32x4 xq[KBW], xk[KBW];
 #pragma unroll
-  for (int i = 0; i < TB; ++i) {
-    xq[i] = sm.gt.EG[bt + i] * accQ[i];
-    xk[i] = accK[i];
+  for (int cb = 0; cb < KBW; ++cb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xq[cb][i] = sm.gt.EG[16 * tb + 4 * l4 + i] * accQ[cb][i];
+    xk[cb] = accK[cb];
   }
-  for (int s = 0; s < 64; ++s) {
-    const f32x4 ks = ld4(&sm.Kc[s][bk]), qs = ld4(&sm.Qt[s][bk]);
-    const float bs = sm.gt.beta[s];
+  const float bta = sm.gt.beta[ta];
+  for (int j = 0; j < 4 * (tb + 1); ++j) {  // columns s <= t: (dP (.) M) K and diag(beta) W K
+    const int sr = 4 * j + l4;
+    const float a1 = sm.Tm[ta][sr], a2 = bta * sm.u.p.W[ta][sr];
 #pragma unroll
-    for (int i = 0; i < TB; ++i) {
-      const int t = bt + i;
-      // row t of (dP (.) M) K and of diag(beta) W K (zero above the diagonal)
-      xq[i] += sm.Tm[t][s] * ks;
-      xk[i] += (sm.gt.beta[t] * sm.TT[t][s]) * ks;
-      // column t of (dP (.) M)^T Qt and of W^T diag(beta) K
-      xk[i] += sm.Tm[s][t] * qs + (sm.TT[s][t] * bs) * ks;
+    for (int cb = 0; cb < KBW; ++cb) {
+      const float bK = sm.Kc[sr][16 * (KBW * hw + cb) + l16];
+      xq[cb] = mma4(a1, bK, xq[cb]);
+      xk[cb] = mma4(a2, bK, xk[cb]);
+    }
+  }
+  for (int j = 4 * tb; j < 16; ++j) {  // rows t' >= t: (dP (.) M)^T Qt and W^T diag(beta) K
+    const int tr2 = 4 * j + l4;
+    const float a1 = sm.Tm[tr2][ta], a2 = sm.u.p.W[tr2][ta], bb = sm.gt.beta[tr2];
+#pragma unroll
+    for (int cb = 0; cb < KBW; ++cb) {
+      const int kc = 16 * (KBW * hw + cb) + l16;
+      xk[cb] = mma4(a1, sm.Qt[tr2][kc], xk[cb]);
+      xk[cb] = mma4(a2, bb * sm.Kc[tr2][kc], xk[cb]);
     }
   }
   float ddp = 0.f;
 #pragma unroll
-  for (int i = 0; i < TB; ++i) {
-    const int t = bt + i;
-    xk[i] -= dh_ * xq[i];
-    ddp -= hsum(xq[i] * ld4(&sm.Kc[t][bk]));
-    if (t < nrows) {
-      const int64_t off = (tok0 + static_cast<int64_t>(t) * H) * K + bk;
-      st4(dq + off, xq[i]);
-      st4(dk + off, xk[i]);
+  for (int cb = 0; cb < KBW; ++cb) {
+    const int kc = 16 * (KBW * hw + cb) + l16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * l4 + i;
+      xk[cb][i] -= dh_ * xq[cb][i];
+      ddp -= xq[cb][i] * sm.Kc[t][kc];
+      if (t < nrows) {
+        const int64_t off = (tok0 + static_cast<int64_t>(t) * H) * K + kc;
+        dq[off] = xq[cb][i];
+        dk[off] = xk[cb][i];
+      }
     }
   }
 #pragma unroll
@@ -671,7 +719,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     for (int w = 0; w < NT / 64; ++w) hd += sm.red[w];
     const float be = sm.gt.beta[t], b1 = sm.gt.bEGx[t];
     const float t2 = sm.gt.EGnG[t] * sm.vec[3][t];
-    float dG = sm.gt.EG[t] * sm.vec[0][t] + sm.vec[4][t] - sm.vec[6][t] - sm.vec[7][t] - t2;
+    const float sqh = sm.vec[8][t] + sm.vec[9][t];
+    float dG = sm.gt.EG[t] * sqh + sm.vec[4][t] - sm.vec[6][t] - sm.vec[7][t] - t2;
     const float dGx = be * sm.vec[5][t] - b1 * sm.vec[2][t];
     float sum_t2 = t2;
 #pragma unroll
@@ -689,9 +738,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
       dalpha[off] = dlog / sm.gt.raw_a[t];
     }
     if (t == 0) {
-      float s = 0.f;
-      for (int w = 0; w < NT / 64; ++w) s += sm.red[8 + w];
-      dd_part[slot * H + h] = s;
+      float s2 = 0.f;
+      for (int w = 0; w < NT / 64; ++w) s2 += sm.red[8 + w];
+      dd_part[slot * H + h] = s2;
     }
   }
 }
