@@ -35,10 +35,10 @@
 //   chunk_bwd_grad_kernel  one workgroup per (chunk, head): every per-token
 //                          gradient and a partial of dd;
 //   dd_reduce_kernel       dd per head, summed over chunks in a fixed order.
-// All arithmetic is fp32 on the vector units. Each thread owns a small block
-// of outputs and reads its operands as 16-byte LDS vectors from layouts chosen
-// per product (rows, or transposed copies), so that every LDS read feeds
-// several multiply-adds.
+// The scan and the gradient kernel form their products on the fp32 matrix
+// cores (16 x 16 x 4 tiles, exact fp32 operands read from row-major LDS
+// buffers; a transposed operand only swaps the fragment's indices). The prep
+// kernel uses bf16 matrix cores for bf16 inputs and the vector units for fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -259,149 +259,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
-    const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0) {
-  constexpr int NT = 512, VT = kDhVT, NVT = V / VT;
-  constexpr int QPT = 64 * K / NT, OPT = 64 * VT / NT, MPT = 64 * 16 / NT;  // staged elements per thread
-  __shared__ SmemDh<K> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int unit, vt;
-  if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
-  const int h = unit % H, n = unit / H;
-  int b, t0, t1;
-  sequence_range(cu_seqlens, n, T, b, t0, t1);
-  const float dh_ = d[h];
-  const int nch = (t1 - t0 + 63) / 64;
-  const bool packed = cu_seqlens != nullptr;
-  const int64_t srow = (static_cast<int64_t>(n) * H + h) * V + vt * VT;  // state row of channel 0 of the tile
-  // thread blocks: (token, channel quad) for dUbar and dR; (key pair, channel quad) for dh,
-  // the latter for threads with kp < K (whole wavefronts)
-  const int tr = tid >> 3, vq = 4 * (tid & 7);
-  const int kp = 2 * (tid >> 3);
-  const bool kact = kp < K;
-
-  // the next chunk's operands, loaded one chunk ahead into registers
-  float rq[QPT], rk[QPT], ro[OPT], ra = 1.f, rb = 0.f;
-  f32x4 rt[MPT], rp[MPT];
-  auto fetch = [&](int ci) {
-    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
-    const int64_t mb = (chunk_slot(packed, t0, n, ci, T) * H + h) * 64 * 64;
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int e = tid + j * NT, row = e / K, cc = e % K;
-      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
-      rq[j] = row < nrows ? ld(q, off) : 0.f;
-      rk[j] = row < nrows ? ld(k, off) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int e = tid + j * NT, row = e / VT, cc = e % VT;
-      ro[j] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + cc) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) {
-      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-      rt[j] = ld4(&Tg[mb + row * 64 + c4]);
-      rp[j] = ld4(&Pg[mb + row * 64 + c4]);
-    }
-    if (tid < 64) {
-      ra = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
-      rb = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
-    }
-  };
-
-  for (int e = tid; e < K * VT; e += NT) {
-    const int kk = e % K, cc = e / K;
-    sm.dh[kk][cc] = dsf ? dsf[(srow + cc) * K + kk] : 0.f;
-  }
-  if (nch > 0) fetch(nch - 1);
-  for (int ci = nch - 1; ci >= 0; --ci) {
-    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    const int64_t slot = chunk_slot(packed, t0, n, ci, T);
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int e = tid + j * NT, row = e / K, cc = e % K;
-      sm.Kc[row][cc] = rk[j];
-      sm.Qt[row][cc] = rq[j] - dh_ * rk[j];
-    }
-#pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int e = tid + j * NT;
-      sm.dO[e / VT][e % VT] = ro[j];
-    }
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) {
-      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-      st4(&sm.Tm[row][c4], rt[j]);
-      st4(&sm.Pm[row][c4], rp[j]);
-    }
-    if (tid < 64) {
-      sm.gt.raw_a[tid] = ra;
-      sm.gt.raw_b[tid] = rb;
-    }
-    // the gradient of this chunk's outgoing state, for the gradient kernel ([channel][key])
-    if (kact) {
-      float* dst = dhck + (slot * H + h) * V * K + static_cast<int64_t>(vt) * VT * K;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float* row = dst + static_cast<int64_t>(vq + j) * K + kp;
-        row[0] = sm.dh[kp][vq + j];
-        row[1] = sm.dh[kp + 1][vq + j];
-      }
-    }
-    __syncthreads();
-    if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
-    if (wave == 0) chunk_gates(sm.gt, lane, nrows);
-    __syncthreads();
-    // dUbar = P^T dO + diag(e^(Gn - G)) K dh  (row tr, channels vq..vq+3)
-    {
-      f32x4 a{0.f, 0.f, 0.f, 0.f};
-      for (int t2 = tr; t2 < 64; ++t2) a += sm.Pm[t2][tr] * ld4(&sm.dO[t2][vq]);
-      f32x4 kd{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-      for (int kk = 0; kk < K; kk += 4) {
-        const f32x4 r = ld4(&sm.Kc[tr][kk]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kd += r[i] * ld4(&sm.dh[kk + i][vq]);
-      }
-      st4(&sm.dU[tr][vq], a + sm.gt.EGnG[tr] * kd);
-    }
-    __syncthreads();
-    // dR = Tinv^T dUbar
-    f32x4 r{0.f, 0.f, 0.f, 0.f};
-    for (int t2 = tr; t2 < 64; ++t2) r += sm.Tm[t2][tr] * ld4(&sm.dU[t2][vq]);
-    __syncthreads();
-    st4(&sm.dU[tr][vq], r);
-    __syncthreads();
-    // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR   (keys kp, kp+1; channels vq..vq+3)
-    f32x4 acc0, acc1;
-    if (kact) {
-      const float eGn = sm.gt.EG[63];
-      acc0 = eGn * ld4(&sm.dh[kp][vq]);
-      acc1 = eGn * ld4(&sm.dh[kp + 1][vq]);
-#pragma unroll 4
-      for (int t = 0; t < 64; ++t) {
-        const float q0 = sm.Qt[t][kp], q1 = sm.Qt[t][kp + 1], k0 = sm.Kc[t][kp], k1 = sm.Kc[t][kp + 1];
-        const f32x4 o = sm.gt.EG[t] * ld4(&sm.dO[t][vq]), rr = sm.gt.bEGx[t] * ld4(&sm.dU[t][vq]);
-        acc0 += q0 * o - k0 * rr;
-        acc1 += q1 * o - k1 * rr;
-      }
-    }
-    __syncthreads();
-    if (kact) {
-      st4(&sm.dh[kp][vq], acc0);
-      st4(&sm.dh[kp + 1][vq], acc1);
-    }
-  }
-  __syncthreads();
-  if (ds0) {
-    for (int e = tid; e < K * VT; e += NT) {
-      const int kk = e % K, cc = e / K;
-      ds0[(srow + cc) * K + kk] = sm.dh[kk][cc];
-    }
-  }
-}
+    const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0);
 
 // ---- per-chunk gradients ------------------------------------------------------------------
 
@@ -741,6 +599,165 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
       float s2 = 0.f;
       for (int w = 0; w < NT / 64; ++w) s2 += sm.red[8 + w];
       dd_part[slot * H + h] = s2;
+    }
+  }
+}
+
+// Reverse scan of dh on fp32 matrix-core tiles. Wavefront w owns token block
+// tb = w % 4 and channel block vb = w / 4 of dUbar and dR, and the blocks
+// (KBD (w % 4) + c, vb) of dh.
+template <int K, int V, typename InT>
+__global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
+    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
+    const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
+    const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
+    const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0) {
+  constexpr int NT = 512, VT = kDhVT, NVT = V / VT, KBD = K / 64;
+  constexpr int QPT = 64 * K / NT, OPT = 64 * VT / NT, MPT = 64 * 16 / NT;  // staged elements per thread
+  static_assert(VT == 32, "two 16-channel blocks per workgroup");
+  __shared__ SmemDh<K> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int unit, vt;
+  if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
+  const int h = unit % H, n = unit / H;
+  int b, t0, t1;
+  sequence_range(cu_seqlens, n, T, b, t0, t1);
+  const float dh_ = d[h];
+  const int nch = (t1 - t0 + 63) / 64;
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t srow = (static_cast<int64_t>(n) * H + h) * V + vt * VT;  // state row of channel 0 of the tile
+  const int l16 = lane & 15, l4 = lane >> 4;
+  const int tb = wave & 3, vb = wave >> 2, ta = 16 * tb + l16, vc = 16 * vb + l16;
+
+  // the next chunk's operands, loaded one chunk ahead into registers
+  float rq[QPT], rk[QPT], ro[OPT], ra = 1.f, rb = 0.f;
+  f32x4 rt[MPT], rp[MPT];
+  auto fetch = [&](int ci) {
+    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+    const int64_t mb = (chunk_slot(packed, t0, n, ci, T) * H + h) * 64 * 64;
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = tid + j * NT, row = e / K, cc = e % K;
+      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
+      rq[j] = row < nrows ? ld(q, off) : 0.f;
+      rk[j] = row < nrows ? ld(k, off) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int e = tid + j * NT, row = e / VT, cc = e % VT;
+      ro[j] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + cc) : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < MPT; ++j) {
+      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+      rt[j] = ld4(&Tg[mb + row * 64 + c4]);
+      rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+    }
+    if (tid < 64) {
+      ra = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
+      rb = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
+    }
+  };
+
+  for (int e = tid; e < K * VT; e += NT) {
+    const int kk = e % K, cc = e / K;
+    sm.dh[kk][cc] = dsf ? dsf[(srow + cc) * K + kk] : 0.f;
+  }
+  if (nch > 0) fetch(nch - 1);
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+    const int64_t slot = chunk_slot(packed, t0, n, ci, T);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = tid + j * NT, row = e / K, cc = e % K;
+      sm.Kc[row][cc] = rk[j];
+      sm.Qt[row][cc] = rq[j] - dh_ * rk[j];
+    }
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      const int e = tid + j * NT;
+      sm.dO[e / VT][e % VT] = ro[j];
+    }
+#pragma unroll
+    for (int j = 0; j < MPT; ++j) {
+      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+      st4(&sm.Tm[row][c4], rt[j]);
+      st4(&sm.Pm[row][c4], rp[j]);
+    }
+    if (tid < 64) {
+      sm.gt.raw_a[tid] = ra;
+      sm.gt.raw_b[tid] = rb;
+    }
+    // the gradient of this chunk's outgoing state, for the gradient kernel ([channel][key])
+    {
+      float* dst = dhck + (slot * H + h) * V * K + static_cast<int64_t>(vt) * VT * K;
+      for (int e = tid; e < VT * K / 4; e += NT) {
+        const int cc = e / (K / 4), k4 = 4 * (e % (K / 4));
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = sm.dh[k4 + i][cc];
+        st4(dst + static_cast<int64_t>(cc) * K + k4, x);
+      }
+    }
+    __syncthreads();
+    if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
+    if (wave == 0) chunk_gates(sm.gt, lane, nrows);
+    __syncthreads();
+    // dUbar = P^T dO + diag(e^(Gn - G)) K dh   (block tb, vb); A[t][t'] = P[t'][t]
+    {
+      f32x4 kd{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int j = 0; j < K / 4; ++j) kd = mma4(sm.Kc[ta][4 * j + l4], sm.dh[4 * j + l4][vc], kd);
+      f32x4 du;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) du[i] = sm.gt.EGnG[16 * tb + 4 * l4 + i] * kd[i];
+      for (int j = 4 * tb; j < 16; ++j) du = mma4(sm.Pm[4 * j + l4][ta], sm.dO[4 * j + l4][vc], du);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.dU[16 * tb + 4 * l4 + i][vc] = du[i];
+    }
+    __syncthreads();
+    // dR = Tinv^T dUbar
+    f32x4 dr{0.f, 0.f, 0.f, 0.f};
+    for (int j = 4 * tb; j < 16; ++j) dr = mma4(sm.Tm[4 * j + l4][ta], sm.dU[4 * j + l4][vc], dr);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm.dU[16 * tb + 4 * l4 + i][vc] = dr[i];
+    __syncthreads();
+    // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR   (blocks (KBD tb + c, vb)); A[k][t] = X[t][k]
+    const float eGn = sm.gt.EG[63];
+    f32x4 acc[KBD];
+#pragma unroll
+    for (int cb = 0; cb < KBD; ++cb) {
+      const int kb = KBD * tb + cb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[cb][i] = eGn * sm.dh[16 * kb + 4 * l4 + i][vc];
+    }
+#pragma unroll 4
+    for (int j = 0; j < 16; ++j) {
+      const int tr2 = 4 * j + l4;
+      const float bO = sm.gt.EG[tr2] * sm.dO[tr2][vc], bR = -sm.gt.bEGx[tr2] * sm.dU[tr2][vc];
+#pragma unroll
+      for (int cb = 0; cb < KBD; ++cb) {
+        const int kc = 16 * (KBD * tb + cb) + l16;
+        acc[cb] = mma4(sm.Qt[tr2][kc], bO, acc[cb]);
+        acc[cb] = mma4(sm.Kc[tr2][kc], bR, acc[cb]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int cb = 0; cb < KBD; ++cb) {
+      const int kb = KBD * tb + cb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.dh[16 * kb + 4 * l4 + i][vc] = acc[cb][i];
+    }
+  }
+  __syncthreads();
+  if (ds0) {
+    for (int e = tid; e < K * VT; e += NT) {
+      const int kk = e % K, cc = e / K;
+      ds0[(srow + cc) * K + kk] = sm.dh[kk][cc];
     }
   }
 }
