@@ -318,7 +318,7 @@ __device__ __forceinline__ void invert16(ChunkBuf<K, VT>& bf, const float* Ab, f
 // them: this lane holds row t = 16 R + l16, columns s = 16 C + 4 g + i.
 // B = 0 is the wave's diagonal block; B >= 1 an off-diagonal one whose decay
 // factors are in the wave's tables (slot B - 1).
-template <int B, int R, int C, bool NORM, int K, int VT>
+template <int B, int R, int C, bool NORM, bool SO, int K, int VT>
 __device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps, int lane, float dh,
                                             const f32x4& qk, const f32x4& kk4) {
   const int g = lane >> 4, l16 = lane & 15;
@@ -363,7 +363,7 @@ __device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps
     }
   }
   const int col = perm_col(16 * C + 4 * g);
-  put_split4(bf.Ph, bf.Pl, tp_off(t, col), pv);
+  if constexpr (!SO) put_split4(bf.Ph, bf.Pl, tp_off(t, col), pv);
   if constexpr (B == 0) *reinterpret_cast<f32x4*>(&ps.Aown[l16 * kSS + 4 * g]) = av;
   if constexpr ((R & 1) != 0 && C == R - 1) *reinterpret_cast<f32x4*>(&ps.Aoff[l16 * kSS + 4 * g]) = av;
   if constexpr (R >= 2 && C < 2) put_split4(bf.Th, bf.Tl, tp_off(t, col), -av);  // -A21
@@ -426,7 +426,7 @@ __device__ __forceinline__ void offdiag_inverse(ChunkBuf<K, VT>& bf, const ProdS
 // written as hi / lo bf16. A_DD goes to the wave's scratch for its inverse;
 // A_{R,R-1} (odd R) to the scratch for the off-diagonal step; the A blocks
 // below the 32x32 diagonal enter T's storage negated (-A21).
-template <int D, int NB, int R1, int C1, int R2, int C2, bool NORM, int K, int VT>
+template <int D, int NB, int R1, int C1, int R2, int C2, bool NORM, bool SO, int K, int VT>
 __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, const ProdScratch& prev,
                                                 int* pair_flag, int chunk_tag, int lane, float dh,
                                                 float G, float lg, float rinv, float be, float rk) {
@@ -461,22 +461,24 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
   for (int s = 0; s < K / 32; ++s) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
       const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
       const bf16x8 bk = lds8(&bf.Kc[swz<K>(16 * Cb[b] + l16, 32 * s + 8 * g)]);
-      aqk[b] = mfma16x16x32(bk, aq, aqk[b]);
+      if constexpr (!SO) {  // q k^T only feeds P, which a state-only pass does not form
+        const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
+        aqk[b] = mfma16x16x32(bk, aq, aqk[b]);
+      }
       akk[b] = mfma16x16x32(bk, ak, akk[b]);
     }
   }
-  scale_block<0, D, D, NORM>(bf, ps, lane, dh, aqk[0], akk[0]);
-  if constexpr ((D & 1) != 0) scale_block<1, R1, C1, NORM>(bf, ps, lane, dh, aqk[1], akk[1]);  // A_{D,D-1}
+  scale_block<0, D, D, NORM, SO>(bf, ps, lane, dh, aqk[0], akk[0]);
+  if constexpr ((D & 1) != 0) scale_block<1, R1, C1, NORM, SO>(bf, ps, lane, dh, aqk[1], akk[1]);  // A_{D,D-1}
   // diagonal inverse of this wave's block (reads this wave's own scratch writes)
   invert16(bf, ps.Aown, ps.Town, 16 * D, lane);
   if constexpr ((D & 1) == 0) {
     // T_DD is what the odd neighbour waits for: signal it before the rest.
     pair_signal(pair_flag, chunk_tag, lane);
-    if constexpr (NB > 1) scale_block<1, R1, C1, NORM>(bf, ps, lane, dh, aqk[1], akk[1]);
-    if constexpr (NB > 2) scale_block<2, R2, C2, NORM>(bf, ps, lane, dh, aqk[2], akk[2]);
+    if constexpr (NB > 1) scale_block<1, R1, C1, NORM, SO>(bf, ps, lane, dh, aqk[1], akk[1]);
+    if constexpr (NB > 2) scale_block<2, R2, C2, NORM, SO>(bf, ps, lane, dh, aqk[2], akk[2]);
   } else {
     static_assert(NB == 2 && R1 == D && C1 == D - 1, "odd waves hold (D, D) and (D, D-1)");
     offdiag_inverse<D>(bf, ps, prev, pair_flag, chunk_tag, lane);
@@ -540,7 +542,7 @@ __device__ __forceinline__ float sumsq8(const u32x4& w) {
 
 // ---- kernel -------------------------------------------------------------------------------
 
-template <int K, int V, int VT, typename OutT, bool NORM>
+template <int K, int V, int VT, typename OutT, bool NORM, bool SO>
 __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
@@ -731,10 +733,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         __builtin_amdgcn_s_setprio(2);
         const int tag = it + 1;
         switch (p) {
-          case 0: producer_blocks<0, 3, 3, 0, 3, 1, NORM>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
-          case 1: producer_blocks<1, 2, 1, 0, 0, 0, NORM>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
-          case 2: producer_blocks<2, 3, 2, 0, 2, 1, NORM>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
-          default: producer_blocks<3, 2, 3, 2, 0, 0, NORM>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          case 0: producer_blocks<0, 3, 3, 0, 3, 1, NORM, SO>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          case 1: producer_blocks<1, 2, 1, 0, 0, 0, NORM, SO>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          case 2: producer_blocks<2, 3, 2, 0, 2, 1, NORM, SO>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          default: producer_blocks<3, 2, 3, 2, 0, 0, NORM, SO>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -791,8 +793,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         bf16x8 fk[2], fq[2];
         fk[0] = kfrag(0, 0);
         fk[1] = kfrag(0, 1);
-        fq[0] = qfrag(0, 0);
-        fq[1] = qfrag(0, 1);
+        if constexpr (!SO) {
+          fq[0] = qfrag(0, 0);
+          fq[1] = qfrag(0, 1);
+        }
         f32x4 KH[4], QH[4];
 #pragma unroll
         for (int j = 0; j < NSTEP; ++j) {
@@ -802,8 +806,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
             const int r4n = (j + 1) / (NS / 2), s0n = 2 * ((j + 1) % (NS / 2));
             nk[0] = kfrag(r4n, s0n);
             nk[1] = kfrag(r4n, s0n + 1);
-            nq[0] = qfrag(r4n, s0n);
-            nq[1] = qfrag(r4n, s0n + 1);
+            if constexpr (!SO) {
+              nq[0] = qfrag(r4n, s0n);
+              nq[1] = qfrag(r4n, s0n + 1);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
           if (s0 == 0) {
@@ -814,15 +820,19 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
           for (int u = 0; u < 2; ++u) {
             KH[r4] = mfma16x16x32(fk[u], hbh[s0 + u], KH[r4]);
             KH[r4] = mfma16x16x32(fk[u], hbl[s0 + u], KH[r4]);
-            QH[r4] = mfma16x16x32(fq[u], hbh[s0 + u], QH[r4]);
-            QH[r4] = mfma16x16x32(fq[u], hbl[s0 + u], QH[r4]);
+            if constexpr (!SO) {
+              QH[r4] = mfma16x16x32(fq[u], hbh[s0 + u], QH[r4]);
+              QH[r4] = mfma16x16x32(fq[u], hbl[s0 + u], QH[r4]);
+            }
           }
           __builtin_amdgcn_sched_barrier(0);
           if (j + 1 < NSTEP) {
             fk[0] = nk[0];
             fk[1] = nk[1];
-            fq[0] = nq[0];
-            fq[1] = nq[1];
+            if constexpr (!SO) {
+              fq[0] = nq[0];
+              fq[1] = nq[1];
+            }
           }
         }
 
@@ -863,10 +873,12 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 
         // ---- stage C: Y = R_bot - A21 Ubar_top ; Ubar_bot = T2 Y (P rows 0-31 read meanwhile)
         bf16x8 p0h[2], p0l[2];
+        if constexpr (!SO) {
 #pragma unroll
-        for (int r4 = 0; r4 < 2; ++r4) {
-          p0h[r4] = lds8(&bf.Ph[tp_off(16 * r4 + l16, 8 * g)]);
-          p0l[r4] = lds8(&bf.Pl[tp_off(16 * r4 + l16, 8 * g)]);
+          for (int r4 = 0; r4 < 2; ++r4) {
+            p0h[r4] = lds8(&bf.Ph[tp_off(16 * r4 + l16, 8 * g)]);
+            p0l[r4] = lds8(&bf.Pl[tp_off(16 * r4 + l16, 8 * g)]);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         f32x4 Y[2];
@@ -876,12 +888,14 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         split_pair(Y[0], Y[1], ybh, ybl);
         // P rows 32-63 for stage D
         bf16x8 p1h[2][2], p1l[2][2];
+        if constexpr (!SO) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
+          for (int r = 0; r < 2; ++r) {
 #pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            p1h[r][hf] = lds8(&bf.Ph[tp_off(32 + 16 * r + l16, 32 * hf + 8 * g)]);
-            p1l[r][hf] = lds8(&bf.Pl[tp_off(32 + 16 * r + l16, 32 * hf + 8 * g)]);
+            for (int hf = 0; hf < 2; ++hf) {
+              p1h[r][hf] = lds8(&bf.Ph[tp_off(32 + 16 * r + l16, 32 * hf + 8 * g)]);
+              p1l[r][hf] = lds8(&bf.Pl[tp_off(32 + 16 * r + l16, 32 * hf + 8 * g)]);
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -896,6 +910,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) kt0[s2] = kt_frag<K>(bf.Kc, 0, s2, g, l16);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!SO) {  // a state-only pass forms no output
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 eg = lds_f4(&bf.gl[2][16 * g + 4 * r4]);
@@ -936,6 +951,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
             for (int i = 0; i < 4; ++i)
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i]), orsrc, ovoff[i], 0, 0);
           }
+        }
         }
 
         // ---- stage E: h' = e^Gn h + K^T diag(e^(Gn - G)) Ubar, K^T fragments
@@ -984,11 +1000,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   }
 }
 
-template <int K, int V, typename OutT, bool NORM>
+template <int K, int V, typename OutT, bool NORM, bool SO>
 static hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t st) {
   constexpr int VT = 64, NVT = V / VT;
   const int units = a.N * a.H;
-  chunk_fwd_bf16_kernel<K, V, VT, OutT, NORM><<<xcd_grid(units, NVT), 512, 0, st>>>(
+  chunk_fwd_bf16_kernel<K, V, VT, OutT, NORM, SO><<<xcd_grid(units, NVT), 512, 0, st>>>(
       static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.alpha,
       a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion, a.hck);
   return hipGetLastError();
@@ -996,8 +1012,10 @@ static hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t st) {
 
 template <int K, int V, bool NORM>
 static hipError_t launch_bf16_n(const FwdArgs& a, hipStream_t st) {
-  if (a.out_dtype == COMBA_BF16) return launch_bf16_t<K, V, u16, NORM>(a, st);
-  return launch_bf16_t<K, V, float, NORM>(a, st);
+  // a pass without output (state maps, checkpoints) runs the state-only instantiation
+  if (a.fusion & kModeNoOutput) return launch_bf16_t<K, V, u16, NORM, true>(a, st);
+  if (a.out_dtype == COMBA_BF16) return launch_bf16_t<K, V, u16, NORM, false>(a, st);
+  return launch_bf16_t<K, V, float, NORM, false>(a, st);
 }
 
 template <int K, int V>
