@@ -63,6 +63,113 @@ __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ float hsum(f32x4 x) { return (x[0] + x[1]) + (x[2] + x[3]); }
 
+// ---- row loads through buffer resources ---------------------------------------------------
+// A chunk's rows are read with unconditional 16- or 8-byte buffer loads whose
+// resource ends after the chunk's last valid row: loads past it return zeros,
+// the padding the chunk algebra needs. The loaded words stay raw in registers
+// until they are written to LDS, so a load issued one chunk (or tile) ahead is
+// waited for only there.
+
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Third descriptor word of a raw buffer resource (32-bit data format, no
+// swizzle): with stride 0, a load at or beyond num_records bytes returns zero.
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  T* p = reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), kRsrcWord3);
+}
+
+// Four consecutive elements: 8 bytes of bf16 or 16 bytes of fp32.
+template <typename InT>
+struct Piece4 {
+  typedef typename std::conditional<sizeof(InT) == 2, u32x2, u32x4>::type type;
+};
+
+template <typename InT>
+__device__ __forceinline__ typename Piece4<InT>::type load4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  if constexpr (sizeof(InT) == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+}
+
+// The four floats of a Piece4. Words go through scalar copies: a bit cast of
+// a vector subscript reads element 0 for every index with this compiler.
+__device__ __forceinline__ f32x4 unpack4(const u32x2& w) {
+  const unsigned e0 = w.x, e1 = w.y;
+  return f32x4{__uint_as_float(e0 << 16), __uint_as_float(e0 & 0xffff0000u), __uint_as_float(e1 << 16),
+               __uint_as_float(e1 & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 unpack4(const u32x4& w) {
+  const unsigned e0 = w.x, e1 = w.y, e2 = w.z, e3 = w.w;
+  return f32x4{__uint_as_float(e0), __uint_as_float(e1), __uint_as_float(e2), __uint_as_float(e3)};
+}
+
+__device__ __forceinline__ float to_f32(u16 b) { return bf16_bits_to_float(b); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// The floats of a 16-byte piece: eight bf16 (lo = elements 0-3, hi = 4-7) or
+// four fp32 (lo only).
+template <typename InT>
+__device__ __forceinline__ void unpack16(const u32x4& w, f32x4& lo, f32x4& hi) {
+  if constexpr (sizeof(InT) == 2) {
+    lo = unpack4(u32x2{w.x, w.y});
+    hi = unpack4(u32x2{w.z, w.w});
+  } else {
+    lo = unpack4(w);
+    hi = lo;
+  }
+}
+
+// q and k rows of a chunk, one thread's share: QP 16-byte pieces of each, the
+// piece p = tid + j NT covering row p / (K / EB), columns EB (p % (K / EB)) ..
+template <int K, int NT, typename InT>
+struct RowPieces {
+  static constexpr int EB = 16 / static_cast<int>(sizeof(InT));  // elements per piece
+  static constexpr int QP = 64 * K / EB / NT;
+  static_assert(QP >= 1 && QP * EB * NT == 64 * K, "whole pieces per thread");
+  u32x4 q[QP], k[QP];
+
+  __device__ __forceinline__ void load(const InT* qg, const InT* kg, int64_t tok0, int H, int nrows, int tid) {
+    const int64_t bytes = static_cast<int64_t>(nrows) * H * K * sizeof(InT);
+    const __amdgpu_buffer_rsrc_t qr = rows_rsrc(qg + tok0 * K, bytes), kr = rows_rsrc(kg + tok0 * K, bytes);
+#pragma unroll
+    for (int j = 0; j < QP; ++j) {
+      const int p = tid + j * NT, row = p / (K / EB), col = EB * (p % (K / EB));
+      const int off = (row * H * K + col) * static_cast<int>(sizeof(InT));
+      q[j] = load16(qr, off);
+      k[j] = load16(kr, off);
+    }
+  }
+  // Kc[row][c] = k, Qt[row][c] = q - d k (fp32 rows of stride LD)
+  template <int LD>
+  __device__ __forceinline__ void store(float* Qt, float* Kc, float dh, int tid) const {
+#pragma unroll
+    for (int j = 0; j < QP; ++j) {
+      const int p = tid + j * NT, row = p / (K / EB), col = EB * (p % (K / EB));
+      f32x4 q0, q1, k0, k1;
+      unpack16<InT>(q[j], q0, q1);
+      unpack16<InT>(k[j], k0, k1);
+      st4(Kc + row * LD + col, k0);
+      st4(Qt + row * LD + col, q0 - dh * k0);
+      if constexpr (EB == 8) {
+        st4(Kc + row * LD + col + 4, k1);
+        st4(Qt + row * LD + col + 4, q1 - dh * k1);
+      }
+    }
+  }
+};
+
 // The chunk of a slot (see chunk_slot). Returns false for a slot between packed sequences.
 __device__ __forceinline__ bool slot_chunk(const int32_t* cu_seqlens, int64_t slot, int T, int N, int& n, int& c,
                                            int& b, int& t0, int& t1) {
@@ -84,23 +191,6 @@ __device__ __forceinline__ bool slot_chunk(const int32_t* cu_seqlens, int64_t sl
     sequence_range(cu_seqlens, n, T, b, t0, t1);
   }
   return c >= 0 && t0 + 64 * c < t1;
-}
-
-// q~ = q - d k and k of the chunk's rows (zeros past the end), fp32 rows of stride LD.
-template <int K, int LD, typename InT>
-__device__ __forceinline__ void stage_rows(const InT* q, const InT* k, float* Qt, float* Kc, int64_t tok0, int H,
-                                           int nrows, float dh, int tid, int nt) {
-  for (int e = tid; e < 64 * K; e += nt) {
-    const int row = e / K, c = e % K;
-    float kv = 0.f, qv = 0.f;
-    if (row < nrows) {
-      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + c;
-      kv = ld(k, off);
-      qv = ld(q, off);
-    }
-    Kc[row * LD + c] = kv;
-    Qt[row * LD + c] = qv - dh * kv;
-  }
 }
 
 __device__ __forceinline__ void stage_gates(ChunkGates& gt, const float* alpha, const float* beta, int64_t tok0,
@@ -243,7 +333,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
 // ---- reverse scan of dh --------------------------------------------------------------------
 
 template <int K>
-struct SmemDh {
+struct alignas(16) SmemDh {
   float Qt[64][K + 4];
   float Kc[64][K + 4];
   float Tm[64][kLdT];
@@ -274,7 +364,7 @@ constexpr int kGrVT = 16;  // value channels per tile of the gradient kernel
 constexpr int kLdV = kGrVT + 4;
 
 template <int K>
-struct SmemGrad {
+struct alignas(16) SmemGrad {
   float Qt[64][K + 4];
   float Kc[64][K + 4];
   float Tm[64][kLdT];  // Tinv, then dP (.) M
@@ -330,20 +420,79 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   const float* dhsrc = dhck + (slot * H + h) * V * K;
   const int64_t mb = (slot * H + h) * 64 * 64;
 
-  stage_rows<K, LQ>(q, k, &sm.Qt[0][0], &sm.Kc[0][0], tok0, H, nrows, dh_, tid, NT);
-  for (int e = tid; e < 64 * 16; e += NT) {
-    const int row = e >> 4, c4 = 4 * (e & 15);
-    st4(&sm.Tm[row][c4], ld4(&Tg[mb + row * 64 + c4]));
-    st4(&sm.Pm[row][c4], ld4(&Pg[mb + row * 64 + c4]));
-  }
-  stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
-  __syncthreads();
-  if (wave == 0) chunk_gates(sm.gt, lane, nrows);
-  __syncthreads();
-
   const int l16 = lane & 15, l4 = lane >> 4;
   const int tb = wave & 3, hw = wave >> 2;
   const int ta = 16 * tb + l16;  // token row this lane supplies to A operands
+
+  // Every load of the chunk's operands is issued before the first wait: q and
+  // k rows, Tinv and P, the gates (at a clamped row; chunk_gates replaces rows
+  // past the end), the k_t.k_s entries of the post phase, and the first value
+  // tile (below).
+  constexpr int MPT = 64 * 16 / NT;
+  RowPieces<K, NT, InT> rqk;
+  rqk.load(q, k, tok0, H, nrows, tid);
+  f32x4 rt[MPT], rp[MPT];
+#pragma unroll
+  for (int j = 0; j < MPT; ++j) {
+    const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+    rt[j] = ld4(&Tg[mb + row * 64 + c4]);
+    rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+  }
+  float ga = 1.f, gb = 0.f;
+  if (tid < 64) {
+    const int64_t tok = tok0 + static_cast<int64_t>(min(tid, nrows - 1)) * H;
+    ga = alpha[tok];
+    gb = beta[tok];
+  }
+  float kkv[2][4];  // k_t.k_s of this lane's entries of the blocks (tb, 2 hw + cb)
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kkv[cb][i] = KKg[mb + (16 * tb + 4 * l4 + i) * 64 + 16 * (2 * hw + cb) + l16];
+
+  // Value tiles, loaded one tile ahead: the state and state-gradient rows
+  // (one 16-byte piece each per thread), a four-channel piece of dO (threads
+  // below 256) and, in the hw = 0 waves, v at this lane's rows (clamped; rows
+  // past the end are replaced by zero where used).
+  constexpr int SPC = VT * K / 4;  // state pieces per tile
+  static_assert(SPC <= NT && 64 * VT / 4 <= NT, "at most one piece of each per thread");
+  const int srow_ = tid / (K / 4), scol = 4 * (tid % (K / 4));
+  const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));
+  const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * sizeof(InT));
+  f32x4 pS{}, pdS{};
+  typename Piece4<InT>::type pO{};
+  InT pv[4];
+  auto fetch_tile = [&](int jt) {
+    const int v0 = jt * VT;
+    if (tid < SPC) {
+      pS = ld4(hsrc + static_cast<int64_t>(v0 + srow_) * K + scol);
+      pdS = ld4(dhsrc + static_cast<int64_t>(v0 + srow_) * K + scol);
+    }
+    if (tid < 64 * VT / 4) pO = load4<InT>(orsrc, (orow * H * V + v0 + ocol) * static_cast<int>(sizeof(InT)));
+    if (hw == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = min(16 * tb + 4 * l4 + i, nrows - 1);
+        pv[i] = v[(tok0 + static_cast<int64_t>(t) * H) * V + v0 + l16];
+      }
+    }
+  };
+  fetch_tile(0);
+
+  rqk.template store<LQ>(&sm.Qt[0][0], &sm.Kc[0][0], dh_, tid);
+#pragma unroll
+  for (int j = 0; j < MPT; ++j) {
+    const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+    st4(&sm.Tm[row][c4], rt[j]);
+    st4(&sm.Pm[row][c4], rp[j]);
+  }
+  if (tid < 64) {
+    sm.gt.raw_a[tid] = ga;
+    sm.gt.raw_b[tid] = gb;
+  }
+  __syncthreads();
+  if (wave == 0) chunk_gates(sm.gt, lane, nrows);
+  __syncthreads();
   f32x4 accQ[KBW], accK[KBW], accA[2], accP[2];
 #pragma unroll
   for (int i = 0; i < KBW; ++i) accQ[i] = accK[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -356,18 +505,18 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   for (int jt = 0; jt < NTILE; ++jt) {
     const int v0 = jt * VT;
     __syncthreads();
-    for (int e = tid; e < VT * K / 4; e += NT) {
-      const int row = e / (K / 4), c4 = 4 * (e % (K / 4));
-      const f32x4 hv = ld4(hsrc + static_cast<int64_t>(v0 + row) * K + c4);
-      const f32x4 dv_ = ld4(dhsrc + static_cast<int64_t>(v0 + row) * K + c4);
-      st4(&sm.u.t.S[row][c4], hv);
-      st4(&sm.u.t.dS[row][c4], dv_);
-      shdh += hsum(hv * dv_);
+    if (tid < SPC) {
+      st4(&sm.u.t.S[srow_][scol], pS);
+      st4(&sm.u.t.dS[srow_][scol], pdS);
+      shdh += hsum(pS * pdS);
     }
-    for (int e = tid; e < 64 * VT; e += NT) {
-      const int t = e / VT, cc = e % VT;
-      sm.u.t.dO[t][cc] = t < nrows ? ld(dO, (tok0 + static_cast<int64_t>(t) * H) * V + v0 + cc) : 0.f;
+    if (tid < 64 * VT / 4) st4(&sm.u.t.dO[orow][ocol], unpack4(pO));
+    float vv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (hw == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = 16 * tb + 4 * l4 + i < nrows ? to_f32(pv[i]) : 0.f;
     }
+    if (jt + 1 < NTILE) fetch_tile(jt + 1);  // in flight during this tile's work
     __syncthreads();
     // K h (hw = 0) or K dh (hw = 1) for token block tb; B[k][v] = X[v][k]
     f32x4 kx{0.f, 0.f, 0.f, 0.f};
@@ -376,12 +525,10 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
 #pragma unroll 8
       for (int j = 0; j < K / 4; ++j) kx = mma4(sm.Kc[ta][4 * j + l4], X[l16][4 * j + l4], kx);
     }
-    float vv[4] = {0.f, 0.f, 0.f, 0.f};
     if (hw == 0) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * tb + 4 * l4 + i;
-        vv[i] = t < nrows ? ld(v, (tok0 + static_cast<int64_t>(t) * H) * V + v0 + l16) : 0.f;
         sm.u.t.R[t][l16] = sm.gt.beta[t] * vv[i] - sm.gt.bEGx[t] * kx[i];
       }
     }
@@ -497,7 +644,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
       sm.Pm[t][s_] = dpv * sm.Pm[t][s_];  // dP (.) P
       sm.Tm[t][s_] = dpv * M;             // dP (.) M
       sm.u.p.W[t][s_] = w;
-      sm.u.p.X[t][s_] = w * KKg[mb + t * 64 + s_];
+      sm.u.p.X[t][s_] = w * kkv[cb][i];
     }
   }
   __syncthreads();
@@ -613,8 +760,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
     const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0) {
   constexpr int NT = 512, VT = kDhVT, NVT = V / VT, KBD = K / 64;
-  constexpr int QPT = 64 * K / NT, OPT = 64 * VT / NT, MPT = 64 * 16 / NT;  // staged elements per thread
+  constexpr int MPT = 64 * 16 / NT;  // 16-byte pieces of Tinv and P per thread
   static_assert(VT == 32, "two 16-channel blocks per workgroup");
+  static_assert(64 * VT / 4 == NT, "one four-element piece of dO per thread");
   __shared__ SmemDh<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int unit, vt;
@@ -629,25 +777,22 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
   const int l16 = lane & 15, l4 = lane >> 4;
   const int tb = wave & 3, vb = wave >> 2, ta = 16 * tb + l16, vc = 16 * vb + l16;
 
-  // the next chunk's operands, loaded one chunk ahead into registers
-  float rq[QPT], rk[QPT], ro[OPT], ra = 1.f, rb = 0.f;
+  // The next chunk's operands, loaded one chunk ahead into registers (raw
+  // words; rows past the end of the sequence load as zeros). alpha and beta are
+  // read at a clamped row; chunk_gates replaces the rows past the end.
+  RowPieces<K, NT, InT> rqk;
+  typename Piece4<InT>::type ro;
+  float ra = 1.f, rb = 0.f;
   f32x4 rt[MPT], rp[MPT];
+  const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));  // this thread's piece of dO
   auto fetch = [&](int ci) {
     const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
     const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
     const int64_t mb = (chunk_slot(packed, t0, n, ci, T) * H + h) * 64 * 64;
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int e = tid + j * NT, row = e / K, cc = e % K;
-      const int64_t off = (tok0 + static_cast<int64_t>(row) * H) * K + cc;
-      rq[j] = row < nrows ? ld(q, off) : 0.f;
-      rk[j] = row < nrows ? ld(k, off) : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int e = tid + j * NT, row = e / VT, cc = e % VT;
-      ro[j] = row < nrows ? ld(dO, (tok0 + static_cast<int64_t>(row) * H) * V + vt * VT + cc) : 0.f;
-    }
+    rqk.load(q, k, tok0, H, nrows, tid);
+    const __amdgpu_buffer_rsrc_t orsrc =
+        rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * sizeof(InT));
+    ro = load4<InT>(orsrc, (orow * H * V + vt * VT + ocol) * static_cast<int>(sizeof(InT)));
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
@@ -655,31 +800,36 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
       rp[j] = ld4(&Pg[mb + row * 64 + c4]);
     }
     if (tid < 64) {
-      ra = tid < nrows ? alpha[tok0 + static_cast<int64_t>(tid) * H] : 1.f;
-      rb = tid < nrows ? beta[tok0 + static_cast<int64_t>(tid) * H] : 0.f;
+      const int64_t tok = tok0 + static_cast<int64_t>(min(tid, nrows - 1)) * H;
+      ra = alpha[tok];
+      rb = beta[tok];
     }
   };
 
-  for (int e = tid; e < K * VT; e += NT) {
-    const int kk = e % K, cc = e / K;
-    sm.dh[kk][cc] = dsf ? dsf[(srow + cc) * K + kk] : 0.f;
+  {
+    // dh of the last chunk = dL/dS_final ([channel][key] in memory, [key][channel] here)
+    constexpr int FP = K * VT / 4 / NT;
+    static_assert(FP * 4 * NT == K * VT, "whole pieces per thread");
+    f32x4 x[FP];
+#pragma unroll
+    for (int j = 0; j < FP; ++j) {
+      const int e = tid + j * NT, cc = e / (K / 4), k4 = 4 * (e % (K / 4));
+      x[j] = dsf ? ld4(dsf + (srow + cc) * K + k4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < FP; ++j) {
+      const int e = tid + j * NT, cc = e / (K / 4), k4 = 4 * (e % (K / 4));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.dh[k4 + i][cc] = x[j][i];
+    }
   }
   if (nch > 0) fetch(nch - 1);
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
     const int64_t slot = chunk_slot(packed, t0, n, ci, T);
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int e = tid + j * NT, row = e / K, cc = e % K;
-      sm.Kc[row][cc] = rk[j];
-      sm.Qt[row][cc] = rq[j] - dh_ * rk[j];
-    }
-#pragma unroll
-    for (int j = 0; j < OPT; ++j) {
-      const int e = tid + j * NT;
-      sm.dO[e / VT][e % VT] = ro[j];
-    }
+    rqk.template store<K + 4>(&sm.Qt[0][0], &sm.Kc[0][0], dh_, tid);
+    st4(&sm.dO[orow][ocol], unpack4(ro));
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
