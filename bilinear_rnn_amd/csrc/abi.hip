@@ -323,7 +323,7 @@ COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const 
 namespace {
 
 struct BwdWorkspace {
-  size_t hck, dhck, tm, pm, kk, dd, total;
+  size_t hck, dhck, tm, pm, kk, gt, dd, total;
 };
 
 BwdWorkspace bwd_workspace(int64_t nslots, int32_t H, int32_t K, int32_t V) {
@@ -335,7 +335,8 @@ BwdWorkspace bwd_workspace(int64_t nslots, int32_t H, int32_t K, int32_t V) {
   w.tm = 2 * state;
   w.pm = w.tm + mat;
   w.kk = w.pm + mat;
-  w.dd = w.kk + mat;
+  w.gt = w.kk + mat;
+  w.dd = w.gt + align_up(static_cast<size_t>(nslots) * H * 7 * 64 * 4);
   w.total = w.dd + align_up(static_cast<size_t>(nslots) * H * 4);
   return w;
 }
@@ -383,7 +384,8 @@ COMBA_API int32_t comba_chunk_bwd(const void* q, const void* k, const void* v, c
   comba::BwdArgs g{q, k, v, alpha, beta, d, d_o, cu_seqlens, a.N, a.B, a.T, H, K, V, in_dtype, d_final_state,
                    hck, reinterpret_cast<float*>(ws + w.dhck), reinterpret_cast<float*>(ws + w.dd),
                    reinterpret_cast<float*>(ws + w.tm), reinterpret_cast<float*>(ws + w.pm),
-                   reinterpret_cast<float*>(ws + w.kk), dq, dk, dv, dalpha, dbeta, dd, d_initial_state};
+                   reinterpret_cast<float*>(ws + w.kk), reinterpret_cast<float*>(ws + w.gt), dq, dk, dv, dalpha,
+                   dbeta, dd, d_initial_state};
   return launched(comba::launch_chunk_bwd(g, st));
 }
 

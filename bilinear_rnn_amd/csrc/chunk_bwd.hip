@@ -27,7 +27,8 @@
 // Launches after a forward pass that stores every chunk's incoming state (the
 // chunk kernels' checkpoint option):
 //   chunk_bwd_prep_kernel  one workgroup per (chunk, head), all chunks at once:
-//                          Tinv, P and k_t.k_s of the chunk, stored;
+//                          Tinv, P, k_t.k_s and the decay gates of the chunk,
+//                          stored;
 //   chunk_bwd_dh_kernel    reverse scan over chunks, one workgroup per
 //                          (sequence, head, 32 value channels), next chunk
 //                          prefetched into registers: stores each
@@ -42,6 +43,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstddef>
 #include <type_traits>
 
 #include "chunk_common.h"
@@ -52,6 +54,10 @@ namespace comba {
 namespace {
 
 constexpr int kDhVT = 32;  // value channels per workgroup of the reverse scan
+// Stored gates of a chunk: the first seven rows of ChunkGates (G, Gx, beta,
+// bEGx, EG, EGnG, alpha with 1 on padded rows), read back as one block.
+constexpr int kGateWords = 7 * 64;
+static_assert(offsetof(ChunkGates, raw_a) == 6 * 64 * sizeof(float), "gate rows in order");
 constexpr int kLdT = 68;   // row stride of 64-wide fp32 tiles (16-byte aligned rows)
 
 template <typename InT>
@@ -204,7 +210,7 @@ __device__ __forceinline__ void stage_gates(ChunkGates& gt, const float* alpha, 
 // ---- prep: Tinv, P and k_t.k_s of every chunk -------------------------------------------
 
 template <int K>
-struct SmemPrepValu {
+struct alignas(16) SmemPrepValu {
   float QtT[K][kLdT];  // q~ transposed: [key channel][token]
   float KT[K][kLdT];
   float Am[64 * kLdF];
@@ -213,7 +219,7 @@ struct SmemPrepValu {
   ChunkGates gt;
 };
 
-struct SmemPrepMfma {
+struct alignas(16) SmemPrepMfma {
   float Am[64 * kLdF];
   float Tm[64 * kLdF];
   float Ys[768];
@@ -232,7 +238,8 @@ template <int K, typename InT>
 __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ d, const int32_t* __restrict__ cu_seqlens, int T,
-    int H, int N, int64_t nslots, float* __restrict__ Tg, float* __restrict__ Pg, float* __restrict__ KKg) {
+    int H, int N, int64_t nslots, float* __restrict__ Tg, float* __restrict__ Pg, float* __restrict__ KKg,
+    float* __restrict__ Gg) {
   constexpr int NT = 256;
   constexpr bool kMfma = sizeof(InT) == 2;  // bf16 q / k: exact matrix-core operands
   using Smem = typename std::conditional<kMfma, SmemPrepMfma, SmemPrepValu<K>>::type;
@@ -264,6 +271,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
   __syncthreads();
   if (wave == 0) chunk_gates(sm.gt, lane, nrows);
   __syncthreads();
+  // the gates, for the scan and the gradient kernel
+  if (tid < kGateWords / 4) st4(Gg + (slot * H + h) * kGateWords + 4 * tid, ld4(&sm.gt.G[0] + 4 * tid));
   if constexpr (kMfma) {
     // wavefront w: token rows 16 w .. 16 w + 15 against all 64 columns. Lane l
     // supplies row (l % 16) of a block and the 8 keys 32 j + 8 (l / 16) + 0..7
@@ -340,16 +349,17 @@ struct alignas(16) SmemDh {
   float Pm[64][kLdT];
   float dh[K][kDhVT + 4];
   float dO[64][kDhVT + 4];
-  float dU[64][kDhVT + 4];  // dUbar, then dR
+  float dU[64][kDhVT + 4];  // dUbar
+  float dR[64][kDhVT + 4];
   ChunkGates gt;
 };
 
 template <int K, int V, typename InT>
 __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
+    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ d, const InT* __restrict__ dO,
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
-    const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0);
+    const float* __restrict__ Pg, const float* __restrict__ Gg, const float* __restrict__ dsf,
+    float* __restrict__ dhck, float* __restrict__ ds0);
 
 // ---- per-chunk gradients ------------------------------------------------------------------
 
@@ -396,15 +406,16 @@ struct alignas(16) SmemGrad {
 // accumulates its blocks of dO h^T, Ubar dh^T, dR h^T, dR Ubar^T, dO Ubar^T.
 template <int K, int V, typename InT>
 __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
+    const InT* __restrict__ q, const InT* __restrict__ k, const InT* __restrict__ v, const float* __restrict__ d,
     const InT* __restrict__ dO, const int32_t* __restrict__ cu_seqlens, int T, int H, int N, int64_t nslots,
     const float* __restrict__ hck, const float* __restrict__ dhck, const float* __restrict__ Tg,
-    const float* __restrict__ Pg, const float* __restrict__ KKg, float* __restrict__ dq, float* __restrict__ dk,
+    const float* __restrict__ Pg, const float* __restrict__ KKg, const float* __restrict__ Gg,
+    float* __restrict__ dq, float* __restrict__ dk,
     float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta, float* __restrict__ dd_part) {
   constexpr int NT = 512, VT = kGrVT, NTILE = V / VT, LQ = K + 4, KB = K / 16, KBW = KB / 2;
   __shared__ SmemGrad<K> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x % H;
   const int64_t slot = blockIdx.x / H;
   if (slot >= nslots) return;
@@ -425,9 +436,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   const int ta = 16 * tb + l16;  // token row this lane supplies to A operands
 
   // Every load of the chunk's operands is issued before the first wait: q and
-  // k rows, Tinv and P, the gates (at a clamped row; chunk_gates replaces rows
-  // past the end), the k_t.k_s entries of the post phase, and the first value
-  // tile (below).
+  // k rows, Tinv and P, the gates the prep kernel stored, the k_t.k_s entries
+  // of the post phase, and the first value tile (below).
   constexpr int MPT = 64 * 16 / NT;
   RowPieces<K, NT, InT> rqk;
   rqk.load(q, k, tok0, H, nrows, tid);
@@ -438,12 +448,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     rt[j] = ld4(&Tg[mb + row * 64 + c4]);
     rp[j] = ld4(&Pg[mb + row * 64 + c4]);
   }
-  float ga = 1.f, gb = 0.f;
-  if (tid < 64) {
-    const int64_t tok = tok0 + static_cast<int64_t>(min(tid, nrows - 1)) * H;
-    ga = alpha[tok];
-    gb = beta[tok];
-  }
+  f32x4 rg{};
+  if (tid < kGateWords / 4) rg = ld4(Gg + (slot * H + h) * kGateWords + 4 * tid);
   float kkv[2][4];  // k_t.k_s of this lane's entries of the blocks (tb, 2 hw + cb)
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb)
@@ -486,12 +492,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     st4(&sm.Tm[row][c4], rt[j]);
     st4(&sm.Pm[row][c4], rp[j]);
   }
-  if (tid < 64) {
-    sm.gt.raw_a[tid] = ga;
-    sm.gt.raw_b[tid] = gb;
-  }
-  __syncthreads();
-  if (wave == 0) chunk_gates(sm.gt, lane, nrows);
+  if (tid < kGateWords / 4) st4(&sm.gt.G[0] + 4 * tid, rg);
   __syncthreads();
   f32x4 accQ[KBW], accK[KBW], accA[2], accP[2];
 #pragma unroll
@@ -750,21 +751,24 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   }
 }
 
-// Reverse scan of dh on fp32 matrix-core tiles. Wavefront w owns token block
-// tb = w % 4 and channel block vb = w / 4 of dUbar and dR, and the blocks
-// (KBD (w % 4) + c, vb) of dh.
+// Reverse scan of dh on fp32 matrix-core tiles. Wavefront w owns channel
+// block vb = w / 4 and token block tb of dUbar and dR, and the blocks
+// (KBD tb + c, vb) of dh, with tb = w % 4 for vb = 0 and 3 - w % 4 for vb = 1:
+// the two wavefronts of a SIMD (w and w + 4) then hold triangle rows of
+// complementary length, 16 - 4 tb blocks each for P^T dO and Tinv^T dUbar.
 template <int K, int V, typename InT>
 __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
-    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
-    const float* __restrict__ beta, const float* __restrict__ d, const InT* __restrict__ dO,
+    const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ d, const InT* __restrict__ dO,
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
-    const float* __restrict__ Pg, const float* __restrict__ dsf, float* __restrict__ dhck, float* __restrict__ ds0) {
+    const float* __restrict__ Pg, const float* __restrict__ Gg, const float* __restrict__ dsf,
+    float* __restrict__ dhck, float* __restrict__ ds0) {
   constexpr int NT = 512, VT = kDhVT, NVT = V / VT, KBD = K / 64;
   constexpr int MPT = 64 * 16 / NT;  // 16-byte pieces of Tinv and P per thread
   static_assert(VT == 32, "two 16-channel blocks per workgroup");
   static_assert(64 * VT / 4 == NT, "one four-element piece of dO per thread");
   __shared__ SmemDh<K> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int unit, vt;
   if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
   const int h = unit % H, n = unit / H;
@@ -775,14 +779,15 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
   const bool packed = cu_seqlens != nullptr;
   const int64_t srow = (static_cast<int64_t>(n) * H + h) * V + vt * VT;  // state row of channel 0 of the tile
   const int l16 = lane & 15, l4 = lane >> 4;
-  const int tb = wave & 3, vb = wave >> 2, ta = 16 * tb + l16, vc = 16 * vb + l16;
+  const int vb = wave >> 2, tb = vb == 0 ? (wave & 3) : 3 - (wave & 3);
+  const int ta = 16 * tb + l16, vc = 16 * vb + l16;
 
   // The next chunk's operands, loaded one chunk ahead into registers (raw
-  // words; rows past the end of the sequence load as zeros). alpha and beta are
-  // read at a clamped row; chunk_gates replaces the rows past the end.
+  // words; rows past the end of the sequence load as zeros), and its gates as
+  // the prep kernel stored them.
   RowPieces<K, NT, InT> rqk;
   typename Piece4<InT>::type ro;
-  float ra = 1.f, rb = 0.f;
+  f32x4 rg{};
   f32x4 rt[MPT], rp[MPT];
   const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));  // this thread's piece of dO
   auto fetch = [&](int ci) {
@@ -799,11 +804,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
       rt[j] = ld4(&Tg[mb + row * 64 + c4]);
       rp[j] = ld4(&Pg[mb + row * 64 + c4]);
     }
-    if (tid < 64) {
-      const int64_t tok = tok0 + static_cast<int64_t>(min(tid, nrows - 1)) * H;
-      ra = alpha[tok];
-      rb = beta[tok];
-    }
+    if (tid < kGateWords / 4) rg = ld4(Gg + (chunk_slot(packed, t0, n, ci, T) * H + h) * kGateWords + 4 * tid);
   };
 
   {
@@ -825,7 +826,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
   }
   if (nch > 0) fetch(nch - 1);
   for (int ci = nch - 1; ci >= 0; --ci) {
-    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
     const int64_t slot = chunk_slot(packed, t0, n, ci, T);
     __syncthreads();
     rqk.template store<K + 4>(&sm.Qt[0][0], &sm.Kc[0][0], dh_, tid);
@@ -836,10 +836,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
       st4(&sm.Tm[row][c4], rt[j]);
       st4(&sm.Pm[row][c4], rp[j]);
     }
-    if (tid < 64) {
-      sm.gt.raw_a[tid] = ra;
-      sm.gt.raw_b[tid] = rb;
-    }
+    if (tid < kGateWords / 4) st4(&sm.gt.G[0] + 4 * tid, rg);
     // the gradient of this chunk's outgoing state, for the gradient kernel ([channel][key])
     {
       float* dst = dhck + (slot * H + h) * V * K + static_cast<int64_t>(vt) * VT * K;
@@ -853,8 +850,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
     }
     __syncthreads();
     if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
-    if (wave == 0) chunk_gates(sm.gt, lane, nrows);
-    __syncthreads();
     // dUbar = P^T dO + diag(e^(Gn - G)) K dh   (block tb, vb); A[t][t'] = P[t'][t]
     {
       f32x4 kd{0.f, 0.f, 0.f, 0.f};
@@ -871,9 +866,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
     // dR = Tinv^T dUbar
     f32x4 dr{0.f, 0.f, 0.f, 0.f};
     for (int j = 4 * tb; j < 16; ++j) dr = mma4(sm.Tm[4 * j + l4][ta], sm.dU[4 * j + l4][vc], dr);
-    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sm.dU[16 * tb + 4 * l4 + i][vc] = dr[i];
+    for (int i = 0; i < 4; ++i) sm.dR[16 * tb + 4 * l4 + i][vc] = dr[i];
     __syncthreads();
     // dh_in = e^Gn dh + Qt^T diag(e^G) dO - K^T diag(b1) dR   (blocks (KBD tb + c, vb)); A[k][t] = X[t][k]
     const float eGn = sm.gt.EG[63];
@@ -887,7 +881,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
 #pragma unroll 4
     for (int j = 0; j < 16; ++j) {
       const int tr2 = 4 * j + l4;
-      const float bO = sm.gt.EG[tr2] * sm.dO[tr2][vc], bR = -sm.gt.bEGx[tr2] * sm.dU[tr2][vc];
+      const float bO = sm.gt.EG[tr2] * sm.dO[tr2][vc], bR = -sm.gt.bEGx[tr2] * sm.dR[tr2][vc];
 #pragma unroll
       for (int cb = 0; cb < KBD; ++cb) {
         const int kc = 16 * (KBD * tb + cb) + l16;
@@ -931,17 +925,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   const unsigned grid = static_cast<unsigned>(nslots * a.H);
   chunk_bwd_prep_kernel<K, InT><<<grid, 256, 0, st>>>(
       static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.alpha, a.beta, a.d, a.cu_seqlens, a.T, a.H, a.N,
-      nslots, a.Tg, a.Pg, a.KKg);
+      nslots, a.Tg, a.Pg, a.KKg, a.Gg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 512, 0, st>>>(
-      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.alpha, a.beta, a.d,
-      static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.dsf, a.dhck, a.ds0);
+      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.d, static_cast<const InT*>(a.dO),
+      a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.Gg, a.dsf, a.dhck, a.ds0);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   chunk_bwd_grad_kernel<K, V, InT><<<grid, 512, 0, st>>>(
-      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v), a.alpha, a.beta,
-      a.d, static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg,
+      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v), a.d,
+      static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg, a.Gg,
       a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dd_part);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -59,6 +59,7 @@ struct BwdArgs {
   float* Tg;                  // per chunk and head: Tinv, P and k_t.k_s, fp32 64 x 64 each
   float* Pg;
   float* KKg;
+  float* Gg;                  // per chunk and head: the chunk's decay gates, fp32 7 x 64 (see ChunkGates)
   float* dq;                  // [B, T, H, K] fp32
   float* dk;
   float* dv;                  // [B, T, H, V] fp32

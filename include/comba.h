@@ -266,8 +266,9 @@ int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const void* v,
  * forms each chunk's inverse and score matrices, then runs a reverse scan over
  * the chunks and a chunk-parallel gradient pass. It needs a device workspace
  * of at least comba_chunk_bwd_workspace_size(B, T, H, K, V, num_seqs) bytes
- * (per chunk and head two fp32 states and three fp32 64 x 64 matrices: about
- * 1.4 GiB for B = 8, T = 4096, H = 16, K = V = 128), 256-byte aligned.
+ * (per chunk and head two fp32 states, three fp32 64 x 64 matrices and the
+ * chunk's decay gates: about 1.4 GiB for B = 8, T = 4096, H = 16,
+ * K = V = 128), 256-byte aligned.
  * Errors: as comba_chunk_fwd, COMBA_ERR_INVALID_ARG for a NULL d_o or
  * gradient output, COMBA_ERR_WORKSPACE for a short workspace.
  */

@@ -188,12 +188,14 @@ def test_backward_rejects_bad_arguments(kw, code):
 
 def test_backward_workspace_size():
     ws = comba.bwd_workspace_size
-    # per chunk and head: two fp32 states, three fp32 64 x 64 matrices, one float
+    # per chunk and head: two fp32 states, three fp32 64 x 64 matrices, seven
+    # rows of 64 gate values, one float
     pairs = 8 * 64 * 16
-    assert ws(8, 4096, 16, 128, 128) == pairs * (2 * 128 * 128 * 4 + 3 * 64 * 64 * 4 + 4)
+    assert ws(8, 4096, 16, 128, 128) == pairs * (2 * 128 * 128 * 4 + 3 * 64 * 64 * 4 + 7 * 64 * 4 + 4)
     # packed: T / 64 + N + 1 slots
     pairs = (1000 // 64 + 5 + 1) * 2
-    assert ws(1, 1000, 2, 64, 64, 5) == pairs * (2 * 64 * 64 * 4 + 3 * 64 * 64 * 4) + ((pairs * 4 + 255) // 256) * 256
+    assert ws(1, 1000, 2, 64, 64, 5) == (pairs * (2 * 64 * 64 * 4 + 3 * 64 * 64 * 4 + 7 * 64 * 4)
+                                         + ((pairs * 4 + 255) // 256) * 256)
 
 
 def test_workspace_rules():
