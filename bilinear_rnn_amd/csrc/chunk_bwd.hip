@@ -30,22 +30,25 @@
 //                          Tinv, P, k_t.k_s and the decay gates of the chunk,
 //                          stored;
 //   chunk_bwd_dh_kernel    reverse scan over chunks, one workgroup per
-//                          (sequence, head, 32 value channels), next chunk
+//   (_bf16_kernel)         (sequence, head, 32 value channels), next chunk
 //                          prefetched into registers: stores each
 //                          chunk's outgoing-state gradient dh, writes dS_0;
 //   chunk_bwd_grad_kernel  one workgroup per (chunk, head): every per-token
 //                          gradient and a partial of dd;
 //   dd_reduce_kernel       dd per head, summed over chunks in a fixed order.
-// The scan and the gradient kernel form their products on the fp32 matrix
-// cores (16 x 16 x 4 tiles, exact fp32 operands read from row-major LDS
-// buffers; a transposed operand only swaps the fragment's indices). The prep
-// kernel uses bf16 matrix cores for bf16 inputs and the vector units for fp32.
+// The gradient kernel, and the scan for fp32 inputs, form their products on
+// the fp32 matrix cores (16 x 16 x 4 tiles, exact fp32 operands read from
+// row-major LDS buffers; a transposed operand only swaps the fragment's
+// indices). For bf16 inputs the scan runs on the bf16 matrix cores with every
+// fp32 operand split into hi + lo bf16, and the prep kernel forms its scores on
+// them; for fp32 inputs the prep kernel uses the vector units.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <cstddef>
 #include <type_traits>
 
+#include "bf16_tiles.h"
 #include "chunk_common.h"
 #include "launch.h"
 
@@ -76,21 +79,10 @@ __device__ __forceinline__ float hsum(f32x4 x) { return (x[0] + x[1]) + (x[2] + 
 // until they are written to LDS, so a load issued one chunk (or tile) ahead is
 // waited for only there.
 
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// Third descriptor word of a raw buffer resource (32-bit data format, no
-// swizzle): with stride 0, a load at or beyond num_records bytes returns zero.
-constexpr int kRsrcWord3 = 0x00020000;
-
 template <typename T>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const T* base, int64_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  T* p = reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0),
-                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), kRsrcWord3);
+  return __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<T*>(base)), static_cast<short>(0),
+                                           __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), kBufferWord3);
 }
 
 // Four consecutive elements: 8 bytes of bf16 or 16 bytes of fp32.
@@ -155,6 +147,19 @@ struct RowPieces {
       const int off = (row * H * K + col) * static_cast<int>(sizeof(InT));
       q[j] = load16(qr, off);
       k[j] = load16(kr, off);
+    }
+  }
+  // bf16 q and k tiles of K per row (swz<K>), keys of each 32-block in perm32 order
+  __device__ __forceinline__ void store_bf16(u16* Qc, u16* Kc, int tid) const {
+    static_assert(EB == 8, "bf16 pieces");
+#pragma unroll
+    for (int j = 0; j < QP; ++j) {
+      const int p = tid + j * NT, row = p / (K / EB), col = EB * (p % (K / EB));
+      const int p0 = swz<K>(row, perm_col(col)), p1 = swz<K>(row, perm_col(col + 4));
+      *reinterpret_cast<u32x2*>(Qc + p0) = u32x2{q[j].x, q[j].y};
+      *reinterpret_cast<u32x2*>(Qc + p1) = u32x2{q[j].z, q[j].w};
+      *reinterpret_cast<u32x2*>(Kc + p0) = u32x2{k[j].x, k[j].y};
+      *reinterpret_cast<u32x2*>(Kc + p1) = u32x2{k[j].z, k[j].w};
     }
   }
   // Kc[row][c] = k, Qt[row][c] = q - d k (fp32 rows of stride LD)
@@ -906,6 +911,178 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
   }
 }
 
+// ---- reverse scan of dh on bf16 matrix cores (bf16 q, k, dO) ----------------------------
+
+// One chunk of the scan in LDS. Exact bf16 operands: q, k (token rows, keys
+// of each 32-block in perm32 order) and dO (token rows). Split into hi / lo
+// bf16: P and Tinv ([t'][t] as the prep kernel stores them), and the
+// right-hand operands dUbar, X = diag(e^G) dO, Z = -d X - diag(b1) dR and dh,
+// stored by channel with the reduction axis (tokens or keys) in perm32 order.
+template <int K>
+struct alignas(16) SmemDhB {
+  u16 Qc[64 * K], Kc[64 * K];
+  u16 Ph[64 * 64], Pl[64 * 64], Th[64 * 64], Tl[64 * 64];
+  u16 dO[64 * kDhVT];
+  u16 dUh[kDhVT * 64], dUl[kDhVT * 64], Xh[kDhVT * 64], Xl[kDhVT * 64], Zh[kDhVT * 64], Zl[kDhVT * 64];
+  u16 dhh[kDhVT * K], dhl[kDhVT * K];
+  ChunkGates gt;
+};
+
+// Reverse scan of dh for bf16 inputs: the products of chunk_bwd_dh_kernel on
+// 16x16x32 bf16 matrix cores, every fp32 operand split into hi + lo bf16
+// (exact operands enter once). Wavefront w owns channel block cb = w / 4: the
+// token block tb of dUbar and dR (tb = w % 4 for cb = 0, 3 - w % 4 for cb = 1,
+// so that the wavefronts of a SIMD hold triangle rows of complementary length)
+// and the key blocks NBW (w % 4) + c of dh, kept in fp32 registers across the
+// chunks. Per chunk, three barriers after the staging one:
+//   dUbar = diag(e^(Gn - G)) K dh + P^T dO
+//   dR    = Tinv^T dUbar,  X = diag(e^G) dO,  Z = -d X - diag(b1) dR
+//   dh   <- e^Gn dh + q^T X + k^T Z          (q~^T X = q^T X - d k^T X)
+template <int K, int V>
+__global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const float* __restrict__ d, const u16* __restrict__ dO,
+    const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
+    const float* __restrict__ Pg, const float* __restrict__ Gg, const float* __restrict__ dsf,
+    float* __restrict__ dhck, float* __restrict__ ds0) {
+  constexpr int NT = 512, VT = kDhVT, NVT = V / VT, NBW = K / 64;  // dh key blocks per wavefront
+  constexpr int MPT = 64 * 16 / NT;
+  static_assert(VT == 32 && 64 * VT / 4 == NT, "two 16-channel blocks, one dO piece per thread");
+  __shared__ SmemDhB<K> sm;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int unit, vt;
+  if (!unit_of_block(blockIdx.x, NVT, N * H, unit, vt)) return;
+  const int h = unit % H, n = unit / H;
+  int b, t0, t1;
+  sequence_range(cu_seqlens, n, T, b, t0, t1);
+  const float dd_ = d[h];
+  const int nch = (t1 - t0 + 63) / 64;
+  const bool packed = cu_seqlens != nullptr;
+  const int cb = wave >> 2, tb = cb == 0 ? (wave & 3) : 3 - (wave & 3);
+  const int ch = 16 * cb + l16;                                 // this lane's channel in the tile
+  const int64_t crow = (static_cast<int64_t>(n) * H + h) * V + vt * VT + ch;  // its state row
+
+  // dh blocks (keys 16 kb + 4 g + i, channel ch), fp32, from dL/dS_final
+  f32x4 dhr[NBW];
+#pragma unroll
+  for (int c = 0; c < NBW; ++c) {
+    const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
+    dhr[c] = dsf ? ld4(dsf + crow * K + key4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // next chunk's operands, one chunk ahead in registers
+  RowPieces<K, NT, u16> rqk;
+  u32x2 ro;
+  f32x4 rg{};
+  f32x4 rt[MPT], rp[MPT];
+  const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));
+  auto fetch = [&](int ci) {
+    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+    const int64_t sl = chunk_slot(packed, t0, n, ci, T) * H + h;
+    rqk.load(q, k, tok0, H, nrows, tid);
+    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
+    ro = __builtin_amdgcn_raw_buffer_load_b64(orsrc, (orow * H * V + vt * VT + ocol) * 2, 0, 0);
+#pragma unroll
+    for (int j = 0; j < MPT; ++j) {
+      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+      rt[j] = ld4(&Tg[sl * 64 * 64 + row * 64 + c4]);
+      rp[j] = ld4(&Pg[sl * 64 * 64 + row * 64 + c4]);
+    }
+    if (tid < kGateWords / 4) rg = ld4(Gg + sl * kGateWords + 4 * tid);
+  };
+
+  if (nch > 0) fetch(nch - 1);
+  for (int ci = nch - 1; ci >= 0; --ci) {
+    const int64_t slot = chunk_slot(packed, t0, n, ci, T);
+    __syncthreads();
+    rqk.store_bf16(sm.Qc, sm.Kc, tid);
+    *reinterpret_cast<u32x2*>(&sm.dO[swz<VT>(orow, ocol)]) = ro;
+#pragma unroll
+    for (int j = 0; j < MPT; ++j) {
+      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+      put_split4(sm.Th, sm.Tl, swz<64>(row, c4), rt[j]);
+      put_split4(sm.Ph, sm.Pl, swz<64>(row, c4), rp[j]);
+    }
+    if (tid < kGateWords / 4) st4(&sm.gt.G[0] + 4 * tid, rg);
+    // this chunk's outgoing-state gradient: hi / lo for the products, fp32 for
+    // the gradient kernel ([channel][key])
+    float* dst = dhck + ((slot * H + h) * V + vt * VT + ch) * K;
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) {
+      const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
+      put_split4(sm.dhh, sm.dhl, swz<K>(ch, perm_col(key4)), dhr[c]);
+      st4(dst + key4, dhr[c]);
+    }
+    __syncthreads();
+    if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
+
+    // dUbar of block (tb, cb): diag(e^(Gn - G)) K dh, then + P^T dO
+    f32x4 kd{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s_ = 0; s_ < K / 32; ++s_) {
+      const bf16x8 a = lds8(&sm.Kc[swz<K>(16 * tb + l16, 32 * s_ + 8 * g)]);
+      kd = mfma16x16x32(a, lds8(&sm.dhh[swz<K>(ch, 32 * s_ + 8 * g)]), kd);
+      kd = mfma16x16x32(a, lds8(&sm.dhl[swz<K>(ch, 32 * s_ + 8 * g)]), kd);
+    }
+    const f32x4 en = ld4(&sm.gt.EGnG[16 * tb + 4 * g]);
+    f32x4 du = en * kd;
+#pragma unroll
+    for (int s_ = 0; s_ < 2; ++s_) {
+      if (s_ == 0 && tb >= 2) continue;  // P[t'][t] = 0 for t' < t
+      const int pos = 16 * tb + 4 * (l16 & 3);
+      const bf16x8 o = tr_frag<VT>(sm.dO, 32 * s_, 16 * cb + 4 * (l16 & 3), g, l16);
+      du = mfma16x16x32(tr_frag<64>(sm.Ph, 32 * s_, pos, g, l16), o, du);
+      du = mfma16x16x32(tr_frag<64>(sm.Pl, 32 * s_, pos, g, l16), o, du);
+    }
+    put_split4(sm.dUh, sm.dUl, swz<64>(ch, perm_col(16 * tb + 4 * g)), du);
+    __syncthreads();
+
+    // dR = Tinv^T dUbar, then X and Z of block (tb, cb)
+    f32x4 dr{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s_ = 0; s_ < 2; ++s_) {
+      if (s_ == 0 && tb >= 2) continue;  // Tinv[t'][t] = 0 for t' < t
+      const int pos = 16 * tb + 4 * (l16 & 3);
+      dr = mma3(tr_frag<64>(sm.Th, 32 * s_, pos, g, l16), tr_frag<64>(sm.Tl, 32 * s_, pos, g, l16),
+                lds8(&sm.dUh[swz<64>(ch, 32 * s_ + 8 * g)]), lds8(&sm.dUl[swz<64>(ch, 32 * s_ + 8 * g)]), dr);
+    }
+    {
+      const f32x4 eg = ld4(&sm.gt.EG[16 * tb + 4 * g]), b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
+      const f32x4 x = eg * tr4<VT>(sm.dO, 16 * tb, 16 * cb, g, l16);
+      const f32x4 z = -dd_ * x - b1 * dr;
+      const int off = swz<64>(ch, perm_col(16 * tb + 4 * g));
+      put_split4(sm.Xh, sm.Xl, off, x);
+      put_split4(sm.Zh, sm.Zl, off, z);
+    }
+    __syncthreads();
+
+    // dh <- e^Gn dh + q^T X + k^T Z for the wavefront's key blocks
+    const float eGn = sm.gt.EG[63];
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) {
+      const int kb = NBW * (wave & 3) + c;
+      f32x4 acc = eGn * dhr[c];
+#pragma unroll
+      for (int s_ = 0; s_ < 2; ++s_) {
+        const int pos = perm_col(16 * kb + 4 * (l16 & 3));
+        const bf16x8 aq = tr_frag<K>(sm.Qc, 32 * s_, pos, g, l16);
+        const bf16x8 ak = tr_frag<K>(sm.Kc, 32 * s_, pos, g, l16);
+        const int off = swz<64>(ch, 32 * s_ + 8 * g);
+        acc = mfma16x16x32(aq, lds8(&sm.Xh[off]), acc);
+        acc = mfma16x16x32(aq, lds8(&sm.Xl[off]), acc);
+        acc = mfma16x16x32(ak, lds8(&sm.Zh[off]), acc);
+        acc = mfma16x16x32(ak, lds8(&sm.Zl[off]), acc);
+      }
+      dhr[c] = acc;
+    }
+  }
+  if (ds0) {
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) st4(ds0 + crow * K + 16 * (NBW * (wave & 3) + c) + 4 * g, dhr[c]);
+  }
+}
+
 // dd per head: one 64-thread block per head sums the chunks in a fixed order
 // (strided partial sums, then a fixed butterfly).
 __global__ __launch_bounds__(64) void dd_reduce_kernel(const float* __restrict__ dd_part, int64_t nslots, int H,
@@ -928,9 +1105,15 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
       nslots, a.Tg, a.Pg, a.KKg, a.Gg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 512, 0, st>>>(
-      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.d, static_cast<const InT*>(a.dO),
-      a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.Gg, a.dsf, a.dhck, a.ds0);
+  if constexpr (sizeof(InT) == 2) {
+    chunk_bwd_dh_bf16_kernel<K, V><<<xcd_grid(a.N * a.H, V / kDhVT), 512, 0, st>>>(
+        static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), a.d, static_cast<const u16*>(a.dO),
+        a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.Gg, a.dsf, a.dhck, a.ds0);
+  } else {
+    chunk_bwd_dh_kernel<K, V, InT><<<xcd_grid(a.N * a.H, V / kDhVT), 512, 0, st>>>(
+        static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), a.d, static_cast<const InT*>(a.dO),
+        a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.Gg, a.dsf, a.dhck, a.ds0);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   chunk_bwd_grad_kernel<K, V, InT><<<grid, 512, 0, st>>>(

@@ -41,41 +41,15 @@
 // costs about three times as much as a conflict-free 16-byte read. K^T operands
 // for the state update and V for R come from row-major tiles through the
 // transposing LDS read (ds_read_b64_tr_b16).
+#include "bf16_tiles.h"
 #include "chunk_common.h"
 #include "launch.h"
 #include "comba.h"
 
 namespace comba {
 
-typedef short s4 __attribute__((ext_vector_type(4)));
-typedef short s8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s4 lds_s4;
+constexpr int kTP = 32 * 32 + 32 * 64;  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
 
-constexpr int kTP = 32 * 32 + 32 * 64;
-// Third descriptor word of a raw buffer resource on gfx9-family parts
-// (32-bit data format, no swizzle): with stride 0, an access at or beyond
-// num_records bytes is dropped (stores) or returns zero (loads).
-constexpr int kBufferWord3 = 0x00020000;
-
-// A wave-uniform pointer held in scalar registers (the value of lane 0): a
-// buffer resource built from it needs no per-lane waterfall loop.
-template <typename T>
-__device__ __forceinline__ T* uniform_ptr(T* p) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
-  return reinterpret_cast<T*>((static_cast<uint64_t>(hi) << 32) | lo);
-}  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
-
-// Row-major tile of L bf16 per row: 16-byte chunk c of row r is stored at
-// chunk c ^ (r mod L/8). Sixteen consecutive rows then start on sixteen
-// different bank groups (L = 128), so 16-byte fragment reads of 16 rows are
-// free of bank conflicts.
-template <int L>
-__device__ __forceinline__ int swz(int row, int pos) {
-  constexpr int mask = L / 8 - 1;
-  return row * L + (((pos >> 3) ^ (row & mask)) << 3) + (pos & 7);
-}
 __device__ __forceinline__ int tp_off(int row, int pos) {
   // rows 0-31: 32 per row, chunks swizzled by row & 3; rows 32-63: 64 per row
   // after the first 1024, swizzled by row & 7 (arithmetic, no branch)
@@ -130,43 +104,7 @@ struct alignas(16) SmemV3 {
   int pair_flag[2];
 };
 
-__device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 __device__ __forceinline__ f32x4 lds_f4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-// hi / lo bf16 split of two floats, packed: hi = round-to-nearest bf16 pair
-// (one v_cvt_pk_bf16_f32), its exact fp32 values by shift and mask, lo = the
-// rounded remainders (a second conversion). Three VALU instructions per value.
-__device__ __forceinline__ void split2(float x0, float x1, unsigned& hi, unsigned& lo) {
-  const bf16x2 h = __builtin_convertvector((f32x2){x0, x1}, bf16x2);
-  hi = __builtin_bit_cast(unsigned, h);
-  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
-  const bf16x2 l = __builtin_convertvector((f32x2){x0 - h0, x1 - h1}, bf16x2);
-  lo = __builtin_bit_cast(unsigned, l);
-}
-
-// Eight values (m0 then m1) as an MFMA operand pair.
-__device__ __forceinline__ void split_pair(const f32x4& m0, const f32x4& m1, bf16x8& hi, bf16x8& lo) {
-  unsigned h0, h1, h2, h3, l0, l1, l2, l3;
-  split2(m0[0], m0[1], h0, l0);
-  split2(m0[2], m0[3], h1, l1);
-  split2(m1[0], m1[1], h2, l2);
-  split2(m1[2], m1[3], h3, l3);
-  hi = __builtin_bit_cast(bf16x8, (u32x4){h0, h1, h2, h3});
-  lo = __builtin_bit_cast(bf16x8, (u32x4){l0, l1, l2, l3});
-}
-
-__device__ __forceinline__ void split4(const f32x4& x, s4& hi, s4& lo) {
-  unsigned h0, h1, l0, l1;
-  split2(x[0], x[1], h0, l0);
-  split2(x[2], x[3], h1, l1);
-  hi = __builtin_bit_cast(s4, (u32x2){h0, h1});
-  lo = __builtin_bit_cast(s4, (u32x2){l0, l1});
-}
 
 // 2^x with the hardware instruction (about 1 ulp; x <= 0 here, underflow to 0 is exact enough).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -188,24 +126,6 @@ __device__ __forceinline__ void put_split(u16* hi, u16* lo, int off, float x) {
   split_bf16(x, a, b);
   hi[off] = __builtin_bit_cast(u16, a);
   lo[off] = __builtin_bit_cast(u16, b);
-}
-
-// Split four fp32 values into hi / lo bf16 and write them as two 8-byte stores.
-__device__ __forceinline__ void put_split4(u16* hi, u16* lo, int off, const f32x4& x) {
-  unsigned h0, h1, l0, l1;
-  split2(x[0], x[1], h0, l0);
-  split2(x[2], x[3], h1, l1);
-  *reinterpret_cast<u32x2*>(hi + off) = (u32x2){h0, h1};
-  *reinterpret_cast<u32x2*>(lo + off) = (u32x2){l0, l1};
-}
-
-// hi + lo * (a*b + c) style triple product accumulate with both operands split.
-__device__ __forceinline__ f32x4 mma3(const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl,
-                                      f32x4 acc) {
-  acc = mfma16x16x32(ah, bh, acc);
-  acc = mfma16x16x32(ah, bl, acc);
-  acc = mfma16x16x32(al, bh, acc);
-  return acc;
 }
 
 // Producer-only barrier (4 wavefronts) through a monotonically increasing LDS counter.
