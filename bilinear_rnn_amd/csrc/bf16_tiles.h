@@ -122,12 +122,13 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16* tile, int row32, int pos, i
   return __builtin_bit_cast(bf16x8, both);
 }
 
-// Four values in accumulator order: tile[row16 + 4 g + i][col0 + l16], i = 0..3,
-// from a row-major tile of L bf16 per row (natural column order), as floats.
+// Four values in accumulator order: the rows row16 + 4 g + i, i = 0..3, of
+// this lane's column of a row-major tile of L bf16 per row, as floats; pos as
+// for tr_frag.
 template <int L>
-__device__ __forceinline__ f32x4 tr4(const u16* tile, int row16, int col0, int g, int l16) {
+__device__ __forceinline__ f32x4 tr4(const u16* tile, int row16, int pos, int g, int l16) {
   const int row = row16 + 4 * g + (l16 >> 2);
-  const s4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile + swz<L>(row, col0 + 4 * (l16 & 3))));
+  const s4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(tile + swz<L>(row, pos)));
   const uint2 w = __builtin_bit_cast(uint2, x);  // whole-vector reinterpretation (see tr_frag)
   return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
                __uint_as_float(w.y & 0xffff0000u)};

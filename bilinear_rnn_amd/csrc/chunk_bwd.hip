@@ -403,6 +403,44 @@ struct alignas(16) SmemGrad {
   float red[16];
 };
 
+// Per-token scalars of a chunk, run by one wavefront (lane = row). vec rows:
+// 1 sum dR.(v - e^Gx K h), 2 sum (K h).dR, 3 sum (K dh).Ubar, 4 / 6 row / column
+// sums of dP (.) P, 5 / 7 row sums of W (.) KK / column sums of beta W (.) KK,
+// 8 + 9 the two halves of (q~ h).dO; red[0..7] partial <h, dh>, red[8..15]
+// partial dd.
+__device__ __forceinline__ void grad_scalars(const ChunkGates& gt, const float (*vec)[64], const float* red, int lane,
+                                             int nrows, int64_t tok0, int H, float* dalpha, float* dbeta,
+                                             float* dd_out) {
+  const int t = lane;
+  float hd = 0.f;
+  for (int w = 0; w < 8; ++w) hd += red[w];
+  const float be = gt.beta[t], b1 = gt.bEGx[t];
+  const float t2 = gt.EGnG[t] * vec[3][t];
+  const float sqh = vec[8][t] + vec[9][t];
+  float dG = gt.EG[t] * sqh + vec[4][t] - vec[6][t] - vec[7][t] - t2;
+  const float dGx = be * vec[5][t] - b1 * vec[2][t];
+  float sum_t2 = t2;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) sum_t2 += __shfl_xor(sum_t2, m, kWave);
+  if (t == 63) dG += gt.EG[63] * hd + sum_t2;  // dGn
+  // reverse inclusive sum of dG + dGx over the chunk
+  const float x = dG + dGx;
+  const float xr = __shfl(x, 63 - t, kWave);
+  const float sr = wave_inclusive_scan(xr, t);
+  const float rev = __shfl(sr, 63 - t, kWave);
+  const float dlog = rev - dGx;
+  if (t < nrows) {
+    const int64_t off = tok0 + static_cast<int64_t>(t) * H;
+    dbeta[off] = vec[5][t] + vec[1][t];
+    dalpha[off] = dlog / gt.raw_a[t];
+  }
+  if (t == 0) {
+    float s2 = 0.f;
+    for (int w = 0; w < 8; ++w) s2 += red[8 + w];
+    *dd_out = s2;
+  }
+}
+
 // Gradients of one (chunk, head). Wavefront w owns token block tb = w % 4
 // (rows 16 tb ..) and, with half hw = w / 4, the 16 x 16 blocks (tb, key
 // block KBW hw + c) of the 64 x K accumulators and (tb, 2 hw + c) of the
@@ -723,37 +761,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   __syncthreads();
   if (lane == 0) sm.red[8 + wave] = ddp;
   __syncthreads();
-  if (wave == 0) {
-    // per-token scalars, lane = row
-    const int t = lane;
-    float hd = 0.f;
-    for (int w = 0; w < NT / 64; ++w) hd += sm.red[w];
-    const float be = sm.gt.beta[t], b1 = sm.gt.bEGx[t];
-    const float t2 = sm.gt.EGnG[t] * sm.vec[3][t];
-    const float sqh = sm.vec[8][t] + sm.vec[9][t];
-    float dG = sm.gt.EG[t] * sqh + sm.vec[4][t] - sm.vec[6][t] - sm.vec[7][t] - t2;
-    const float dGx = be * sm.vec[5][t] - b1 * sm.vec[2][t];
-    float sum_t2 = t2;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) sum_t2 += __shfl_xor(sum_t2, m, kWave);
-    if (t == 63) dG += sm.gt.EG[63] * hd + sum_t2;  // dGn
-    // reverse inclusive sum of dG + dGx over the chunk
-    const float x = dG + dGx;
-    const float xr = __shfl(x, 63 - t, kWave);
-    const float sr = wave_inclusive_scan(xr, t);
-    const float rev = __shfl(sr, 63 - t, kWave);
-    const float dlog = rev - dGx;
-    if (t < nrows) {
-      const int64_t off = tok0 + static_cast<int64_t>(t) * H;
-      dbeta[off] = sm.vec[5][t] + sm.vec[1][t];
-      dalpha[off] = dlog / sm.gt.raw_a[t];
-    }
-    if (t == 0) {
-      float s2 = 0.f;
-      for (int w = 0; w < NT / 64; ++w) s2 += sm.red[8 + w];
-      dd_part[slot * H + h] = s2;
-    }
-  }
+  if (wave == 0) grad_scalars(sm.gt, sm.vec, sm.red, lane, nrows, tok0, H, dalpha, dbeta, dd_part + slot * H + h);
 }
 
 // Reverse scan of dh on fp32 matrix-core tiles. Wavefront w owns channel
@@ -1049,7 +1057,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
     }
     {
       const f32x4 eg = ld4(&sm.gt.EG[16 * tb + 4 * g]), b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
-      const f32x4 x = eg * tr4<VT>(sm.dO, 16 * tb, 16 * cb, g, l16);
+      const f32x4 x = eg * tr4<VT>(sm.dO, 16 * tb, 16 * cb + 4 * (l16 & 3), g, l16);
       const f32x4 z = -dd_ * x - b1 * dr;
       const int off = swz<64>(ch, perm_col(16 * tb + 4 * g));
       put_split4(sm.Xh, sm.Xl, off, x);
@@ -1081,6 +1089,430 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
 #pragma unroll
     for (int c = 0; c < NBW; ++c) st4(ds0 + crow * K + 16 * (NBW * (wave & 3) + c) + 4 * g, dhr[c]);
   }
+}
+
+// ---- per-chunk gradients on bf16 matrix cores (bf16 q, k, v, dO) -------------------------
+
+constexpr int kGbVT = 32;  // value channels per tile of the bf16 gradient kernel
+
+// LDS of the bf16 gradient kernel. Exact bf16: q, k ([token][key], keys in
+// perm32 order), dO ([token][channel], perm32) and v ([token][channel]). Split
+// hi / lo: Tinv and P ([t][s], s in perm32 order), the state and
+// state-gradient tiles ([channel][key], perm32) and R, Ubar, dUbar, dR
+// ([channel][token], perm32); after the value tiles, dP (.) M and beta W as
+// [s][t] (t in perm32 order) and the fp32 products summed by rows and columns.
+template <int K>
+struct alignas(16) SmemGradB {
+  u16 Qc[64 * K], Kc[64 * K];
+  u16 Th[64 * 64], Tl[64 * 64], Ph[64 * 64], Pl[64 * 64];
+  union {
+    struct {
+      u16 hh[kGbVT * K], hl[kGbVT * K], dhh[kGbVT * K], dhl[kGbVT * K];
+      u16 dO[64 * kGbVT], Vt[64 * kGbVT];
+      u16 Rh[kGbVT * 64], Rl[kGbVT * 64], Uh[kGbVT * 64], Ul[kGbVT * 64];
+      u16 dUh[kGbVT * 64], dUl[kGbVT * 64], dRh[kGbVT * 64], dRl[kGbVT * 64];
+    } t;
+    struct {
+      u16 dPMh[64 * 64], dPMl[64 * 64], WBh[64 * 64], WBl[64 * 64];
+      float dPP[64][kLdT];  // dP (.) P
+      float X[64][kLdT];    // W (.) k_t.k_s
+    } p;
+  } u;
+  ChunkGates gt;
+  float vec[10][64];
+  float red[16];
+};
+
+// Gradients of one (chunk, head) for bf16 inputs: the products of
+// chunk_bwd_grad_kernel on 16x16x32 bf16 matrix cores, every fp32 operand
+// split into hi + lo bf16 (exact operands enter once), over value tiles of 32
+// channels. Wavefront w owns token block tb = w % 4 and half hw = w / 4: per
+// tile the hw = 0 wavefronts form K h, R, Ubar and dR of their token block
+// and the hw = 1 wavefronts K dh and dUbar (both channel blocks), then every
+// wavefront accumulates its blocks (tb, KBW hw + c) of dO h^T, Ubar dh^T and
+// dR h^T and (tb, 2 hw + c) of dR Ubar^T and dO Ubar^T. The row scales
+// e^(Gn - G) and b1 of Ubar dh^T and dR h^T apply after the channel sums.
+template <int K, int V>
+__global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, const float* __restrict__ d,
+    const u16* __restrict__ dO, const int32_t* __restrict__ cu_seqlens, int T, int H, int N, int64_t nslots,
+    const float* __restrict__ hck, const float* __restrict__ dhck, const float* __restrict__ Tg,
+    const float* __restrict__ Pg, const float* __restrict__ KKg, const float* __restrict__ Gg,
+    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dalpha,
+    float* __restrict__ dbeta, float* __restrict__ dd_part) {
+  constexpr int NT = 512, VT = kGbVT, NTILE = V / VT, KB = K / 16, KBW = KB / 2;
+  constexpr int HP = VT * K / 4 / NT;  // 16-byte pieces of a state tile per thread
+  constexpr int MPT = 64 * 16 / NT;
+  static_assert(HP >= 1 && HP * 4 * NT == VT * K && 64 * VT / 4 == NT, "whole pieces per thread");
+  __shared__ SmemGradB<K> sm;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = blockIdx.x % H;
+  const int64_t slot = blockIdx.x / H;
+  if (slot >= nslots) return;
+  int n, c, b, t0, t1;
+  if (!slot_chunk(cu_seqlens, slot, T, N, n, c, b, t0, t1)) {
+    if (tid == 0) dd_part[slot * H + h] = 0.f;
+    return;
+  }
+  const int c0 = t0 + 64 * c, nrows = min(64, t1 - c0);
+  const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+  const float dd_ = d[h];
+  const float* hsrc = hck + (slot * H + h) * V * K;
+  const float* dhsrc = dhck + (slot * H + h) * V * K;
+  const int64_t mb = (slot * H + h) * 64 * 64;
+  const int tb = wave & 3, hw = wave >> 2;
+  const int pt = perm_col(16 * tb + 4 * (l16 & 3));  // tile position of this lane's token quad (block tb)
+
+  // every load of the chunk's operands before the first wait
+  RowPieces<K, NT, u16> rqk;
+  rqk.load(q, k, tok0, H, nrows, tid);
+  f32x4 rt[MPT], rp[MPT];
+#pragma unroll
+  for (int j = 0; j < MPT; ++j) {
+    const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+    rt[j] = ld4(&Tg[mb + row * 64 + c4]);
+    rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+  }
+  f32x4 rg{};
+  if (tid < kGateWords / 4) rg = ld4(Gg + (slot * H + h) * kGateWords + 4 * tid);
+  float kkv[2][4];  // k_t.k_s of this lane's entries of the blocks (tb, 2 hw + cc), loaded with the last tile
+  // value tiles, one tile ahead: state rows, state-gradient rows, dO and v pieces
+  const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));
+  const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
+  const __amdgpu_buffer_rsrc_t vrsrc = rows_rsrc(v + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
+  f32x4 pS[HP], pdS[HP];
+  u32x2 pO, pV;
+  auto fetch_tile = [&](int jt) {
+    const int v0 = jt * VT;
+#pragma unroll
+    for (int j = 0; j < HP; ++j) {
+      const int e = tid + j * NT, row = e / (K / 4), k4 = 4 * (e % (K / 4));
+      pS[j] = ld4(hsrc + static_cast<int64_t>(v0 + row) * K + k4);
+      pdS[j] = ld4(dhsrc + static_cast<int64_t>(v0 + row) * K + k4);
+    }
+    const int off = (orow * H * V + v0 + ocol) * 2;
+    pO = __builtin_amdgcn_raw_buffer_load_b64(orsrc, off, 0, 0);
+    pV = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, off, 0, 0);
+  };
+  fetch_tile(0);
+
+  rqk.store_bf16(sm.Qc, sm.Kc, tid);
+#pragma unroll
+  for (int j = 0; j < MPT; ++j) {
+    const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
+    put_split4(sm.Th, sm.Tl, swz<64>(row, perm_col(c4)), rt[j]);
+    put_split4(sm.Ph, sm.Pl, swz<64>(row, perm_col(c4)), rp[j]);
+  }
+  if (tid < kGateWords / 4) st4(&sm.gt.G[0] + 4 * tid, rg);
+
+  f32x4 accQ[KBW], accUd[KBW], accRh[KBW], accA[2], accP[2];
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) accQ[i] = accUd[i] = accRh[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) accA[i] = accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // per-lane sums over channels, for the rows 16 tb + 4 g + i
+  f32x4 sbR{0.f, 0.f, 0.f, 0.f}, sKhdR{0.f, 0.f, 0.f, 0.f}, st2{0.f, 0.f, 0.f, 0.f};
+  float shdh = 0.f;
+
+  for (int jt = 0; jt < NTILE; ++jt) {
+    const int v0 = jt * VT;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < HP; ++j) {
+      const int e = tid + j * NT, row = e / (K / 4), k4 = 4 * (e % (K / 4));
+      put_split4(sm.u.t.hh, sm.u.t.hl, swz<K>(row, perm_col(k4)), pS[j]);
+      put_split4(sm.u.t.dhh, sm.u.t.dhl, swz<K>(row, perm_col(k4)), pdS[j]);
+      shdh += hsum(pS[j] * pdS[j]);
+    }
+    *reinterpret_cast<u32x2*>(&sm.u.t.dO[swz<VT>(orow, perm_col(ocol))]) = pO;
+    *reinterpret_cast<u32x2*>(&sm.u.t.Vt[swz<VT>(orow, ocol)]) = pV;
+    if (jt + 1 < NTILE) {
+      fetch_tile(jt + 1);  // in flight during this tile's work
+    } else {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kkv[cc][i] = KKg[mb + (16 * tb + 4 * g + i) * 64 + 16 * (2 * hw + cc) + l16];
+    }
+    __syncthreads();
+    // Opaque per-tile copies of the lane coordinates: the LDS addresses below
+    // are then formed inside the loop instead of being hoisted out of it,
+    // which exhausts the registers.
+    int olane;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
+    const int g = olane >> 4, l16 = olane & 15;
+    const int pt = perm_col(16 * tb + 4 * (l16 & 3));
+
+    // K h (hw = 0) or K dh (hw = 1) of the blocks (tb, cb), cb = 0, 1
+    f32x4 kx[2];
+    {
+      const u16* xh = hw == 0 ? sm.u.t.hh : sm.u.t.dhh;
+      const u16* xl = hw == 0 ? sm.u.t.hl : sm.u.t.dhl;
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) kx[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s_ = 0; s_ < K / 32; ++s_) {
+        const bf16x8 a = lds8(&sm.Kc[swz<K>(16 * tb + l16, 32 * s_ + 8 * g)]);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+          const int off = swz<K>(16 * cb + l16, 32 * s_ + 8 * g);
+          kx[cb] = mfma16x16x32(a, lds8(xh + off), kx[cb]);
+          kx[cb] = mfma16x16x32(a, lds8(xl + off), kx[cb]);
+        }
+      }
+    }
+    f32x4 vv[2];
+    const f32x4 bt = ld4(&sm.gt.beta[16 * tb + 4 * g]), b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
+    if (hw == 0) {  // R = diag(beta) V - diag(b1) K h
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        vv[cb] = tr4<VT>(sm.u.t.Vt, 16 * tb, 16 * cb + 4 * (l16 & 3), g, l16);
+        put_split4(sm.u.t.Rh, sm.u.t.Rl, swz<64>(16 * cb + l16, perm_col(16 * tb + 4 * g)), bt * vv[cb] - b1 * kx[cb]);
+      }
+    }
+    __syncthreads();
+    if (hw == 0) {  // Ubar = Tinv R (Tinv[t][s] = 0 for s > t)
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 u{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          if (s_ == 1 && tb < 2) continue;
+          const int ao = swz<64>(16 * tb + l16, 32 * s_ + 8 * g), bo = swz<64>(16 * cb + l16, 32 * s_ + 8 * g);
+          u = mma3(lds8(&sm.Th[ao]), lds8(&sm.Tl[ao]), lds8(&sm.u.t.Rh[bo]), lds8(&sm.u.t.Rl[bo]), u);
+        }
+        put_split4(sm.u.t.Uh, sm.u.t.Ul, swz<64>(16 * cb + l16, perm_col(16 * tb + 4 * g)), u);
+      }
+    } else {  // dUbar = diag(e^(Gn - G)) K dh + P^T dO (P[t'][t] = 0 for t' < t)
+      const f32x4 en = ld4(&sm.gt.EGnG[16 * tb + 4 * g]);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 du = en * kx[cb];
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          if (s_ == 0 && tb >= 2) continue;
+          const bf16x8 o = tr_frag<VT>(sm.u.t.dO, 32 * s_, perm_col(16 * cb + 4 * (l16 & 3)), g, l16);
+          du = mfma16x16x32(tr_frag<64>(sm.Ph, 32 * s_, pt, g, l16), o, du);
+          du = mfma16x16x32(tr_frag<64>(sm.Pl, 32 * s_, pt, g, l16), o, du);
+        }
+        put_split4(sm.u.t.dUh, sm.u.t.dUl, swz<64>(16 * cb + l16, perm_col(16 * tb + 4 * g)), du);
+      }
+    }
+    __syncthreads();
+    if (hw == 0) {  // dR = Tinv^T dUbar, dv = beta dR, and the channel sums of dR
+      const f32x4 ex = {expf(sm.gt.Gx[16 * tb + 4 * g]), expf(sm.gt.Gx[16 * tb + 4 * g + 1]),
+                        expf(sm.gt.Gx[16 * tb + 4 * g + 2]), expf(sm.gt.Gx[16 * tb + 4 * g + 3])};
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        f32x4 dr{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          if (s_ == 0 && tb >= 2) continue;
+          const int bo = swz<64>(16 * cb + l16, 32 * s_ + 8 * g);
+          dr = mma3(tr_frag<64>(sm.Th, 32 * s_, pt, g, l16), tr_frag<64>(sm.Tl, 32 * s_, pt, g, l16),
+                    lds8(&sm.u.t.dUh[bo]), lds8(&sm.u.t.dUl[bo]), dr);
+        }
+        put_split4(sm.u.t.dRh, sm.u.t.dRl, swz<64>(16 * cb + l16, perm_col(16 * tb + 4 * g)), dr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * tb + 4 * g + i;
+          if (t < nrows) dv[(tok0 + static_cast<int64_t>(t) * H) * V + v0 + 16 * cb + l16] = bt[i] * dr[i];
+        }
+        sbR += dr * (vv[cb] - ex * kx[cb]);
+        sKhdR += kx[cb] * dr;
+      }
+    } else {  // (K dh) . Ubar over the channels
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int off = swz<64>(16 * cb + l16, perm_col(16 * tb + 4 * g));
+        const f32x4 u = unpack4(*reinterpret_cast<const u32x2*>(&sm.u.t.Uh[off])) +
+                        unpack4(*reinterpret_cast<const u32x2*>(&sm.u.t.Ul[off]));
+        st2 += kx[cb] * u;
+      }
+    }
+    __syncthreads();
+    // accumulators over the tile's 32 channels
+    {
+      const bf16x8 aO = lds8(&sm.u.t.dO[swz<VT>(16 * tb + l16, 8 * g)]);
+      const bf16x8 aUh = tr_frag<64>(sm.u.t.Uh, 0, pt, g, l16), aUl = tr_frag<64>(sm.u.t.Ul, 0, pt, g, l16);
+      const bf16x8 aRh = tr_frag<64>(sm.u.t.dRh, 0, pt, g, l16), aRl = tr_frag<64>(sm.u.t.dRl, 0, pt, g, l16);
+#pragma unroll
+      for (int cc = 0; cc < KBW; ++cc) {
+        const int pk = perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3));
+        const bf16x8 bh = tr_frag<K>(sm.u.t.hh, 0, pk, g, l16), bl = tr_frag<K>(sm.u.t.hl, 0, pk, g, l16);
+        const bf16x8 dh_h = tr_frag<K>(sm.u.t.dhh, 0, pk, g, l16), dh_l = tr_frag<K>(sm.u.t.dhl, 0, pk, g, l16);
+        accQ[cc] = mfma16x16x32(aO, bh, accQ[cc]);
+        accQ[cc] = mfma16x16x32(aO, bl, accQ[cc]);
+        accUd[cc] = mma3(aUh, aUl, dh_h, dh_l, accUd[cc]);
+        accRh[cc] = mma3(aRh, aRl, bh, bl, accRh[cc]);
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        if (2 * hw + cc > tb) continue;  // blocks above the diagonal are masked to zero
+        const int ps = perm_col(16 * (2 * hw + cc) + 4 * (l16 & 3));
+        const bf16x8 uh = tr_frag<64>(sm.u.t.Uh, 0, ps, g, l16), ul = tr_frag<64>(sm.u.t.Ul, 0, ps, g, l16);
+        accA[cc] = mma3(aRh, aRl, uh, ul, accA[cc]);  // dR Ubar^T (dA is its negative)
+        accP[cc] = mfma16x16x32(aO, uh, accP[cc]);
+        accP[cc] = mfma16x16x32(aO, ul, accP[cc]);
+      }
+    }
+  }
+  __syncthreads();
+
+  // channel sums: reduce over the 16 lanes of a row group
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      sbR[i] += __shfl_xor(sbR[i], m, kWave);
+      sKhdR[i] += __shfl_xor(sKhdR[i], m, kWave);
+      st2[i] += __shfl_xor(st2[i], m, kWave);
+    }
+  }
+  if (l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i;
+      if (hw == 0) {
+        sm.vec[1][t] = sbR[i];
+        sm.vec[2][t] = sKhdR[i];
+      } else {
+        sm.vec[3][t] = st2[i];
+      }
+    }
+  }
+  // q~_t . (dO h^T)_t summed over this wave's keys; q~ = q - d k from the bf16 tiles
+  f32x4 kv[KBW];
+  {
+    f32x4 x{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < KBW; ++cc) {
+      const int pk = perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3));
+      kv[cc] = tr4<K>(sm.Kc, 16 * tb, pk, g, l16);
+      x += (tr4<K>(sm.Qc, 16 * tb, pk, g, l16) - dd_ * kv[cc]) * accQ[cc];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) x[i] += __shfl_xor(x[i], m, kWave);
+      if (l16 == 0) sm.vec[8 + hw][16 * tb + 4 * g + i] = x[i];
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) shdh += __shfl_xor(shdh, m, kWave);
+  if (lane == 0) sm.red[wave] = shdh;
+  // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cc)
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+    const int s_ = 16 * (2 * hw + cc) + l16;
+    // P[t][s] from its hi / lo parts (about 16 significant bits)
+    const int ps = perm_col(16 * (2 * hw + cc) + 4 * (l16 & 3));
+    const f32x4 pv = tr4<64>(sm.Ph, 16 * tb, ps, g, l16) + tr4<64>(sm.Pl, 16 * tb, ps, g, l16);
+    f32x4 dpm, wb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i;
+      const float M = s_ <= t ? expf(fminf(sm.gt.G[t] - sm.gt.G[s_], 0.f)) : 0.f;
+      const float E = s_ < t ? expf(fminf(sm.gt.Gx[t] - sm.gt.G[s_], 0.f)) : 0.f;
+      const float dpv = s_ <= t ? accP[cc][i] : 0.f, dav = s_ < t ? -accA[cc][i] : 0.f;
+      const float w = dav * E;
+      sm.u.p.dPP[t][s_] = dpv * pv[i];
+      sm.u.p.X[t][s_] = w * kkv[cc][i];
+      dpm[i] = dpv * M;
+      wb[i] = sm.gt.beta[t] * w;
+    }
+    const int off = swz<64>(s_, perm_col(16 * tb + 4 * g));
+    put_split4(sm.u.p.dPMh, sm.u.p.dPMl, off, dpm);
+    put_split4(sm.u.p.WBh, sm.u.p.WBl, off, wb);
+  }
+  __syncthreads();
+  // row and column sums (fixed order)
+  if (tid < 64) {
+    float rp = 0.f, rx = 0.f;
+    for (int s_ = 0; s_ < 64; ++s_) {
+      rp += sm.u.p.dPP[tid][s_];
+      rx += sm.u.p.X[tid][s_];
+    }
+    sm.vec[4][tid] = rp;
+    sm.vec[5][tid] = rx;
+  } else if (tid < 128) {
+    const int s_ = tid - 64;
+    float cp = 0.f, cx = 0.f;
+    for (int t = 0; t < 64; ++t) {
+      cp += sm.u.p.dPP[t][s_];
+      cx += sm.gt.beta[t] * sm.u.p.X[t][s_];
+    }
+    sm.vec[6][s_] = cp;
+    sm.vec[7][s_] = cx;
+  }
+  // dq, dk of the blocks (tb, KBW hw + cc):
+  //   dq = diag(e^G) dO h^T + (dP (.) M) K
+  //   dk = diag(e^(Gn - G)) Ubar dh^T - diag(b1) dR h^T + diag(beta) W K + (dP (.) M)^T q
+  //        + W^T diag(beta) K - d (dP (.) M)^T k - d dq
+  const f32x4 eg = ld4(&sm.gt.EG[16 * tb + 4 * g]), en = ld4(&sm.gt.EGnG[16 * tb + 4 * g]);
+  const f32x4 b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
+  f32x4 xq[KBW], xk[KBW], xd[KBW];
+#pragma unroll
+  for (int cc = 0; cc < KBW; ++cc) {
+    xq[cc] = eg * accQ[cc];
+    xk[cc] = en * accUd[cc] - b1 * accRh[cc];
+    xd[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s_ = 0; s_ < 2; ++s_) {
+    if (s_ == 1 && tb < 2) continue;  // columns s <= t
+    const bf16x8 mh = tr_frag<64>(sm.u.p.dPMh, 32 * s_, pt, g, l16), ml = tr_frag<64>(sm.u.p.dPMl, 32 * s_, pt, g, l16);
+    const bf16x8 wh = tr_frag<64>(sm.u.p.WBh, 32 * s_, pt, g, l16), wl = tr_frag<64>(sm.u.p.WBl, 32 * s_, pt, g, l16);
+#pragma unroll
+    for (int cc = 0; cc < KBW; ++cc) {
+      const bf16x8 bk = tr_frag<K>(sm.Kc, 32 * s_, perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3)), g, l16);
+      xq[cc] = mfma16x16x32(mh, bk, xq[cc]);
+      xq[cc] = mfma16x16x32(ml, bk, xq[cc]);
+      xk[cc] = mfma16x16x32(wh, bk, xk[cc]);
+      xk[cc] = mfma16x16x32(wl, bk, xk[cc]);
+    }
+  }
+#pragma unroll
+  for (int s_ = 0; s_ < 2; ++s_) {
+    if (s_ == 0 && tb >= 2) continue;  // rows t' >= t
+    const int ao = swz<64>(16 * tb + l16, 32 * s_ + 8 * g);
+    const bf16x8 mh = lds8(&sm.u.p.dPMh[ao]), ml = lds8(&sm.u.p.dPMl[ao]);
+    const bf16x8 wh = lds8(&sm.u.p.WBh[ao]), wl = lds8(&sm.u.p.WBl[ao]);
+#pragma unroll
+    for (int cc = 0; cc < KBW; ++cc) {
+      const int pk = perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3));
+      const bf16x8 bq = tr_frag<K>(sm.Qc, 32 * s_, pk, g, l16), bk = tr_frag<K>(sm.Kc, 32 * s_, pk, g, l16);
+      xk[cc] = mfma16x16x32(mh, bq, xk[cc]);
+      xk[cc] = mfma16x16x32(ml, bq, xk[cc]);
+      xk[cc] = mfma16x16x32(wh, bk, xk[cc]);
+      xk[cc] = mfma16x16x32(wl, bk, xk[cc]);
+      xd[cc] = mfma16x16x32(mh, bk, xd[cc]);
+      xd[cc] = mfma16x16x32(ml, bk, xd[cc]);
+    }
+  }
+  float ddp = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < KBW; ++cc) {
+    const int kc = 16 * (KBW * hw + cc) + l16;
+    xk[cc] -= dd_ * (xd[cc] + xq[cc]);
+    ddp -= hsum(xq[cc] * kv[cc]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * tb + 4 * g + i;
+      if (t < nrows) {
+        const int64_t off = (tok0 + static_cast<int64_t>(t) * H) * K + kc;
+        dq[off] = xq[cc][i];
+        dk[off] = xk[cc][i];
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) ddp += __shfl_xor(ddp, m, kWave);
+  __syncthreads();
+  if (lane == 0) sm.red[8 + wave] = ddp;
+  __syncthreads();
+  if (wave == 0) grad_scalars(sm.gt, sm.vec, sm.red, lane, nrows, tok0, H, dalpha, dbeta, dd_part + slot * H + h);
 }
 
 // dd per head: one 64-thread block per head sums the chunks in a fixed order
@@ -1116,10 +1548,17 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  chunk_bwd_grad_kernel<K, V, InT><<<grid, 512, 0, st>>>(
-      static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v), a.d,
-      static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg, a.Gg,
-      a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dd_part);
+  if constexpr (sizeof(InT) == 2) {
+    chunk_bwd_grad_bf16_kernel<K, V><<<grid, 512, 0, st>>>(
+        static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.d,
+        static_cast<const u16*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg, a.Gg,
+        a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dd_part);
+  } else {
+    chunk_bwd_grad_kernel<K, V, InT><<<grid, 512, 0, st>>>(
+        static_cast<const InT*>(a.q), static_cast<const InT*>(a.k), static_cast<const InT*>(a.v), a.d,
+        static_cast<const InT*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg, a.Gg,
+        a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dd_part);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   dd_reduce_kernel<<<a.H, 64, 0, st>>>(a.dd_part, nslots, a.H, a.dd);

@@ -1,13 +1,25 @@
 """GPU parity of the chunk backward (comba_chunk_bwd) against the fp64
 reverse-mode oracle of the token recurrence (oracle.comba_backward), on the
-same seeded inputs and cotangents. The gradients are accumulated in fp32 from
-exact inputs (bf16 inputs are exact in fp32). Products are exact-fp32 matrix
-core products, except in the reverse scan for bf16 inputs, whose fp32 operands
-enter the bf16 matrix cores as hi + lo parts (about 16 significant bits, a
-relative error near 2^-17 per operand). The gate is rel-L2 <= 1e-5 per
-gradient tensor: that rounding and fp32's (6e-8), accumulated over sums of a
-few hundred terms, the chunk inverse and the scan over the chunks. Measured:
-4e-8 to 3.1e-6.
+same seeded inputs and cotangents. The gradients are accumulated in fp32.
+
+fp32 inputs: every product is an exact-fp32 matrix-core product, so the gate
+is rel-L2 <= 1e-5 per gradient tensor (fp32 rounding, 6e-8, accumulated over
+sums of a few hundred terms, the chunk inverse and the scan over the chunks).
+Measured: 4e-8 to 8e-7.
+
+bf16 inputs: q, k, v and dO enter the bf16 matrix cores exactly; every fp32
+operand (states, state gradients, the chunk inverse, scores and the
+intermediate products) enters as hi + lo bf16, about 16 significant bits (a
+relative error up to u = 2^-17 = 7.6e-6 per operand); a product of two split
+operands carries about 3u relative to the product of their magnitudes, and a
+gradient that is a short sum of such products with cancellation (dq of a
+one-token sequence: the state term against the score term) more. The gate is
+rel-L2 <= 5e-5 (about 6.6u) per per-token gradient tensor; measured: up to
+5e-6, and 1.1e-5 for one-token sequences. dd is a signed sum over every token
+and key of a head, so cancellation scales its relative error by
+sum |dq k| / |dd|; it is gated by |dd - dd_ref| <= 5e-5 sum |dq k| per head
+(measured up to 1.1e-5). All of these lie far inside the bf16 tolerance of
+the forward (rel-L2 2e-3).
 """
 import dataclasses
 
@@ -22,7 +34,9 @@ from _util import dev_inputs, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
-GATE = 1e-5
+GATE = 1e-5        # fp32 inputs
+GATE_BF16 = 5e-5   # bf16 inputs: hi / lo bf16 matrix-core products
+DD_COND = 5e-5     # bf16 inputs, dd: error relative to sum |dq (.) k| of the head
 NAMES = ("dq", "dk", "dv", "dalpha", "dbeta", "dd", "ds0")
 
 
@@ -67,10 +81,18 @@ def oracle_bwd(inp, do, dsf):
     return oracle.comba_backward(inp.q, inp.k, inp.v, inp.alpha, inp.beta, inp.d, do, inp.s0, dsf, inp.cu_seqlens)
 
 
-def check(got, ref, gate=GATE, names=NAMES):
-    errs = {key: rel_l2(got[key], ref[key]) for key in names}
+def check(got, ref, inp, names=NAMES):
+    bf16 = inp.dtype == "bf16"
+    gate = GATE_BF16 if bf16 else GATE
+    errs = {key: rel_l2(got[key], ref[key]) for key in names if not (bf16 and key == "dd")}
+    limits = dict.fromkeys(errs, gate)
+    if bf16 and "dd" in names:
+        # per head: sum over batch rows, tokens and keys of |dq (.) k|
+        scale = np.abs(np.asarray(ref["dq"], np.float64) * np.asarray(inp.k, np.float64)).sum(axis=(0, 1, 3))
+        errs["dd/cond"] = float(np.max(np.abs(np.asarray(got["dd"], np.float64) - ref["dd"]) / scale))
+        limits["dd/cond"] = DD_COND
     print(" ".join(f"{key}={e:.2e}" for key, e in errs.items()), flush=True)
-    bad = {key: e for key, e in errs.items() if not e <= gate}
+    bad = {key: e for key, e in errs.items() if not e <= limits[key]}
     assert not bad, bad
 
 
@@ -79,7 +101,7 @@ def check(got, ref, gate=GATE, names=NAMES):
 def test_fp32_backward_shapes(K, V, T):
     inp = make_inputs(wl("tiny_fp32", K=K, V=V, B=2, H=2), T=T, s0_std=0.1, seed=71)
     do, do_bits, dsf = cotangents(inp, 72)
-    check(run_bwd(inp, do, do_bits, dsf), oracle_bwd(inp, do, dsf))
+    check(run_bwd(inp, do, do_bits, dsf), oracle_bwd(inp, do, dsf), inp)
 
 
 @pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (128, 64), (64, 128)])
@@ -87,14 +109,14 @@ def test_fp32_backward_shapes(K, V, T):
 def test_bf16_backward_shapes(K, V, T, s0):
     inp = make_inputs(wl("layer_340m", K=K, V=V, B=2, H=2), T=T, s0_std=s0, seed=73)
     do, do_bits, dsf = cotangents(inp, 74, with_dsf=s0 > 0)
-    check(run_bwd(inp, do, do_bits, dsf), oracle_bwd(inp, do, dsf))
+    check(run_bwd(inp, do, do_bits, dsf), oracle_bwd(inp, do, dsf), inp)
 
 
 def test_bf16_backward_many_chunks():
     """Eight chunks of the 340M-layer head shape: the reverse scan's carry."""
     inp = make_inputs(wl("layer_340m", B=1, H=2), T=512, s0_std=0.02, seed=75)
     do, do_bits, dsf = cotangents(inp, 76)
-    check(run_bwd(inp, do, do_bits, dsf), oracle_bwd(inp, do, dsf))
+    check(run_bwd(inp, do, do_bits, dsf), oracle_bwd(inp, do, dsf), inp)
 
 
 def test_backward_varlen_edge_lengths():
@@ -102,7 +124,7 @@ def test_backward_varlen_edge_lengths():
     inp = make_inputs(wl("varlen", H=3), lengths=lengths, s0_std=0.05, seed=77)
     do, do_bits, dsf = cotangents(inp, 78)
     got = run_bwd(inp, do, do_bits, dsf)
-    check(got, oracle_bwd(inp, do, dsf))
+    check(got, oracle_bwd(inp, do, dsf), inp)
     # an empty sequence passes its final-state gradient straight to its initial state
     for n in np.flatnonzero(lengths == 0):
         np.testing.assert_array_equal(got["ds0"][n], dsf[n].astype(np.float64))
@@ -111,7 +133,7 @@ def test_backward_varlen_edge_lengths():
 def test_backward_without_final_state_gradient():
     inp = make_inputs(wl("layer_340m", B=2, H=2), T=200, s0_std=0.02, seed=79)
     do, do_bits, _ = cotangents(inp, 80, with_dsf=False)
-    check(run_bwd(inp, do, do_bits, None), oracle_bwd(inp, do, None))
+    check(run_bwd(inp, do, do_bits, None), oracle_bwd(inp, do, None), inp)
 
 
 def test_backward_deterministic():
@@ -139,5 +161,5 @@ def test_backward_layer_1p3b_full_size_sampled():
         part = {"dq": got["dq"][b:b + 1, :, h:h + 1], "dk": got["dk"][b:b + 1, :, h:h + 1],
                 "dv": got["dv"][b:b + 1, :, h:h + 1], "dalpha": got["dalpha"][b:b + 1, :, h:h + 1],
                 "dbeta": got["dbeta"][b:b + 1, :, h:h + 1], "ds0": got["ds0"][b:b + 1, h:h + 1]}
-        check(part, ref, names=tuple(part))
+        check(part, ref, inp, names=tuple(part))
     assert all(np.isfinite(x).all() for x in got.values())
