@@ -58,6 +58,28 @@ def chunk_fwd_algorithmic(B, T, H, K, V, with_s0=True):
     return nbytes, flops
 
 
+def chunk_bwd_algorithmic(B, T, H, K, V):
+    """Bytes and flops of the chunk backward at the algorithm's floor.
+
+    Bytes: q, k, v, dO (bf16), alpha, beta (fp32) read once and dq, dk, dv,
+    dalpha, dbeta (fp32) written once per head-token, plus S0 and dS_final
+    read and dS0 written once per (sequence, head). Checkpoints, the cached
+    inverse and score matrices and every re-read are design traffic beyond it.
+    Flops (per chunk of C tokens, triangle-aware as for the forward): forming
+    Ubar from the chunk's state (K h, Tinv R), dUbar = P^T dO + e^(Gn-G) K dh,
+    dR = Tinv^T dUbar, dh_in = q~^T diag(e^G) dO - K^T diag(b1) dR, dA, dP,
+    dO h^T, dR h^T, Ubar dh^T, (dP (.) M) K, (dP (.) M)^T q~, beta W K and
+    W^T beta K; the chunk inverse (cached or recomputed) is not counted.
+    """
+    ht = B * T * H
+    nbytes = ht * (2 * K * 2 + 2 * V * 2 + 8) + ht * (2 * K * 4 + V * 4 + 8) + 3 * B * H * V * K * 4
+    C = CHUNK
+    per_chunk = (14 * C * K * V + 4 * C * (C + 1) * V + C * (C - 1) * V
+                 + 2 * C * (C + 1) * K + 2 * C * (C - 1) * K)
+    flops = per_chunk / C * ht
+    return nbytes, flops
+
+
 # the sources the counted chunk-forward kernel is compiled from
 FWD_SOURCES = ("chunk_fwd_bf16.hip", "chunk_common.h", "device_common.h", "launch.h")
 
@@ -381,8 +403,12 @@ def main():
                             workspace=bws)
 
         bms, _ = time_loop(torch, bstep, max(args.steps // 20, 3), 2)
+        bbytes, bflops = chunk_bwd_algorithmic(B, T, H, K, V)
         result["backward"] = {"workload": "layer_1p3b, chunk backward (dq, dk, dv, dalpha, dbeta, dd, dS0)",
                               "us_per_step": bms * 1e3, "tokens/s": B * T / (bms * 1e-3),
+                              "algorithmic_bytes": bbytes, "hbm_frac": bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "algorithmic_flops": bflops,
+                              "mfma_frac": bflops / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                               "workspace_bytes": bws.numel()}
         del bws, do_, dsf_
 
@@ -403,9 +429,12 @@ def main():
         lsteps, lwarm = max(args.steps // 10, 5), min(args.warmup // 10 + 2, 12)
         pms, _ = time_loop(torch, lstep(None), lsteps, lwarm)
         sms_, _ = time_loop(torch, lstep(0), lsteps, lwarm)
+        lbytes, _ = chunk_fwd_algorithmic(1, wl_.T, wl_.H, wl_.K, wl_.V)
         result["long_context"] = {"workload": "long_context", "B": 1, "T": wl_.T, "H": wl_.H, "K": wl_.K, "V": wl_.V,
                                   "plain_us": pms * 1e3, "segmented_us": sms_ * 1e3,
                                   "segmented_tokens/s": wl_.T / (sms_ * 1e-3), "plain_tokens/s": wl_.T / (pms * 1e-3),
+                                  "algorithmic_bytes": lbytes,
+                                  "segmented_hbm_frac": lbytes / (sms_ * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                   "segments": "automatic (8 x 8192 tokens)", "workspace_bytes": nws}
         del tl, li
 
