@@ -30,9 +30,10 @@
 //                          Tinv, P, k_t.k_s and the decay gates of the chunk,
 //                          stored;
 //   chunk_bwd_dh_kernel    reverse scan over chunks, one workgroup per
-//   (_bf16_kernel)         (sequence, head, 32 value channels), next chunk
-//                          prefetched into registers: stores each
-//                          chunk's outgoing-state gradient dh, writes dS_0;
+//   (_bf16_kernel)         (sequence, head, 32 (fp32) or 64 (bf16) value
+//                          channels), next chunk prefetched into registers:
+//                          stores each chunk's outgoing-state gradient dh,
+//                          writes dS_0;
 //   chunk_bwd_grad_kernel  one workgroup per (chunk, head): every per-token
 //                          gradient and a partial of dd;
 //   dd_reduce_kernel       dd per head, summed over chunks in a fixed order.
@@ -921,6 +922,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
 
 // ---- reverse scan of dh on bf16 matrix cores (bf16 q, k, dO) ----------------------------
 
+constexpr int kDhbVT = 64;  // value channels per workgroup of the bf16 reverse scan
+
 // One chunk of the scan in LDS. Exact bf16 operands: q, k (token rows, keys
 // of each 32-block in perm32 order) and dO (token rows). Split into hi / lo
 // bf16: P and Tinv ([t'][t] as the prep kernel stores them), and the
@@ -930,18 +933,19 @@ template <int K>
 struct alignas(16) SmemDhB {
   u16 Qc[64 * K], Kc[64 * K];
   u16 Ph[64 * 64], Pl[64 * 64], Th[64 * 64], Tl[64 * 64];
-  u16 dO[64 * kDhVT];
-  u16 dUh[kDhVT * 64], dUl[kDhVT * 64], Xh[kDhVT * 64], Xl[kDhVT * 64], Zh[kDhVT * 64], Zl[kDhVT * 64];
-  u16 dhh[kDhVT * K], dhl[kDhVT * K];
+  u16 dO[64 * kDhbVT];
+  u16 dUh[kDhbVT * 64], dUl[kDhbVT * 64], Xh[kDhbVT * 64], Xl[kDhbVT * 64], Zh[kDhbVT * 64], Zl[kDhbVT * 64];
+  u16 dhh[kDhbVT * K], dhl[kDhbVT * K];
   ChunkGates gt;
 };
 
 // Reverse scan of dh for bf16 inputs: the products of chunk_bwd_dh_kernel on
 // 16x16x32 bf16 matrix cores, every fp32 operand split into hi + lo bf16
-// (exact operands enter once). Wavefront w owns channel block cb = w / 4: the
-// token block tb of dUbar and dR (tb = w % 4 for cb = 0, 3 - w % 4 for cb = 1,
-// so that the wavefronts of a SIMD hold triangle rows of complementary length)
-// and the key blocks NBW (w % 4) + c of dh, kept in fp32 registers across the
+// (exact operands enter once), 64 value channels per workgroup. Wavefront w
+// owns the channel blocks cb = 2 (w / 4) + {0, 1}: the token block tb of their
+// dUbar and dR (tb = w % 4 for w < 4, 3 - w % 4 otherwise, so that the two
+// wavefronts of a SIMD hold triangle rows of complementary length) and the key
+// blocks NBW (w % 4) + c of their dh, kept in fp32 registers across the
 // chunks. Per chunk, three barriers after the staging one:
 //   dUbar = diag(e^(Gn - G)) K dh + P^T dO
 //   dR    = Tinv^T dUbar,  X = diag(e^G) dO,  Z = -d X - diag(b1) dR
@@ -952,9 +956,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
     const float* __restrict__ Pg, const float* __restrict__ Gg, const float* __restrict__ dsf,
     float* __restrict__ dhck, float* __restrict__ ds0) {
-  constexpr int NT = 512, VT = kDhVT, NVT = V / VT, NBW = K / 64;  // dh key blocks per wavefront
+  constexpr int NT = 512, VT = kDhbVT, NVT = V / VT, NBW = K / 64;  // dh key blocks per channel block
   constexpr int MPT = 64 * 16 / NT;
-  static_assert(VT == 32 && 64 * VT / 4 == NT, "two 16-channel blocks, one dO piece per thread");
+  static_assert(VT == 64 && 64 * VT / 8 == NT, "four 16-channel blocks, one 16-byte dO piece per thread");
   __shared__ SmemDhB<K> sm;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -966,31 +970,32 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
   const float dd_ = d[h];
   const int nch = (t1 - t0 + 63) / 64;
   const bool packed = cu_seqlens != nullptr;
-  const int cb = wave >> 2, tb = cb == 0 ? (wave & 3) : 3 - (wave & 3);
-  const int ch = 16 * cb + l16;                                 // this lane's channel in the tile
-  const int64_t crow = (static_cast<int64_t>(n) * H + h) * V + vt * VT + ch;  // its state row
+  const int cb0 = 2 * (wave >> 2), tb = wave < 4 ? (wave & 3) : 3 - (wave & 3);
+  const int64_t crow0 = (static_cast<int64_t>(n) * H + h) * V + vt * VT + l16;  // state row of channel l16
 
-  // dh blocks (keys 16 kb + 4 g + i, channel ch), fp32, from dL/dS_final
-  f32x4 dhr[NBW];
+  // dh blocks (keys 16 kb + 4 g + i, channel 16 cb + l16), fp32, from dL/dS_final
+  f32x4 dhr[2][NBW];
 #pragma unroll
-  for (int c = 0; c < NBW; ++c) {
-    const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
-    dhr[c] = dsf ? ld4(dsf + crow * K + key4) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int c = 0; c < NBW; ++c) {
+      const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
+      dhr[j][c] = dsf ? ld4(dsf + (crow0 + 16 * (cb0 + j)) * K + key4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
   // next chunk's operands, one chunk ahead in registers
   RowPieces<K, NT, u16> rqk;
-  u32x2 ro;
+  u32x4 ro;
   f32x4 rg{};
   f32x4 rt[MPT], rp[MPT];
-  const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));
+  const int orow = tid / (VT / 8), ocol = 8 * (tid % (VT / 8));
   auto fetch = [&](int ci) {
     const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
     const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
     const int64_t sl = chunk_slot(packed, t0, n, ci, T) * H + h;
     rqk.load(q, k, tok0, H, nrows, tid);
     const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
-    ro = __builtin_amdgcn_raw_buffer_load_b64(orsrc, (orow * H * V + vt * VT + ocol) * 2, 0, 0);
+    ro = load16(orsrc, (orow * H * V + vt * VT + ocol) * 2);
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
@@ -1005,7 +1010,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
     const int64_t slot = chunk_slot(packed, t0, n, ci, T);
     __syncthreads();
     rqk.store_bf16(sm.Qc, sm.Kc, tid);
-    *reinterpret_cast<u32x2*>(&sm.dO[swz<VT>(orow, ocol)]) = ro;
+    *reinterpret_cast<u32x4*>(&sm.dO[swz<VT>(orow, ocol)]) = ro;
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
@@ -1015,79 +1020,104 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
     if (tid < kGateWords / 4) st4(&sm.gt.G[0] + 4 * tid, rg);
     // this chunk's outgoing-state gradient: hi / lo for the products, fp32 for
     // the gradient kernel ([channel][key])
-    float* dst = dhck + ((slot * H + h) * V + vt * VT + ch) * K;
 #pragma unroll
-    for (int c = 0; c < NBW; ++c) {
-      const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
-      put_split4(sm.dhh, sm.dhl, swz<K>(ch, perm_col(key4)), dhr[c]);
-      st4(dst + key4, dhr[c]);
+    for (int j = 0; j < 2; ++j) {
+      const int ch = 16 * (cb0 + j) + l16;
+      float* dst = dhck + ((slot * H + h) * V + vt * VT + ch) * K;
+#pragma unroll
+      for (int c = 0; c < NBW; ++c) {
+        const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
+        put_split4(sm.dhh, sm.dhl, swz<K>(ch, perm_col(key4)), dhr[j][c]);
+        st4(dst + key4, dhr[j][c]);
+      }
     }
     __syncthreads();
     if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
 
-    // dUbar of block (tb, cb): diag(e^(Gn - G)) K dh, then + P^T dO
-    f32x4 kd{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s_ = 0; s_ < K / 32; ++s_) {
-      const bf16x8 a = lds8(&sm.Kc[swz<K>(16 * tb + l16, 32 * s_ + 8 * g)]);
-      kd = mfma16x16x32(a, lds8(&sm.dhh[swz<K>(ch, 32 * s_ + 8 * g)]), kd);
-      kd = mfma16x16x32(a, lds8(&sm.dhl[swz<K>(ch, 32 * s_ + 8 * g)]), kd);
-    }
-    const f32x4 en = ld4(&sm.gt.EGnG[16 * tb + 4 * g]);
-    f32x4 du = en * kd;
-#pragma unroll
-    for (int s_ = 0; s_ < 2; ++s_) {
-      if (s_ == 0 && tb >= 2) continue;  // P[t'][t] = 0 for t' < t
-      const int pos = 16 * tb + 4 * (l16 & 3);
-      const bf16x8 o = tr_frag<VT>(sm.dO, 32 * s_, 16 * cb + 4 * (l16 & 3), g, l16);
-      du = mfma16x16x32(tr_frag<64>(sm.Ph, 32 * s_, pos, g, l16), o, du);
-      du = mfma16x16x32(tr_frag<64>(sm.Pl, 32 * s_, pos, g, l16), o, du);
-    }
-    put_split4(sm.dUh, sm.dUl, swz<64>(ch, perm_col(16 * tb + 4 * g)), du);
-    __syncthreads();
-
-    // dR = Tinv^T dUbar, then X and Z of block (tb, cb)
-    f32x4 dr{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s_ = 0; s_ < 2; ++s_) {
-      if (s_ == 0 && tb >= 2) continue;  // Tinv[t'][t] = 0 for t' < t
-      const int pos = 16 * tb + 4 * (l16 & 3);
-      dr = mma3(tr_frag<64>(sm.Th, 32 * s_, pos, g, l16), tr_frag<64>(sm.Tl, 32 * s_, pos, g, l16),
-                lds8(&sm.dUh[swz<64>(ch, 32 * s_ + 8 * g)]), lds8(&sm.dUl[swz<64>(ch, 32 * s_ + 8 * g)]), dr);
-    }
+    // dUbar of the blocks (tb, cb): diag(e^(Gn - G)) K dh, then + P^T dO
     {
-      const f32x4 eg = ld4(&sm.gt.EG[16 * tb + 4 * g]), b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
-      const f32x4 x = eg * tr4<VT>(sm.dO, 16 * tb, 16 * cb + 4 * (l16 & 3), g, l16);
-      const f32x4 z = -dd_ * x - b1 * dr;
-      const int off = swz<64>(ch, perm_col(16 * tb + 4 * g));
-      put_split4(sm.Xh, sm.Xl, off, x);
-      put_split4(sm.Zh, sm.Zl, off, z);
+      f32x4 kd[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int s_ = 0; s_ < K / 32; ++s_) {
+        const bf16x8 a = lds8(&sm.Kc[swz<K>(16 * tb + l16, 32 * s_ + 8 * g)]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int off = swz<K>(16 * (cb0 + j) + l16, 32 * s_ + 8 * g);
+          kd[j] = mfma16x16x32(a, lds8(&sm.dhh[off]), kd[j]);
+          kd[j] = mfma16x16x32(a, lds8(&sm.dhl[off]), kd[j]);
+        }
+      }
+      const f32x4 en = ld4(&sm.gt.EGnG[16 * tb + 4 * g]);
+      const int pos = 16 * tb + 4 * (l16 & 3);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4 du = en * kd[j];
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          if (s_ == 0 && tb >= 2) continue;  // P[t'][t] = 0 for t' < t
+          const bf16x8 o = tr_frag<VT>(sm.dO, 32 * s_, 16 * (cb0 + j) + 4 * (l16 & 3), g, l16);
+          du = mfma16x16x32(tr_frag<64>(sm.Ph, 32 * s_, pos, g, l16), o, du);
+          du = mfma16x16x32(tr_frag<64>(sm.Pl, 32 * s_, pos, g, l16), o, du);
+        }
+        put_split4(sm.dUh, sm.dUl, swz<64>(16 * (cb0 + j) + l16, perm_col(16 * tb + 4 * g)), du);
+      }
     }
     __syncthreads();
 
-    // dh <- e^Gn dh + q^T X + k^T Z for the wavefront's key blocks
+    // dR = Tinv^T dUbar, then X and Z of the blocks (tb, cb)
+    {
+      const int pos = 16 * tb + 4 * (l16 & 3);
+      const f32x4 eg = ld4(&sm.gt.EG[16 * tb + 4 * g]), b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ch = 16 * (cb0 + j) + l16;
+        f32x4 dr{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s_ = 0; s_ < 2; ++s_) {
+          if (s_ == 0 && tb >= 2) continue;  // Tinv[t'][t] = 0 for t' < t
+          const int bo = swz<64>(ch, 32 * s_ + 8 * g);
+          dr = mma3(tr_frag<64>(sm.Th, 32 * s_, pos, g, l16), tr_frag<64>(sm.Tl, 32 * s_, pos, g, l16),
+                    lds8(&sm.dUh[bo]), lds8(&sm.dUl[bo]), dr);
+        }
+        const f32x4 x = eg * tr4<VT>(sm.dO, 16 * tb, 16 * (cb0 + j) + 4 * (l16 & 3), g, l16);
+        const f32x4 z = -dd_ * x - b1 * dr;
+        const int off = swz<64>(ch, perm_col(16 * tb + 4 * g));
+        put_split4(sm.Xh, sm.Xl, off, x);
+        put_split4(sm.Zh, sm.Zl, off, z);
+      }
+    }
+    __syncthreads();
+
+    // dh <- e^Gn dh + q^T X + k^T Z for the wavefront's blocks
     const float eGn = sm.gt.EG[63];
 #pragma unroll
     for (int c = 0; c < NBW; ++c) {
       const int kb = NBW * (wave & 3) + c;
-      f32x4 acc = eGn * dhr[c];
+      f32x4 acc[2] = {eGn * dhr[0][c], eGn * dhr[1][c]};
 #pragma unroll
       for (int s_ = 0; s_ < 2; ++s_) {
         const int pos = perm_col(16 * kb + 4 * (l16 & 3));
         const bf16x8 aq = tr_frag<K>(sm.Qc, 32 * s_, pos, g, l16);
         const bf16x8 ak = tr_frag<K>(sm.Kc, 32 * s_, pos, g, l16);
-        const int off = swz<64>(ch, 32 * s_ + 8 * g);
-        acc = mfma16x16x32(aq, lds8(&sm.Xh[off]), acc);
-        acc = mfma16x16x32(aq, lds8(&sm.Xl[off]), acc);
-        acc = mfma16x16x32(ak, lds8(&sm.Zh[off]), acc);
-        acc = mfma16x16x32(ak, lds8(&sm.Zl[off]), acc);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int off = swz<64>(16 * (cb0 + j) + l16, 32 * s_ + 8 * g);
+          acc[j] = mfma16x16x32(aq, lds8(&sm.Xh[off]), acc[j]);
+          acc[j] = mfma16x16x32(aq, lds8(&sm.Xl[off]), acc[j]);
+          acc[j] = mfma16x16x32(ak, lds8(&sm.Zh[off]), acc[j]);
+          acc[j] = mfma16x16x32(ak, lds8(&sm.Zl[off]), acc[j]);
+        }
       }
-      dhr[c] = acc;
+      dhr[0][c] = acc[0];
+      dhr[1][c] = acc[1];
     }
   }
   if (ds0) {
 #pragma unroll
-    for (int c = 0; c < NBW; ++c) st4(ds0 + crow * K + 16 * (NBW * (wave & 3) + c) + 4 * g, dhr[c]);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int c = 0; c < NBW; ++c)
+        st4(ds0 + (crow0 + 16 * (cb0 + j)) * K + 16 * (NBW * (wave & 3) + c) + 4 * g, dhr[j][c]);
   }
 }
 
@@ -1538,7 +1568,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(InT) == 2) {
-    chunk_bwd_dh_bf16_kernel<K, V><<<xcd_grid(a.N * a.H, V / kDhVT), 512, 0, st>>>(
+    chunk_bwd_dh_bf16_kernel<K, V><<<xcd_grid(a.N * a.H, V / kDhbVT), 512, 0, st>>>(
         static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), a.d, static_cast<const u16*>(a.dO),
         a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.Gg, a.dsf, a.dhck, a.ds0);
   } else {
