@@ -232,12 +232,14 @@ struct alignas(16) SmemPrepMfma {
   ChunkGates gt;
 };
 
-// A (to LDS, for the inverse), P and k_t.k_s (to the per-chunk buffers) of one entry.
+// A (to LDS, for the inverse), P and, for the fp32 gradient kernel, k_t.k_s
+// (to the per-chunk buffers) of one entry. Hardware exp (about 2 ulp).
+template <bool kStoreKK>
 __device__ __forceinline__ void prep_entry(const ChunkGates& gt, int t, int s, float kk, float qtk, float* Am,
                                            float* Pg, float* KKg) {
-  Am[t * kLdF + s] = s < t ? gt.beta[t] * expf(gt.Gx[t] - gt.G[s]) * kk : 0.f;
-  Pg[t * 64 + s] = s <= t ? qtk * expf(fminf(gt.G[t] - gt.G[s], 0.f)) : 0.f;
-  KKg[t * 64 + s] = kk;
+  Am[t * kLdF + s] = s < t ? gt.beta[t] * __expf(gt.Gx[t] - gt.G[s]) * kk : 0.f;
+  Pg[t * 64 + s] = s <= t ? qtk * __expf(fminf(gt.G[t] - gt.G[s], 0.f)) : 0.f;
+  if constexpr (kStoreKK) KKg[t * 64 + s] = kk;
 }
 
 template <int K, typename InT>
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * rb + 4 * g + i, s_ = 16 * cb + l16;
-        prep_entry(sm.gt, t, s_, akk[cb][i], aqk[cb][i] - dh * akk[cb][i], sm.Am, Pg + mb, KKg + mb);
+        prep_entry<false>(sm.gt, t, s_, akk[cb][i], aqk[cb][i] - dh * akk[cb][i], sm.Am, Pg + mb, KKg + mb);
       }
     }
   } else {
@@ -335,7 +337,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) prep_entry(sm.gt, tb + i, sb + j, kk[i][j], qk[i][j], sm.Am, Pg + mb, KKg + mb);
+      for (int j = 0; j < 4; ++j) prep_entry<true>(sm.gt, tb + i, sb + j, kk[i][j], qk[i][j], sm.Am, Pg + mb, KKg + mb);
   }
   __syncthreads();
   unit_lower_inverse64<NT>(sm.Am, sm.Tm, sm.Ys, tid);
@@ -1130,7 +1132,7 @@ constexpr int kGbVT = 32;  // value channels per tile of the bf16 gradient kerne
 // hi / lo: Tinv and P ([t][s], s in perm32 order), the state and
 // state-gradient tiles ([channel][key], perm32) and R, Ubar, dUbar, dR
 // ([channel][token], perm32); after the value tiles, dP (.) M and beta W as
-// [s][t] (t in perm32 order) and the fp32 products summed by rows and columns.
+// [s][t] (t in perm32 order) and partial row and column sums.
 template <int K>
 struct alignas(16) SmemGradB {
   u16 Qc[64 * K], Kc[64 * K];
@@ -1144,8 +1146,8 @@ struct alignas(16) SmemGradB {
     } t;
     struct {
       u16 dPMh[64 * 64], dPMl[64 * 64], WBh[64 * 64], WBl[64 * 64];
-      float dPP[64][kLdT];  // dP (.) P
-      float X[64][kLdT];    // W (.) k_t.k_s
+      float rows[2][2][64];  // per wave half: row sums of dP (.) P and W (.) k_t.k_s
+      float cols[4][2][64];  // per token block: column sums of dP (.) P and beta W (.) k_t.k_s
     } p;
   } u;
   ChunkGates gt;
@@ -1167,9 +1169,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v, const float* __restrict__ d,
     const u16* __restrict__ dO, const int32_t* __restrict__ cu_seqlens, int T, int H, int N, int64_t nslots,
     const float* __restrict__ hck, const float* __restrict__ dhck, const float* __restrict__ Tg,
-    const float* __restrict__ Pg, const float* __restrict__ KKg, const float* __restrict__ Gg,
-    float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv, float* __restrict__ dalpha,
-    float* __restrict__ dbeta, float* __restrict__ dd_part) {
+    const float* __restrict__ Pg, const float* __restrict__ Gg, float* __restrict__ dq, float* __restrict__ dk,
+    float* __restrict__ dv, float* __restrict__ dalpha, float* __restrict__ dbeta, float* __restrict__ dd_part) {
   constexpr int NT = 512, VT = kGbVT, NTILE = V / VT, KB = K / 16, KBW = KB / 2;
   constexpr int HP = VT * K / 4 / NT;  // 16-byte pieces of a state tile per thread
   constexpr int MPT = 64 * 16 / NT;
@@ -1206,7 +1207,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   }
   f32x4 rg{};
   if (tid < kGateWords / 4) rg = ld4(Gg + (slot * H + h) * kGateWords + 4 * tid);
-  float kkv[2][4];  // k_t.k_s of this lane's entries of the blocks (tb, 2 hw + cc), loaded with the last tile
   // value tiles, one tile ahead: state rows, state-gradient rows, dO and v pieces
   const int orow = tid / (VT / 4), ocol = 4 * (tid % (VT / 4));
   const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
@@ -1257,14 +1257,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     }
     *reinterpret_cast<u32x2*>(&sm.u.t.dO[swz<VT>(orow, perm_col(ocol))]) = pO;
     *reinterpret_cast<u32x2*>(&sm.u.t.Vt[swz<VT>(orow, ocol)]) = pV;
-    if (jt + 1 < NTILE) {
-      fetch_tile(jt + 1);  // in flight during this tile's work
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kkv[cc][i] = KKg[mb + (16 * tb + 4 * g + i) * 64 + 16 * (2 * hw + cc) + l16];
-    }
+    if (jt + 1 < NTILE) fetch_tile(jt + 1);  // in flight during this tile's work
     __syncthreads();
     // Opaque per-tile copies of the lane coordinates: the LDS addresses below
     // are then formed inside the loop instead of being hoisted out of it,
@@ -1331,8 +1324,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     }
     __syncthreads();
     if (hw == 0) {  // dR = Tinv^T dUbar, dv = beta dR, and the channel sums of dR
-      const f32x4 ex = {expf(sm.gt.Gx[16 * tb + 4 * g]), expf(sm.gt.Gx[16 * tb + 4 * g + 1]),
-                        expf(sm.gt.Gx[16 * tb + 4 * g + 2]), expf(sm.gt.Gx[16 * tb + 4 * g + 3])};
+      f32x4 eGx;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eGx[i] = __expf(sm.gt.Gx[16 * tb + 4 * g + i]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         f32x4 dr{0.f, 0.f, 0.f, 0.f};
@@ -1349,7 +1343,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
           const int t = 16 * tb + 4 * g + i;
           if (t < nrows) dv[(tok0 + static_cast<int64_t>(t) * H) * V + v0 + 16 * cb + l16] = bt[i] * dr[i];
         }
-        sbR += dr * (vv[cb] - ex * kx[cb]);
+        sbR += dr * (vv[cb] - eGx * kx[cb]);
         sKhdR += kx[cb] * dr;
       }
     } else {  // (K dh) . Ubar over the channels
@@ -1432,49 +1426,86 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
 #pragma unroll
   for (int m = 1; m < kWave; m <<= 1) shdh += __shfl_xor(shdh, m, kWave);
   if (lane == 0) sm.red[wave] = shdh;
-  // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cc)
+  // k_t.k_s of the blocks (tb, 2 hw + cc) from the exact bf16 k tile
+  f32x4 kkv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int s_ = 0; s_ < K / 32; ++s_) {
+    const bf16x8 a = lds8(&sm.Kc[swz<K>(16 * tb + l16, 32 * s_ + 8 * g)]);
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      kkv[cc] = mfma16x16x32(a, lds8(&sm.Kc[swz<K>(16 * (2 * hw + cc) + l16, 32 * s_ + 8 * g)]), kkv[cc]);
+  }
+  // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cc); the
+  // row sums (over s) and column sums (over t) of dP (.) P and W (.) k_t.k_s
+  // are reduced in registers: over this lane's two blocks and the 16 lanes of a
+  // row group for the rows, over its four rows and the four row groups for the
+  // columns, then per wavefront into LDS partials (summed in a fixed order).
+  f32x4 rowP{0.f, 0.f, 0.f, 0.f}, rowX{0.f, 0.f, 0.f, 0.f};
+  float colP[2], colX[2];
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int s_ = 16 * (2 * hw + cc) + l16;
     // P[t][s] from its hi / lo parts (about 16 significant bits)
     const int ps = perm_col(16 * (2 * hw + cc) + 4 * (l16 & 3));
     const f32x4 pv = tr4<64>(sm.Ph, 16 * tb, ps, g, l16) + tr4<64>(sm.Pl, 16 * tb, ps, g, l16);
+    const float Gs = sm.gt.G[s_];
     f32x4 dpm, wb;
+    colP[cc] = colX[cc] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * tb + 4 * g + i;
-      const float M = s_ <= t ? expf(fminf(sm.gt.G[t] - sm.gt.G[s_], 0.f)) : 0.f;
-      const float E = s_ < t ? expf(fminf(sm.gt.Gx[t] - sm.gt.G[s_], 0.f)) : 0.f;
+      const float M = s_ <= t ? __expf(fminf(sm.gt.G[t] - Gs, 0.f)) : 0.f;
+      const float E = s_ < t ? __expf(fminf(sm.gt.Gx[t] - Gs, 0.f)) : 0.f;
       const float dpv = s_ <= t ? accP[cc][i] : 0.f, dav = s_ < t ? -accA[cc][i] : 0.f;
-      const float w = dav * E;
-      sm.u.p.dPP[t][s_] = dpv * pv[i];
-      sm.u.p.X[t][s_] = w * kkv[cc][i];
+      const float w = dav * E, be = sm.gt.beta[t];
+      const float dpp = dpv * pv[i], xx = w * kkv[cc][i];
+      rowP[i] += dpp;
+      rowX[i] += xx;
+      colP[cc] += dpp;
+      colX[cc] += be * xx;
       dpm[i] = dpv * M;
-      wb[i] = sm.gt.beta[t] * w;
+      wb[i] = be * w;
     }
     const int off = swz<64>(s_, perm_col(16 * tb + 4 * g));
     put_split4(sm.u.p.dPMh, sm.u.p.dPMl, off, dpm);
     put_split4(sm.u.p.WBh, sm.u.p.WBl, off, wb);
   }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      rowP[i] += __shfl_xor(rowP[i], m, kWave);
+      rowX[i] += __shfl_xor(rowX[i], m, kWave);
+    }
+  }
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc) {
+#pragma unroll
+    for (int m = 16; m < kWave; m <<= 1) {
+      colP[cc] += __shfl_xor(colP[cc], m, kWave);
+      colX[cc] += __shfl_xor(colX[cc], m, kWave);
+    }
+  }
+  if (l16 == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sm.u.p.rows[hw][0][16 * tb + 4 * g + i] = rowP[i];
+      sm.u.p.rows[hw][1][16 * tb + 4 * g + i] = rowX[i];
+    }
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      sm.u.p.cols[tb][0][16 * (2 * hw + cc) + l16] = colP[cc];
+      sm.u.p.cols[tb][1][16 * (2 * hw + cc) + l16] = colX[cc];
+    }
+  }
   __syncthreads();
-  // row and column sums (fixed order)
   if (tid < 64) {
-    float rp = 0.f, rx = 0.f;
-    for (int s_ = 0; s_ < 64; ++s_) {
-      rp += sm.u.p.dPP[tid][s_];
-      rx += sm.u.p.X[tid][s_];
-    }
-    sm.vec[4][tid] = rp;
-    sm.vec[5][tid] = rx;
-  } else if (tid < 128) {
-    const int s_ = tid - 64;
-    float cp = 0.f, cx = 0.f;
-    for (int t = 0; t < 64; ++t) {
-      cp += sm.u.p.dPP[t][s_];
-      cx += sm.gt.beta[t] * sm.u.p.X[t][s_];
-    }
-    sm.vec[6][s_] = cp;
-    sm.vec[7][s_] = cx;
+    sm.vec[4][tid] = sm.u.p.rows[0][0][tid] + sm.u.p.rows[1][0][tid];
+    sm.vec[5][tid] = sm.u.p.rows[0][1][tid] + sm.u.p.rows[1][1][tid];
+    sm.vec[6][tid] = (sm.u.p.cols[0][0][tid] + sm.u.p.cols[1][0][tid]) + (sm.u.p.cols[2][0][tid] + sm.u.p.cols[3][0][tid]);
+    sm.vec[7][tid] = (sm.u.p.cols[0][1][tid] + sm.u.p.cols[1][1][tid]) + (sm.u.p.cols[2][1][tid] + sm.u.p.cols[3][1][tid]);
   }
   // dq, dk of the blocks (tb, KBW hw + cc):
   //   dq = diag(e^G) dO h^T + (dP (.) M) K
@@ -1581,7 +1612,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   if constexpr (sizeof(InT) == 2) {
     chunk_bwd_grad_bf16_kernel<K, V><<<grid, 512, 0, st>>>(
         static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.d,
-        static_cast<const u16*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.KKg, a.Gg,
+        static_cast<const u16*>(a.dO), a.cu_seqlens, a.T, a.H, a.N, nslots, a.hck, a.dhck, a.Tg, a.Pg, a.Gg,
         a.dq, a.dk, a.dv, a.dalpha, a.dbeta, a.dd_part);
   } else {
     chunk_bwd_grad_kernel<K, V, InT><<<grid, 512, 0, st>>>(
