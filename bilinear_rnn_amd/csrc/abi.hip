@@ -301,15 +301,21 @@ COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const 
   p1.s0 = nullptr;
   p1.sf = bst;
   p1.fusion = fusion | comba::kModeNoOutput;
-  rc = launched(launch(p1));
-  if (rc != COMBA_OK) return rc;
-  // Phi_j: v = 0 from the identity, a K x K state
-  comba::FwdArgs p2 = p1;
-  p2.V = K;
-  p2.sf = phi;
-  p2.fusion = fusion | comba::kModeNoOutput | comba::kModeZeroV | comba::kModeIdentityInit;
-  rc = launched(launch(p2));
-  if (rc != COMBA_OK) return rc;
+  if (in_dtype == COMBA_BF16 && K == V) {
+    // one launch forms both: the producers' work serves the b_j and Phi_j consumers
+    rc = launched(comba::launch_chunk_bf16_pair(p1, phi, st));
+    if (rc != COMBA_OK) return rc;
+  } else {
+    rc = launched(launch(p1));
+    if (rc != COMBA_OK) return rc;
+    // Phi_j: v = 0 from the identity, a K x K state
+    comba::FwdArgs p2 = p1;
+    p2.V = K;
+    p2.sf = phi;
+    p2.fusion = fusion | comba::kModeNoOutput | comba::kModeZeroV | comba::kModeIdentityInit;
+    rc = launched(launch(p2));
+    if (rc != COMBA_OK) return rc;
+  }
   // X_{j+1} = X_j Phi_j + b_j; the last one is the final state
   rc = launched(comba::launch_segment_scan(initial_state, bst, phi, X, final_state, B, H, K, V, p.S, st));
   if (rc != COMBA_OK) return rc;

@@ -462,15 +462,21 @@ __device__ __forceinline__ float sumsq8(const u32x4& w) {
 
 // ---- kernel -------------------------------------------------------------------------------
 
-template <int K, int V, int VT, typename OutT, bool NORM, bool SO>
-__global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
+// The kernel body. PAIR (a state-only pass for the segment-parallel forward,
+// K == V): a second group of four consumer wavefronts (waves 8-11) runs the
+// same chunks from the identity with v = 0 over K state rows and writes its
+// final state to sf2, the segment's K x K map, while waves 0-3 form the
+// segment-end state from zero; the producers' work serves both groups.
+template <int K, int V, int VT, typename OutT, bool NORM, bool SO, bool PAIR>
+__device__ __forceinline__ void chunk_fwd_bf16_body(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
     const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
-    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck) {
+    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck, float* __restrict__ sf2) {
   static_assert(VT == 64, "four consumer wavefronts of 16 channels");
-  constexpr int NVT = V / VT;
+  static_assert(!PAIR || (SO && K == V), "the paired pass is state-only, with K == V");
+  constexpr int NVT = V / VT, NT = PAIR ? 768 : 512;
   __shared__ SmemV3<K, VT> sm;
 
   const int tid = threadIdx.x;
@@ -492,7 +498,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 
   // Zero both buffers' T / P storage once: the upper blocks (0,1), (2,3) are
   // read by the 32-wide reduction steps and never written.
-  for (int e = tid; e < kTP; e += 512) {
+  for (int e = tid; e < kTP; e += NT) {
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       sm.buf[bb].Th[e] = 0;
@@ -508,7 +514,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
   }
   __syncthreads();
 
-  if (wave >= 4) {
+  if (wave >= 4 && (!PAIR || wave < 8)) {
     // ======================= producers: prepare chunk it in iteration it =======================
     const int p = wave - 4;
     const int ptid = tid - 256;
@@ -664,7 +670,10 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     }
   } else {
     // ======================= consumers: run chunk it-1 in iteration it =======================
-    const int vloc = wave * 16 + l16;
+    // Group 1 of a paired pass: the identity-start, zero-v run over K state rows.
+    const bool grp1 = PAIR && wave >= 8;
+    const int cw = PAIR ? (wave & 3) : wave;  // consumer index within the group
+    const int vloc = cw * 16 + l16;
     const int vcol = vt * VT + vloc;
     // Byte offsets of this lane's four output rows (4 g + i) inside a 16-row
     // block, channel vcol; H * V elements separate consecutive tokens.
@@ -673,11 +682,11 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) ovoff[i] = ((4 * g + i) * hv + vcol) * static_cast<int>(sizeof(OutT));
     f32x4 hs[K / 16];
-    const int64_t srow = ((static_cast<int64_t>(n) * H + h) * V + vcol) * K;
+    const int64_t srow = ((static_cast<int64_t>(n) * H + h) * V + vcol) * K;  // (V == K when paired)
 #pragma unroll
     for (int kb = 0; kb < K / 16; ++kb) {
-      hs[kb] = s0 ? *reinterpret_cast<const f32x4*>(s0 + srow + 16 * kb + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (fusion & kModeIdentityInit) {
+      hs[kb] = s0 && !grp1 ? *reinterpret_cast<const f32x4*>(s0 + srow + 16 * kb + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+      if ((fusion & kModeIdentityInit) || grp1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) hs[kb][i] = (16 * kb + 4 * g + i == vcol) ? 1.f : 0.f;
       }
@@ -768,7 +777,7 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
         for (int r4 = 0; r4 < 4; ++r4) {
           const f32x4 bt = lds_f4(&bf.gl[0][16 * g + 4 * r4]);
           const f32x4 bx = lds_f4(&bf.gl[1][16 * g + 4 * r4]);
-          const f32x4 vv = v_frag<VT>(bf.Vv, r4, wave * 16, g, l16);
+          const f32x4 vv = grp1 ? f32x4{0.f, 0.f, 0.f, 0.f} : v_frag<VT>(bf.Vv, r4, cw * 16, g, l16);
 #pragma unroll
           for (int i = 0; i < 4; ++i) R[r4][i] = bt[i] * vv[i] - bx[i] * KH[r4][i];
         }
@@ -913,11 +922,35 @@ __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
       }
       __syncthreads();
     }
-    if (sf) {
+    float* const dst = grp1 ? sf2 : sf;
+    if (dst) {
 #pragma unroll
-      for (int kb = 0; kb < K / 16; ++kb) *reinterpret_cast<f32x4*>(sf + srow + 16 * kb + 4 * g) = hs[kb];
+      for (int kb = 0; kb < K / 16; ++kb) *reinterpret_cast<f32x4*>(dst + srow + 16 * kb + 4 * g) = hs[kb];
     }
   }
+}
+
+template <int K, int V, int VT, typename OutT, bool NORM, bool SO>
+__global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
+    const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
+    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck) {
+  chunk_fwd_bf16_body<K, V, VT, OutT, NORM, SO, false>(q, k, v, alpha, beta, d, s0, cu_seqlens, order, T, H, Hk, N,
+                                                        o, sf, fusion, hck, nullptr);
+}
+
+// State-only pass of the segment-parallel forward that forms both the
+// segment-end states (sf) and the segment maps (sf2) in one launch.
+template <int K, int VT, bool NORM>
+__global__ __launch_bounds__(768) void chunk_fwd_bf16_pair_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
+    const int32_t* __restrict__ cu_seqlens, int T, int H, int Hk, int N, float* __restrict__ sf, unsigned fusion,
+    float* __restrict__ sf2) {
+  chunk_fwd_bf16_body<K, K, VT, u16, NORM, true, true>(q, k, v, alpha, beta, d, nullptr, cu_seqlens, nullptr, T, H,
+                                                       Hk, N, nullptr, sf, fusion, nullptr, sf2);
 }
 
 template <int K, int V, typename OutT, bool NORM, bool SO>
@@ -927,6 +960,15 @@ static hipError_t launch_bf16_t(const FwdArgs& a, hipStream_t st) {
   chunk_fwd_bf16_kernel<K, V, VT, OutT, NORM, SO><<<xcd_grid(units, NVT), 512, 0, st>>>(
       static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.alpha,
       a.beta, a.d, a.s0, a.cu_seqlens, a.order, a.T, a.H, a.Hk, a.N, static_cast<OutT*>(a.o), a.sf, a.fusion, a.hck);
+  return hipGetLastError();
+}
+
+template <int K, bool NORM>
+static hipError_t launch_pair_t(const FwdArgs& a, float* sf2, hipStream_t st) {
+  constexpr int VT = 64, NVT = K / VT;
+  chunk_fwd_bf16_pair_kernel<K, VT, NORM><<<xcd_grid(a.N * a.H, NVT), 768, 0, st>>>(
+      static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), static_cast<const u16*>(a.v), a.alpha, a.beta,
+      a.d, a.cu_seqlens, a.T, a.H, a.Hk, a.N, a.sf, a.fusion, sf2);
   return hipGetLastError();
 }
 
@@ -942,6 +984,13 @@ template <int K, int V>
 static hipError_t launch_bf16_kv(const FwdArgs& a, hipStream_t st) {
   if (a.fusion & kFuseQkL2Norm) return launch_bf16_n<K, V, true>(a, st);
   return launch_bf16_n<K, V, false>(a, st);
+}
+
+hipError_t launch_chunk_bf16_pair(const FwdArgs& a, float* sf2, hipStream_t st) {
+  if (a.K != a.V || (a.K != 64 && a.K != 128)) return hipErrorInvalidValue;
+  const bool norm = (a.fusion & kFuseQkL2Norm) != 0;
+  if (a.K == 128) return norm ? launch_pair_t<128, true>(a, sf2, st) : launch_pair_t<128, false>(a, sf2, st);
+  return norm ? launch_pair_t<64, true>(a, sf2, st) : launch_pair_t<64, false>(a, sf2, st);
 }
 
 hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st) {

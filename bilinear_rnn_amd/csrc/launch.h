@@ -72,6 +72,9 @@ struct BwdArgs {
 hipError_t launch_recurrent(const FwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bwd(const BwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st);
+// State-only pass over bf16 inputs (K == V) that writes the final states from
+// a.s0 == null to a.sf and, from the identity with v = 0, the K x K maps to sf2.
+hipError_t launch_chunk_bf16_pair(const FwdArgs& a, float* sf2, hipStream_t st);
 hipError_t launch_chunk_fp32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_varlen_order(const int32_t* cu_seqlens, int N, int32_t* order, hipStream_t st);
 hipError_t launch_segment_bounds(int B, int T, int L, int S, int32_t* cu, hipStream_t st);
