@@ -24,6 +24,12 @@
 // Double-buffered LDS holds everything a consumer reads for one chunk; one
 // workgroup barrier per chunk hands a buffer from producers to consumers.
 //
+// Instantiations: output in bf16 or fp32; q / k normalised in the kernel or
+// not; a state-only form (no Q K^T, P or output stage) for passes that need
+// final states only; and chunk_fwd_bf16_pair_kernel, a state-only form with a
+// second group of four consumers (waves 8-11) that runs the same chunks from
+// the identity with v = 0, for the segment-parallel forward's segment maps.
+//
 // Precision: q, k, v are exact bf16 operands. Every other operand (h, T1, T2,
 // A21, P, R, Ubar) is split into a high and a low bf16 part; the products
 // hi*hi + hi*lo + lo*hi (or hi + lo against an exact operand) accumulate in
