@@ -3,7 +3,8 @@
 Each check is an independent route to the same number: a hand-derived
 example, an explicit-matrix brute force, an adjoint (backward) algorithm,
 closed forms of special cases, an autograd gradient step on the delta loss,
-and invariants (linearity, row slicing, packing, resumption, a norm bound).
+and invariants (linearity, row slicing, packing, resumption, the composition of
+segment maps, a norm bound).
 Every pin runs against both oracle implementations (numpy and C).
 """
 import os
@@ -285,6 +286,30 @@ def test_split_and_resume(impl):
     ob, fb = run(impl, q[:, b], k[:, b], v[:, b], alpha[:, b], beta[:, b], d, fa)
     np.testing.assert_allclose(np.concatenate([oa, ob], axis=1), o, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(fb, f, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("impl", IMPLS)
+def test_segment_maps_compose_to_the_unsplit_run(impl):
+    """The segment-parallel scheme on the oracle: the state after a segment is
+    X Phi_j + b_j, with b_j the run from a zero state and Phi_j the run from the
+    identity with v = 0 (a K x K state); chaining X_{j+1} = X_j Phi_j + b_j from
+    S0 gives the unsplit final state, and each segment rerun from its X_j gives
+    the unsplit outputs (the write-up's state-transition form, the Comba section)."""
+    B, T, H, K, V = 2, 61, 3, 8, 5
+    q, k, v, alpha, beta, d, S0 = small_case(21, B=B, T=T, H=H, K=K, V=V)
+    o, f = run(impl, q, k, v, alpha, beta, d, S0)
+    bounds = [0, 17, 18, 40, 61]  # uneven segments, one of a single token
+    X = S0.copy()
+    for a, e in zip(bounds[:-1], bounds[1:]):
+        sl = slice(a, e)
+        seg = (q[:, sl], k[:, sl])
+        o_j, _ = run(impl, *seg, v[:, sl], alpha[:, sl], beta[:, sl], d, X)
+        np.testing.assert_allclose(o_j, o[:, sl], rtol=1e-12, atol=1e-13)
+        _, b_j = run(impl, *seg, v[:, sl], alpha[:, sl], beta[:, sl], d, np.zeros_like(S0))
+        eye = np.broadcast_to(np.eye(K), (B, H, K, K)).copy()
+        _, phi_j = run(impl, *seg, np.zeros((B, e - a, H, K)), alpha[:, sl], beta[:, sl], d, eye)
+        X = X @ phi_j + b_j
+    np.testing.assert_allclose(X, f, rtol=1e-12, atol=1e-13)
 
 
 # --- chunk-wise form --------------------------------------------------------------------
