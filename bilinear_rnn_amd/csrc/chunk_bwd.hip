@@ -20,7 +20,9 @@
 //           - colsum(dA (.) A)_t - e^(Gn - G_t) (K dh)_t . Ubar_t
 //   dGx_t = rowsum(dA (.) A)_t - b1_t (K h)_t . dR_t
 //   dGn   = e^Gn <h, dh> + sum_t e^(Gn - G_t) (K dh)_t . Ubar_t   (added to dG at the last row)
-//   dlog(alpha_t) = -dGx_t + sum_{s >= t} (dG_s + dGx_s),   dalpha_t = dlog(alpha_t) / alpha_t.
+//   dlog(alpha_t) = -dGx_t + sum_{s >= t} (dG_s + dGx_s),   dalpha_t = dlog(alpha_t) / alpha_t,
+// evaluated in the equivalent form without cancelling terms (grad_scalars), so
+// that alpha_t near zero keeps dalpha_t accurate.
 // An fp64 prototype of exactly these formulas matches the reverse-mode oracle
 // of the token recurrence to 1e-15.
 //
@@ -402,36 +404,47 @@ struct alignas(16) SmemGrad {
     } p;
   } u;
   ChunkGates gt;
-  float vec[10][64];
+  float vec[12][64];
   float red[16];
 };
 
 // Per-token scalars of a chunk, run by one wavefront (lane = row). vec rows:
-// 1 sum dR.(v - e^Gx K h), 2 sum (K h).dR, 3 sum (K dh).Ubar, 4 / 6 row / column
-// sums of dP (.) P, 5 / 7 row sums of W (.) KK / column sums of beta W (.) KK,
-// 8 + 9 the two halves of (q~ h).dO; red[0..7] partial <h, dh>, red[8..15]
-// partial dd.
+// 1 sum dR.(v - e^Gx K h), 2 sum (K h).dR, 3 sum (K dh).Ubar, 5 row sums of
+// W (.) k_t.k_s, 8 + 9 the two halves of (q~ h).dO, 10 and 11 the rectangle
+// sums R_P(t) = sum_{s>=t, r<t} (dP (.) P)[s][r] and R_A(t) = sum_{s>t, r<t}
+// (dA (.) A)[s][r]; red[0..7] partial <h, dh>, red[8..15] partial dd.
+//
+// The gradient of log alpha_t is a reverse cumulative sum of dG + dGx over the
+// chunk (see the formulas above), but the row and column sums in it cancel
+// wherever both indices are >= t, and the t2 terms against dGn. Written
+// without those cancelling parts, every remaining term carries the factor
+// alpha_t, so a tiny alpha_t leaves no catastrophic cancellation:
+//   dlog_t = sum_{s>=t} e^G_s (q~ h)_s.dO_s + R_P(t) + R_A(t) + e^Gn <h, dh>
+//            + sum_{s<t} e^(Gn - G_s) (K dh)_s.Ubar_s - sum_{s>t} b1_s (K h)_s.dR_s
+// (exclusive sums formed directly, never as an inclusive sum minus its term).
 __device__ __forceinline__ void grad_scalars(const ChunkGates& gt, const float (*vec)[64], const float* red, int lane,
                                              int nrows, int64_t tok0, int H, float* dalpha, float* dbeta,
                                              float* dd_out) {
   const int t = lane;
   float hd = 0.f;
   for (int w = 0; w < 8; ++w) hd += red[w];
-  const float be = gt.beta[t], b1 = gt.bEGx[t];
+  const float x1 = gt.EG[t] * (vec[8][t] + vec[9][t]);
   const float t2 = gt.EGnG[t] * vec[3][t];
-  const float sqh = vec[8][t] + vec[9][t];
-  float dG = gt.EG[t] * sqh + vec[4][t] - vec[6][t] - vec[7][t] - t2;
-  const float dGx = be * vec[5][t] - b1 * vec[2][t];
-  float sum_t2 = t2;
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) sum_t2 += __shfl_xor(sum_t2, m, kWave);
-  if (t == 63) dG += gt.EG[63] * hd + sum_t2;  // dGn
-  // reverse inclusive sum of dG + dGx over the chunk
-  const float x = dG + dGx;
-  const float xr = __shfl(x, 63 - t, kWave);
-  const float sr = wave_inclusive_scan(xr, t);
-  const float rev = __shfl(sr, 63 - t, kWave);
-  const float dlog = rev - dGx;
+  const float x3 = gt.bEGx[t] * vec[2][t];
+  // sum_{s>=t} x1 and sum_{s>t} x3: scans over the reversed lane order. Every
+  // cross-lane read runs in all 64 lanes (never under a lane condition, where
+  // an inactive source lane would not supply its value); the exclusive sums
+  // are the inclusive ones moved up by one lane, lane 0 then set to zero.
+  const float s1 = wave_inclusive_scan(__shfl(x1, 63 - t, kWave), t);
+  const float s3 = wave_inclusive_scan(__shfl(x3, 63 - t, kWave), t);
+  const float s3up = __shfl_up(s3, 1, kWave);
+  const float s3x = t == 0 ? 0.f : s3up;  // reversed exclusive
+  const float suf1 = __shfl(s1, 63 - t, kWave), suf3 = __shfl(s3x, 63 - t, kWave);
+  // sum_{s<t} t2
+  const float p2 = wave_inclusive_scan(t2, t);
+  const float p2up = __shfl_up(p2, 1, kWave);
+  const float pre2 = t == 0 ? 0.f : p2up;
+  const float dlog = suf1 + vec[10][t] + vec[11][t] + gt.EG[63] * hd + pre2 - suf3;
   if (t < nrows) {
     const int64_t off = tok0 + static_cast<int64_t>(t) * H;
     dbeta[off] = vec[5][t] + vec[1][t];
@@ -441,6 +454,50 @@ __device__ __forceinline__ void grad_scalars(const ChunkGates& gt, const float (
     float s2 = 0.f;
     for (int w = 0; w < 8; ++w) s2 += red[8 + w];
     *dd_out = s2;
+  }
+}
+
+// The rectangle sums of grad_scalars from two 64 x 64 fp32 products in LDS
+// (row stride kLdT): X = dP (.) P and Z = W (.) k_t.k_s, whose rows scaled by
+// beta_s give Y = dA (.) A. Two passes by the first 128 threads, with a
+// workgroup barrier between them:
+//   rect_row_prefix: row s of X (threads 0-63) or of Y (64-127) becomes its
+//     exclusive prefix sum_{r<t}, formed by running sums; the Z threads also
+//     write the plain row sum of Z (vec row 5, for dbeta);
+//   rect_column_sums: R_P(t) = sum_{s>=t} X'[s][t], R_A(t) = sum_{s>t} Y'[s][t].
+__device__ __forceinline__ void rect_row_prefix(float (*X)[kLdT], float (*Z)[kLdT], const float* beta,
+                                                float (*vec)[64], int tid) {
+  if (tid < 64) {
+    float acc = 0.f;
+    for (int r = 0; r < 64; ++r) {
+      const float x = X[tid][r];
+      X[tid][r] = acc;
+      acc += x;
+    }
+  } else if (tid < 128) {
+    const int s_ = tid - 64;
+    const float b = beta[s_];
+    float acc = 0.f, raw = 0.f;
+    for (int r = 0; r < 64; ++r) {
+      const float z = Z[s_][r];
+      Z[s_][r] = acc;
+      acc += b * z;
+      raw += z;
+    }
+    vec[5][s_] = raw;
+  }
+}
+__device__ __forceinline__ void rect_column_sums(const float (*X)[kLdT], const float (*Y)[kLdT], float (*vec)[64],
+                                                 int tid) {
+  if (tid < 64) {
+    float acc = 0.f;
+    for (int s_ = tid; s_ < 64; ++s_) acc += X[s_][tid];
+    vec[10][tid] = acc;
+  } else if (tid < 128) {
+    const int t = tid - 64;
+    float acc = 0.f;
+    for (int s_ = t + 1; s_ < 64; ++s_) acc += Y[s_][t];
+    vec[11][t] = acc;
   }
 }
 
@@ -695,25 +752,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
     }
   }
   __syncthreads();
-  // row and column sums (fixed order)
-  if (tid < 64) {
-    float rp = 0.f, rx = 0.f;
-    for (int s_ = 0; s_ < 64; ++s_) {
-      rp += sm.Pm[tid][s_];
-      rx += sm.u.p.X[tid][s_];
-    }
-    sm.vec[4][tid] = rp;
-    sm.vec[5][tid] = rx;
-  } else if (tid < 128) {
-    const int s_ = tid - 64;
-    float cp = 0.f, cx = 0.f;
-    for (int t = 0; t < 64; ++t) {
-      cp += sm.Pm[t][s_];
-      cx += sm.gt.beta[t] * sm.u.p.X[t][s_];
-    }
-    sm.vec[6][s_] = cp;
-    sm.vec[7][s_] = cx;
-  }
+  // first pass of the rectangle sums (dP (.) P in Pm, W (.) k_t.k_s in X)
+  rect_row_prefix(sm.Pm, sm.u.p.X, sm.gt.beta, sm.vec, tid);
   // dq, dk of the blocks (tb, KBW hw + cb)
   f32x4 xq[KBW], xk[KBW];
 #pragma unroll
@@ -763,6 +803,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
   for (int m = 1; m < kWave; m <<= 1) ddp += __shfl_xor(ddp, m, kWave);
   __syncthreads();
   if (lane == 0) sm.red[8 + wave] = ddp;
+  rect_column_sums(sm.Pm, sm.u.p.X, sm.vec, tid);
   __syncthreads();
   if (wave == 0) grad_scalars(sm.gt, sm.vec, sm.red, lane, nrows, tok0, H, dalpha, dbeta, dd_part + slot * H + h);
 }
@@ -1132,7 +1173,7 @@ constexpr int kGbVT = 32;  // value channels per tile of the bf16 gradient kerne
 // hi / lo: Tinv and P ([t][s], s in perm32 order), the state and
 // state-gradient tiles ([channel][key], perm32) and R, Ubar, dUbar, dR
 // ([channel][token], perm32); after the value tiles, dP (.) M and beta W as
-// [s][t] (t in perm32 order) and partial row and column sums.
+// [s][t] (t in perm32 order), and dP (.) P and W (.) k_t.k_s in fp32.
 template <int K>
 struct alignas(16) SmemGradB {
   u16 Qc[64 * K], Kc[64 * K];
@@ -1146,12 +1187,12 @@ struct alignas(16) SmemGradB {
     } t;
     struct {
       u16 dPMh[64 * 64], dPMl[64 * 64], WBh[64 * 64], WBl[64 * 64];
-      float rows[2][2][64];  // per wave half: row sums of dP (.) P and W (.) k_t.k_s
-      float cols[4][2][64];  // per token block: column sums of dP (.) P and beta W (.) k_t.k_s
+      float dPP[64][kLdT];  // dP (.) P
+      float Z[64][kLdT];    // W (.) k_t.k_s
     } p;
   } u;
   ChunkGates gt;
-  float vec[10][64];
+  float vec[12][64];
   float red[16];
 };
 
@@ -1435,13 +1476,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     for (int cc = 0; cc < 2; ++cc)
       kkv[cc] = mfma16x16x32(a, lds8(&sm.Kc[swz<K>(16 * (2 * hw + cc) + l16, 32 * s_ + 8 * g)]), kkv[cc]);
   }
-  // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cc); the
-  // row sums (over s) and column sums (over t) of dP (.) P and W (.) k_t.k_s
-  // are reduced in registers: over this lane's two blocks and the 16 lanes of a
-  // row group for the rows, over its four rows and the four row groups for the
-  // columns, then per wavefront into LDS partials (summed in a fixed order).
-  f32x4 rowP{0.f, 0.f, 0.f, 0.f}, rowX{0.f, 0.f, 0.f, 0.f};
-  float colP[2], colX[2];
+  // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cc):
+  // dP (.) M and beta W as hi / lo bf16 for the products below, dP (.) P and
+  // W (.) k_t.k_s in fp32 for the rectangle sums
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int s_ = 16 * (2 * hw + cc) + l16;
@@ -1450,63 +1487,25 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     const f32x4 pv = tr4<64>(sm.Ph, 16 * tb, ps, g, l16) + tr4<64>(sm.Pl, 16 * tb, ps, g, l16);
     const float Gs = sm.gt.G[s_];
     f32x4 dpm, wb;
-    colP[cc] = colX[cc] = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * tb + 4 * g + i;
       const float M = s_ <= t ? __expf(fminf(sm.gt.G[t] - Gs, 0.f)) : 0.f;
       const float E = s_ < t ? __expf(fminf(sm.gt.Gx[t] - Gs, 0.f)) : 0.f;
       const float dpv = s_ <= t ? accP[cc][i] : 0.f, dav = s_ < t ? -accA[cc][i] : 0.f;
-      const float w = dav * E, be = sm.gt.beta[t];
-      const float dpp = dpv * pv[i], xx = w * kkv[cc][i];
-      rowP[i] += dpp;
-      rowX[i] += xx;
-      colP[cc] += dpp;
-      colX[cc] += be * xx;
+      const float w = dav * E;
+      sm.u.p.dPP[t][s_] = dpv * pv[i];
+      sm.u.p.Z[t][s_] = w * kkv[cc][i];
       dpm[i] = dpv * M;
-      wb[i] = be * w;
+      wb[i] = sm.gt.beta[t] * w;
     }
     const int off = swz<64>(s_, perm_col(16 * tb + 4 * g));
     put_split4(sm.u.p.dPMh, sm.u.p.dPMl, off, dpm);
     put_split4(sm.u.p.WBh, sm.u.p.WBl, off, wb);
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      rowP[i] += __shfl_xor(rowP[i], m, kWave);
-      rowX[i] += __shfl_xor(rowX[i], m, kWave);
-    }
-  }
-#pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-#pragma unroll
-    for (int m = 16; m < kWave; m <<= 1) {
-      colP[cc] += __shfl_xor(colP[cc], m, kWave);
-      colX[cc] += __shfl_xor(colX[cc], m, kWave);
-    }
-  }
-  if (l16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sm.u.p.rows[hw][0][16 * tb + 4 * g + i] = rowP[i];
-      sm.u.p.rows[hw][1][16 * tb + 4 * g + i] = rowX[i];
-    }
-  }
-  if (g == 0) {
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      sm.u.p.cols[tb][0][16 * (2 * hw + cc) + l16] = colP[cc];
-      sm.u.p.cols[tb][1][16 * (2 * hw + cc) + l16] = colX[cc];
-    }
-  }
   __syncthreads();
-  if (tid < 64) {
-    sm.vec[4][tid] = sm.u.p.rows[0][0][tid] + sm.u.p.rows[1][0][tid];
-    sm.vec[5][tid] = sm.u.p.rows[0][1][tid] + sm.u.p.rows[1][1][tid];
-    sm.vec[6][tid] = (sm.u.p.cols[0][0][tid] + sm.u.p.cols[1][0][tid]) + (sm.u.p.cols[2][0][tid] + sm.u.p.cols[3][0][tid]);
-    sm.vec[7][tid] = (sm.u.p.cols[0][1][tid] + sm.u.p.cols[1][1][tid]) + (sm.u.p.cols[2][1][tid] + sm.u.p.cols[3][1][tid]);
-  }
+  // first pass of the rectangle sums (threads 0-127; the products below do not read these tiles)
+  rect_row_prefix(sm.u.p.dPP, sm.u.p.Z, sm.gt.beta, sm.vec, tid);
   // dq, dk of the blocks (tb, KBW hw + cc):
   //   dq = diag(e^G) dO h^T + (dP (.) M) K
   //   dk = diag(e^(Gn - G)) Ubar dh^T - diag(b1) dR h^T + diag(beta) W K + (dP (.) M)^T q
@@ -1572,6 +1571,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   for (int m = 1; m < kWave; m <<= 1) ddp += __shfl_xor(ddp, m, kWave);
   __syncthreads();
   if (lane == 0) sm.red[8 + wave] = ddp;
+  rect_column_sums(sm.u.p.dPP, sm.u.p.Z, sm.vec, tid);
   __syncthreads();
   if (wave == 0) grad_scalars(sm.gt, sm.vec, sm.red, lane, nrows, tok0, H, dalpha, dbeta, dd_part + slot * H + h);
 }

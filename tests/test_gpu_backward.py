@@ -136,6 +136,24 @@ def test_backward_without_final_state_gradient():
     check(run_bwd(inp, do, do_bits, None), oracle_bwd(inp, do, None), inp)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_backward_extreme_gates(dtype):
+    """alpha from 1e-6 to exactly 1 and beta exactly 0 and 1, mixed within every
+    chunk (in-chunk decay products far below fp32's range)."""
+    base = wl("layer_340m", K=64, V=64, B=2, H=2) if dtype == "bf16" else wl("tiny_fp32", B=2, H=2)
+    inp = make_inputs(base, T=150, s0_std=0.05, seed=85)
+    rng = np.random.default_rng(86)
+    shape = inp.alpha.shape
+    alpha = np.choose(rng.integers(0, 4, shape), [np.full(shape, 1e-6), np.ones(shape),
+                                                  rng.uniform(0.0, 1.0, shape), np.full(shape, 0.5)])
+    beta = np.choose(rng.integers(0, 3, shape), [np.zeros(shape), np.ones(shape), rng.uniform(0.0, 1.0, shape)])
+    inp = dataclasses.replace(inp, alpha=alpha.astype(np.float32), beta=beta.astype(np.float32))
+    do, do_bits, dsf = cotangents(inp, 87)
+    got = run_bwd(inp, do, do_bits, dsf)
+    assert all(np.isfinite(x).all() for x in got.values())
+    check(got, oracle_bwd(inp, do, dsf), inp)
+
+
 def test_backward_deterministic():
     inp = make_inputs(wl("layer_340m", B=2, H=2), T=333, s0_std=0.02, seed=81)
     do, do_bits, dsf = cotangents(inp, 82)

@@ -84,6 +84,28 @@ def test_bf16_shapes_ragged(K, V, T, s0):
     assert rel_l2(s32, rs) <= GATE_BF16_IN_FP32_OUT, rel_l2(s32, rs)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_extreme_gates(dtype):
+    """Decays and write strengths at their limits: alpha from 1e-6 (the state
+    forgotten within a token, in-chunk decay products far below fp32's range)
+    to exactly 1 (no decay), beta exactly 0 and 1, mixed within every chunk;
+    chunk and recurrent paths against the oracle."""
+    base = wl("layer_340m", K=64, V=64, B=2, H=2) if dtype == "bf16" else wl("tiny_fp32", B=2, H=2)
+    inp = make_inputs(base, T=200, s0_std=0.05, seed=41)
+    rng = np.random.default_rng(42)
+    shape = inp.alpha.shape
+    alpha = np.choose(rng.integers(0, 4, shape), [np.full(shape, 1e-6), np.ones(shape),
+                                                  rng.uniform(0.0, 1.0, shape), np.full(shape, 0.5)])
+    beta = np.choose(rng.integers(0, 3, shape), [np.zeros(shape), np.ones(shape), rng.uniform(0.0, 1.0, shape)])
+    inp = dataclasses.replace(inp, alpha=alpha.astype(np.float32), beta=beta.astype(np.float32))
+    ro, rs = oracle_of(inp)
+    gate = GATE_BF16 if dtype == "bf16" else GATE_FP32
+    for o, s in (run_chunk(inp), run_step(inp)):
+        assert np.isfinite(o).all() and np.isfinite(s).all()
+        assert rel_l2(o, ro) <= gate, rel_l2(o, ro)
+        assert rel_l2(s, rs) <= gate, rel_l2(s, rs)
+
+
 def test_layer_340m_reduced_batch():
     """340M layer shapes (K = V = 128, H = 16, T = 2048), one batch row."""
     inp = make_inputs(WORKLOADS["layer_340m"], B=1)
