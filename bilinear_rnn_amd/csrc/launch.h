@@ -56,9 +56,9 @@ struct BwdArgs {
   float* hck;                 // chunk incoming states [slots, H, V, K] (from the forward pass)
   float* dhck;                // chunk outgoing-state gradients [slots, H, V, K]
   float* dd_part;             // [slots, H]
-  float* Tg;                  // per chunk and head: Tinv, P and k_t.k_s, fp32 64 x 64 each
+  float* Tg;                  // per chunk and head: Tinv, P and (fp32 inputs) k_t.k_s, fp32 64 x 64 each
   float* Pg;
-  float* KKg;
+  float* KKg;                 // written and read for fp32 inputs only
   float* Gg;                  // per chunk and head: the chunk's decay gates, fp32 7 x 64 (see ChunkGates)
   float* dq;                  // [B, T, H, K] fp32
   float* dk;
