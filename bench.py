@@ -20,7 +20,8 @@ Counter calibration: run under `rocprofv3 --pmc FETCH_SIZE` and again under
 `--pmc WRITE_SIZE` with --calibrate-copy (a plain 256 MiB device-to-device
 copy follows the timed work), then `python bench.py --record-traffic
 <fetch_dir> <write_dir>` turns the two counter tables into the HBM bytes per
-chunk-kernel launch, scaled by what the same counter reads for the copy.
+launch of the chunk kernel and of the decode kernel, scaled by what the same
+counter reads for the copy.
 """
 import argparse
 import hashlib
@@ -84,19 +85,24 @@ def chunk_bwd_algorithmic(B, T, H, K, V):
 FWD_SOURCES = ("chunk_fwd_bf16.hip", "chunk_common.h", "device_common.h", "launch.h")
 
 
-def kernel_source_hash():
+# the sources the counted decode kernel is compiled from
+DECODE_SOURCES = ("recurrent_step.hip", "device_common.h", "launch.h")
+
+
+def kernel_source_hash(files=FWD_SOURCES):
     csrc = os.path.join(ROOT, "bilinear_rnn_amd", "csrc")
     h = hashlib.sha256()
-    for f in FWD_SOURCES:
+    for f in files:
         h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(src_hash):
-    """HBM bytes per launch of the chunk kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
+def measured_traffic(src_hash, path=None):
+    """HBM bytes per launch of a counted kernel (the chunk kernel unless
+    another summary is named) from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source."""
     try:
-        rec = json.load(open(COUNTERS_JSON))
+        rec = json.load(open(path or COUNTERS_JSON))
     except (OSError, ValueError):
         return None
     if rec.get("kernel_source_hash") != src_hash:
@@ -106,6 +112,7 @@ def measured_traffic(src_hash):
 
 COPY_CAL_BYTES = 256 << 20
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "chunk_fwd_bf16_layer_1p3b_counters.json")
+DECODE_COUNTERS_JSON = os.path.join(ROOT, "profiles", "recurrent_decode_counters.json")
 
 
 def calibration_copy(torch, dev):
@@ -134,16 +141,26 @@ def _counter_rows(d):
     return rows
 
 
-def _kernel_and_copy(rows, counter):
-    """Mean counter value (KiB per dispatch) of the chunk kernel, and of the
+def _is_plain_chunk(name):
+    # the plain instantiation: no in-kernel normalisation, not state-only
+    return "chunk_fwd_bf16_kernel<" in name and "unsigned short, false, false>" in name
+
+
+def _is_decode(name):
+    return "recurrent_kernel<" in name
+
+
+def _kernel_and_copy(rows, counter, is_kernel=_is_plain_chunk):
+    """Mean counter value (KiB per dispatch) of the counted kernel, and of the
     calibration copy: the one kernel dispatched exactly three times after the
-    last chunk-kernel dispatch."""
+    last dispatch of any counted kernel (chunk or decode)."""
     import collections
     rows = [r for r in rows if r["Counter_Name"] == counter]
-    # the plain (unfused) instantiation only: the fused one ends its template list with "true>"
-    is_chunk = lambda r: "chunk_fwd_bf16_kernel" in r["Kernel_Name"] and "true>" not in r["Kernel_Name"]
-    ker = [float(r["Counter_Value"]) for r in rows if is_chunk(r)]
-    last = max(int(r["Dispatch_Id"]) for r in rows if is_chunk(r))
+    is_ker = lambda r: is_kernel(r["Kernel_Name"])
+    ker = [float(r["Counter_Value"]) for r in rows if is_ker(r)]
+    if not ker:
+        return None
+    last = max(int(r["Dispatch_Id"]) for r in rows if _is_plain_chunk(r["Kernel_Name"]) or _is_decode(r["Kernel_Name"]))
     groups = collections.defaultdict(list)
     for r in rows:
         if int(r["Dispatch_Id"]) > last:
@@ -156,14 +173,32 @@ def _kernel_and_copy(rows, counter):
 
 
 def record_traffic(fetch_dir, write_dir):
-    """Write the calibrated per-launch HBM traffic of the chunk kernel."""
-    kf, nkf, cf, ncf, cname = _kernel_and_copy(_counter_rows(fetch_dir), "FETCH_SIZE")
-    kw, nkw, cw, ncw, _ = _kernel_and_copy(_counter_rows(write_dir), "WRITE_SIZE")
+    """Write the calibrated per-launch HBM traffic of the chunk kernel and, if
+    the counted run had decode steps, of the decode kernel."""
+    frows, wrows = _counter_rows(fetch_dir), _counter_rows(write_dir)
+    _record_one(frows, wrows, _is_plain_chunk, COUNTERS_JSON,
+                "chunk_fwd_bf16_kernel<128,128,64> on layer_1p3b (B=8 T=4096 H=16 K=V=128)",
+                kernel_source_hash(), chunk_fwd_algorithmic(8, 4096, 16, 128, 128)[0])
+    from bilinear_rnn_amd.inputs import WORKLOADS
+    wd = WORKLOADS["decode"]
+    ht = wd.B * wd.H
+    _record_one(frows, wrows, _is_decode, DECODE_COUNTERS_JSON,
+                f"recurrent_kernel<{wd.K},{wd.V},32,bf16,bf16> on the decode workload ({wd.B} x {wd.H} heads, K={wd.K} V={wd.V})",
+                kernel_source_hash(DECODE_SOURCES), 2 * ht * wd.V * wd.K * 4 + ht * (2 * wd.K * 2 + 2 * wd.V * 2 + 8))
+
+
+def _record_one(frows, wrows, is_kernel, path, label, src_hash, nbytes):
+    got_f, got_w = _kernel_and_copy(frows, "FETCH_SIZE", is_kernel), _kernel_and_copy(wrows, "WRITE_SIZE", is_kernel)
+    if got_f is None or got_w is None:
+        print(f"no dispatches of {label.split()[0]} in the counted runs: {os.path.basename(path)} not written")
+        return
+    kf, nkf, cf, ncf, cname = got_f
+    kw, nkw, cw, ncw, _ = got_w
     f_scale = COPY_CAL_BYTES / (cf * 1024.0)   # counter KiB -> true bytes, from the copy's read side
     w_scale = COPY_CAL_BYTES / (cw * 1024.0)
     rec = {
-        "kernel": "chunk_fwd_bf16_kernel<128,128,64> on layer_1p3b (B=8 T=4096 H=16 K=V=128)",
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel": label,
+        "kernel_source_hash": src_hash,
         "fetch_kib_per_dispatch": kf, "write_kib_per_dispatch": kw,
         "kernel_dispatches": [nkf, nkw],
         "copy_kernel": cname, "copy_bytes": COPY_CAL_BYTES,
@@ -173,10 +208,9 @@ def record_traffic(fetch_dir, write_dir):
         "hbm_write_bytes_per_launch": kw * 1024.0 * w_scale,
     }
     rec["hbm_bytes_per_launch"] = rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
-    nbytes, _ = chunk_fwd_algorithmic(8, 4096, 16, 128, 128)
     rec["algorithmic_bytes_per_launch"] = nbytes
     rec["traffic_over_algorithmic"] = rec["hbm_bytes_per_launch"] / nbytes
-    with open(COUNTERS_JSON, "w") as f:
+    with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
     print(json.dumps(rec, indent=1))
@@ -340,7 +374,8 @@ def main():
         result["decode"] = {"workload": "decode", "B": wd.B, "H": wd.H, "K": wd.K, "V": wd.V,
                             "us_per_step": dms * 1e3, "GB/s": dbytes / (dms * 1e-3) / 1e9,
                             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                            "algorithmic_bytes": dbytes, "kernel": "recurrent_kernel<128,128,bf16,bf16>"}
+                            "algorithmic_bytes": dbytes, "kernel": "recurrent_kernel<128,128,32,bf16,bf16>",
+                            "traffic": measured_traffic(kernel_source_hash(DECODE_SOURCES), DECODE_COUNTERS_JSON)}
 
     if not args.no_fused:
         raw = make_inputs(w, raw=True)
