@@ -243,6 +243,62 @@ def time_loop(torch, fn, steps, warmup):
     return start.elapsed_time(end) / steps, wall
 
 
+def step_distribution(torch, fn, groups=30, per_group=10):
+    """Spread of the step time: `groups` runs of `per_group` back-to-back
+    steps, each run bracketed by its own events on the launch stream; the
+    median, p10 and p90 of the per-step time of a run (us). Reported beside
+    the timed mean, not used for it; runs of several steps keep the events'
+    own cost out of the figure."""
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(groups)]
+    torch.cuda.synchronize()
+    for g, (a, b) in enumerate(ev):
+        a.record(stream)
+        for i in range(per_group):
+            fn(g * per_group + i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 / per_group for a, b in ev])
+    return {"median": float(np.median(us)), "p10": float(np.percentile(us, 10)),
+            "p90": float(np.percentile(us, 90)), "runs": groups, "steps_per_run": per_group}
+
+
+PEAK_COPY_BYTES = 512 << 20     # twice the 256 MB last-level cache
+PEAK_PROBE_BLOCKS = 2048        # eight workgroups of four wavefronts per compute unit
+PEAK_PROBE_ITERS = 4096
+
+
+def measured_peaks(torch, comba, dev):
+    """The part's own ceilings, measured in the same run: HBM bandwidth of an
+    out-of-place and of an in-place elementwise scale over 512 MiB fp32
+    buffers, and the bf16 matrix-core rate of the library's MFMA loop."""
+    n = PEAK_COPY_BYTES // 4
+    src = torch.empty(n, dtype=torch.float32, device=dev).uniform_()
+    dst = torch.empty_like(src)
+    cms, _ = time_loop(torch, lambda i: torch.mul(src, 1.0, out=dst), 20, 5)
+    ims, _ = time_loop(torch, lambda i: src.mul_(1.0), 20, 5)
+    del src, dst
+    sink = torch.empty(PEAK_PROBE_BLOCKS * 256, dtype=torch.float32, device=dev)
+    flops = PEAK_PROBE_BLOCKS * PEAK_PROBE_ITERS * comba.api.PEAK_PROBE_FLOPS_PER_BLOCK_ITER
+    pms, _ = time_loop(torch, lambda i: comba.mfma_peak_probe(sink, PEAK_PROBE_ITERS), 10, 3)
+    del sink
+    return {"hbm_copy_GB/s": 2 * PEAK_COPY_BYTES / (cms * 1e-3) / 1e9,
+            "hbm_inplace_GB/s": 2 * PEAK_COPY_BYTES / (ims * 1e-3) / 1e9,
+            "mfma_bf16_TFLOP/s": flops / (pms * 1e-3) / 1e12,
+            "how": f"out-of-place and in-place fp32 scale of {PEAK_COPY_BYTES >> 20} MiB (bytes read + written); "
+                   f"comba_mfma_peak_probe, {PEAK_PROBE_BLOCKS} workgroups x {PEAK_PROBE_ITERS} iterations"}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, H, min_seconds=10.0):
     """fp64 C oracle on all host cores, whole-batch passes repeated until at
     least ``min_seconds`` of wall time (bounded: one pass is about half a
@@ -261,9 +317,22 @@ def cpu_baseline(inp, H, min_seconds=10.0):
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
+    # one core, on one batch row (all heads), repeated for at least 2 s
+    one = [a[:1] for a in args[:5]] + [args[5]]
+    p1 = 0
+    t1 = time.perf_counter()
+    while True:
+        oracle.comba_forward_c(*one, s0[:1], None, nthreads=1)
+        p1 += 1
+        d1 = time.perf_counter() - t1
+        if d1 >= 2.0:
+            break
     return {"value": passes * B * T / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{passes} passes over the whole batch B={B} T={T} H={H} K=V={inp.q.shape[3]}, "
-                      f"fp64 C oracle, {dt:.1f} s wall"}
+                      f"fp64 C oracle, {dt:.1f} s wall",
+            "cpu_model": _cpu_model(),
+            "single_core_tokens/s": p1 * T / d1,
+            "single_core_sample": f"{p1} passes over one batch row (T={T}, H={H}), {d1:.1f} s wall"}
 
 
 def main():
@@ -277,6 +346,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured copy / MFMA ceilings")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--no-shared-qk", action="store_true")
@@ -353,7 +423,14 @@ def main():
                            "gate": 2e-3},
         "kernel_source_hash": src_hash,
         "wall_s_timed": wall,
+        "step_us": step_distribution(torch, step),
     }
+
+    if not args.no_peaks:
+        peaks = measured_peaks(torch, comba, dev)
+        result["measured_peaks"] = peaks
+        result["roofline"]["frac_of_measured_hbm"] = achieved / max(peaks["hbm_copy_GB/s"], peaks["hbm_inplace_GB/s"])
+        result["mfma"]["frac_of_measured"] = flops / secs / 1e12 / peaks["mfma_bf16_TFLOP/s"]
 
     if not args.no_decode:
         wd = WORKLOADS["decode"]
@@ -375,7 +452,11 @@ def main():
                             "us_per_step": dms * 1e3, "GB/s": dbytes / (dms * 1e-3) / 1e9,
                             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                             "algorithmic_bytes": dbytes, "kernel": "recurrent_kernel<128,128,32,bf16,bf16>",
-                            "traffic": measured_traffic(kernel_source_hash(DECODE_SOURCES), DECODE_COUNTERS_JSON)}
+                            "traffic": measured_traffic(kernel_source_hash(DECODE_SOURCES), DECODE_COUNTERS_JSON),
+                            "step_us": step_distribution(torch, dstep)}
+        if "measured_peaks" in result:
+            result["decode"]["frac_of_measured_inplace"] = (dbytes / (dms * 1e-3) / 1e9
+                                                            / result["measured_peaks"]["hbm_inplace_GB/s"])
 
     if not args.no_fused:
         raw = make_inputs(w, raw=True)

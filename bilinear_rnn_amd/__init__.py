@@ -6,7 +6,7 @@ correction, as hand-written HIP kernels behind a C ABI (include/comba.h).
 This package is the thin Python binding over that library.
 """
 from .api import (CombaError, bwd_workspace_size, chunk_bwd, chunk_fwd, lib, library_path,  # noqa: F401
-                  recurrent_step, segmented_workspace_size, varlen_order, workspace_size)
+                  mfma_peak_probe, recurrent_step, segmented_workspace_size, varlen_order, workspace_size)
 
 __all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "recurrent_step", "varlen_order", "workspace_size", "segmented_workspace_size",
            "CombaError"]

@@ -32,7 +32,7 @@ EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_recurrent_step", "comba_recurrent_step_fused", "comba_recurrent_step_ex",
             "comba_chunk_fwd_segmented_workspace_size",
             "comba_chunk_fwd_segmented", "comba_chunk_bwd_workspace_size", "comba_chunk_bwd",
-            "comba_varlen_order")
+            "comba_varlen_order", "comba_mfma_peak_probe")
 
 
 class CombaError(RuntimeError):
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.comba_chunk_bwd.restype = i32
         L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
         L.comba_varlen_order.restype = i32
+        L.comba_mfma_peak_probe.argtypes = [fp, i32, i32, vp]
+        L.comba_mfma_peak_probe.restype = i32
         _lib = L
     return _lib
 
@@ -315,3 +317,17 @@ def varlen_order(cu_seqlens: torch.Tensor) -> torch.Tensor:
         stream = torch.cuda.current_stream(cu_seqlens.device).cuda_stream
         _check(lib().comba_varlen_order(_ptr(cu_seqlens), N, _ptr(order), ctypes.c_void_p(stream)))
     return order
+
+
+PEAK_PROBE_FLOPS_PER_BLOCK_ITER = 4 * 4 * 16384   # wavefronts x MFMAs per iteration x flops per MFMA
+
+
+def mfma_peak_probe(sink: torch.Tensor, iters: int) -> int:
+    """One launch of ``comba_mfma_peak_probe`` over ``sink.numel() // 256``
+    workgroups; returns the flops it performs."""
+    _require(sink, "sink", torch.float32)
+    blocks = sink.numel() // 256
+    with torch.cuda.device(sink.device):
+        stream = torch.cuda.current_stream(sink.device).cuda_stream
+        _check(lib().comba_mfma_peak_probe(_ptr(sink), blocks, int(iters), ctypes.c_void_p(stream)))
+    return blocks * iters * PEAK_PROBE_FLOPS_PER_BLOCK_ITER

@@ -6,6 +6,7 @@
 
 #include "comba.h"
 #include "launch.h"
+#include "measure.h"
 
 #define COMBA_API extern "C" __attribute__((visibility("default")))
 
@@ -400,4 +401,12 @@ COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs
   if (!cu_seqlens || !order) return fail(COMBA_ERR_INVALID_ARG, "cu_seqlens and order must be non-NULL");
   if (num_seqs < 1) return fail(COMBA_ERR_INVALID_ARG, "num_seqs must be >= 1");
   return launched(comba::launch_varlen_order(cu_seqlens, num_seqs, order, static_cast<hipStream_t>(stream)));
+}
+
+COMBA_API int32_t comba_mfma_peak_probe(float* sink, int32_t blocks, int32_t iters, void* stream) {
+  if (!sink) return fail(COMBA_ERR_INVALID_ARG, "sink must be non-NULL");
+  if (blocks < 1 || iters < 1) return fail(COMBA_ERR_INVALID_ARG, "blocks and iters must be >= 1");
+  if (static_cast<int64_t>(blocks) * comba::kPeakProbeThreads > INT_MAX)
+    return fail(COMBA_ERR_UNSUPPORTED, "blocks * 256 must fit 31 bits");
+  return launched(comba::launch_mfma_peak_probe(sink, blocks, iters, static_cast<hipStream_t>(stream)));
 }

@@ -294,6 +294,20 @@ int32_t comba_chunk_bwd(const void* q, const void* k, const void* v,
 int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,
                            void* stream);
 
+/*
+ * Measurement aid, not part of the recurrence: the matrix-core ceiling of the
+ * device it runs on, to set beside the published dense bf16 peak when the
+ * chunk kernels are rated against it. Launches `blocks` workgroups of four
+ * wavefronts; every wavefront runs `iters` iterations of four independent
+ * 16x16x32 bf16 MFMAs (16,384 flops each) on register operands, so one call
+ * performs blocks * 4 * iters * 4 * 16384 flops and reads no memory. It
+ * writes one float per thread to sink (device, blocks * 256 floats, owned by
+ * the caller; the values carry no meaning). Time it with events on `stream`.
+ * Errors: COMBA_ERR_INVALID_ARG for a NULL sink or blocks, iters < 1;
+ * COMBA_ERR_UNSUPPORTED when blocks * 256 exceeds 2^31 - 1.
+ */
+int32_t comba_mfma_peak_probe(float* sink, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

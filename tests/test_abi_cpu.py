@@ -186,6 +186,14 @@ def test_backward_rejects_bad_arguments(kw, code):
     assert api.last_error() != ""
 
 
+@pytest.mark.parametrize("sink,blocks,iters,code", [
+    (None, 1, 1, -1), (FAKE, 0, 1, -1), (FAKE, 1, 0, -1), (FAKE, -3, 5, -1), (FAKE, 1 << 30, 1, -2),
+])
+def test_mfma_peak_probe_rejects_bad_arguments(sink, blocks, iters, code):
+    assert comba.lib().comba_mfma_peak_probe(sink, blocks, iters, None) == code
+    assert api.last_error() != ""
+
+
 def test_backward_workspace_size():
     ws = comba.bwd_workspace_size
     # per chunk and head: two fp32 states, three fp32 64 x 64 matrices, seven
