@@ -52,8 +52,10 @@ int32_t check_args(const void* q, const void* k, const void* v, const float* alp
   const int64_t N = cu ? num_seqs : B;
   if (N * H * 2 > INT_MAX / 16)
     return fail(COMBA_ERR_UNSUPPORTED, "too many (sequence, head) pairs for one launch");
-  if (static_cast<int64_t>(H) * (K > V ? K : V) > (1 << 24))
-    return fail(COMBA_ERR_UNSUPPORTED, "H * max(K, V) above 2^24 (chunk offsets must fit 32 bits)");
+  // Byte offsets inside one 64-token chunk, 64 * H * max(K, V) * 4 with fp32
+  // rows, are 32-bit in the kernels.
+  if (static_cast<int64_t>(H) * (K > V ? K : V) > (1 << 22))
+    return fail(COMBA_ERR_UNSUPPORTED, "H * max(K, V) above 2^22 (chunk byte offsets must fit 31 bits)");
   if (s0 && sf && s0 != sf) {
     const char* s0b = reinterpret_cast<const char*>(s0);
     const char* sfb = reinterpret_cast<const char*>(sf);

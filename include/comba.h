@@ -35,7 +35,9 @@
  *   device-side preconditions (monotone cu_seqlens, alpha > 0) gives
  *   unspecified values but no out-of-bounds access.
  * - Supported shapes: K, V in {64, 128}; B, H >= 1; T >= 1 (T >= 0 with
- *   cu_seqlens). dtypes: COMBA_BF16 or COMBA_FP32 for q/k/v and for o.
+ *   cu_seqlens); H * max(K, V) <= 2^22 (up to 32768 heads of 128), else
+ *   COMBA_ERR_UNSUPPORTED. Tensors may exceed 4 GiB: token and state offsets
+ *   are 64-bit. dtypes: COMBA_BF16 or COMBA_FP32 for q/k/v and for o.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream). The
  *   call returns without synchronising and never allocates device memory.
  * - Errors detectable on the host (NULL required pointer, bad shape or dtype,

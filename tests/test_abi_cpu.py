@@ -101,6 +101,7 @@ def step_fused(**kw):
     (dict(B=0), -1), (dict(H=0), -1), (dict(T=0), -1), (dict(K=0), -1), (dict(V=-3), -1),
     (dict(idt=2), -1), (dict(odt=-1), -1),
     (dict(K=96), -2), (dict(V=32), -2), (dict(K=256), -2),
+    (dict(H=32769, K=128, V=128), -2), (dict(H=65537), -2), (dict(H=32769, K=64, V=128), -2),
     (dict(cu=FAKE, n=3, B=2), -1), (dict(cu=FAKE, n=0), -1), (dict(cu=FAKE, n=2, T=-1), -1),
     (dict(s0=ctypes.c_void_p(4096), sf=ctypes.c_void_p(4096 + 64)), -1),
 ])
@@ -179,7 +180,8 @@ def bwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(do=None), -1), (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1), (dict(da=None), -1),
     (dict(db=None), -1), (dict(dd=None), -1), (dict(q=None), -1), (dict(T=0), -1), (dict(idt=3), -1),
-    (dict(K=96), -2), (dict(cu=FAKE, n=0), -1), (dict(ws=None, wsb=0), -3), (dict(wsb=100), -3),
+    (dict(K=96), -2), (dict(H=32769, K=128, V=128), -2), (dict(cu=FAKE, n=0), -1), (dict(ws=None, wsb=0), -3),
+    (dict(wsb=100), -3),
 ])
 def test_backward_rejects_bad_arguments(kw, code):
     assert bwd(**kw) == code
