@@ -153,6 +153,10 @@ def _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype):
         N = B
     if initial_state is not None:
         _require(initial_state, "initial_state", torch.float32, (N, H, V, K))
+    for name, t in (("k", k), ("v", v), ("alpha", alpha), ("beta", beta), ("d", d),
+                    ("initial_state", initial_state), ("cu_seqlens", cu_seqlens)):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}, q on {q.device}: all tensors must share one device")
     out_dtype = q.dtype if out_dtype is None else out_dtype
     if out_dtype not in _DT:
         raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
