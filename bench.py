@@ -525,11 +525,30 @@ def main():
                             workspace=bws)
 
         bms, _ = time_loop(torch, bstep, max(args.steps // 20, 3), 2)
+        # a training step: the forward, then the backward; either the backward
+        # recomputes the chunk states, or the forward keeps them for it
+        cs = torch.empty((comba.chunk_states_size(B, T, H, K, V) // 4,), dtype=torch.float32, device=dev)
+
+        def train_recompute(_):
+            step(0)
+            bstep(0)
+
+        def train_cached(_):
+            comba.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], t["s0"], out=o, final_state=sf,
+                            chunk_states=cs)
+            comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], do_, t["s0"], None, dsf_,
+                            workspace=bws, chunk_states=cs)
+
+        trms, _ = time_loop(torch, train_recompute, max(args.steps // 20, 3), 2)
+        tcms, _ = time_loop(torch, train_cached, max(args.steps // 20, 3), 2)
+        del cs
         bbytes, bflops = chunk_bwd_algorithmic(B, T, H, K, V)
         result["backward"] = {"workload": "layer_1p3b, chunk backward (dq, dk, dv, dalpha, dbeta, dd, dS0)",
                               "us_per_step": bms * 1e3, "tokens/s": B * T / (bms * 1e-3),
                               "algorithmic_bytes": bbytes, "hbm_frac": bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                               "algorithmic_flops": bflops,
+                              "train_step_us": {"forward_then_backward_recomputing_states": trms * 1e3,
+                                                "forward_keeping_states_then_cached_backward": tcms * 1e3},
                               "mfma_frac": bflops / (bms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                               "workspace_bytes": bws.numel()}
         del bws, do_, dsf_

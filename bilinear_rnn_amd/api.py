@@ -32,7 +32,8 @@ EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_recurrent_step", "comba_recurrent_step_fused", "comba_recurrent_step_ex",
             "comba_chunk_fwd_segmented_workspace_size",
             "comba_chunk_fwd_segmented", "comba_chunk_bwd_workspace_size", "comba_chunk_bwd",
-            "comba_varlen_order", "comba_mfma_peak_probe")
+            "comba_varlen_order", "comba_mfma_peak_probe", "comba_chunk_states_size", "comba_chunk_fwd_keep_states",
+            "comba_chunk_bwd_cached_workspace_size", "comba_chunk_bwd_cached")
 
 
 class CombaError(RuntimeError):
@@ -92,6 +93,16 @@ def lib() -> ctypes.CDLL:
         L.comba_chunk_bwd.restype = i32
         L.comba_varlen_order.argtypes = [ip, i32, ip, vp]
         L.comba_varlen_order.restype = i32
+        L.comba_chunk_states_size.argtypes = [i32] * 6
+        L.comba_chunk_states_size.restype = sz
+        L.comba_chunk_fwd_keep_states.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
+                                                  i32, i32, vp, fp, vp, sz, fp, sz, vp]
+        L.comba_chunk_fwd_keep_states.restype = i32
+        L.comba_chunk_bwd_cached_workspace_size.argtypes = [i32] * 6
+        L.comba_chunk_bwd_cached_workspace_size.restype = sz
+        L.comba_chunk_bwd_cached.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32, vp,
+                                             fp, fp, sz, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+        L.comba_chunk_bwd_cached.restype = i32
         L.comba_mfma_peak_probe.argtypes = [fp, i32, i32, vp]
         L.comba_mfma_peak_probe.restype = i32
         _lib = L
@@ -179,7 +190,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, gate_logits: bool = False,
               qk_l2norm: bool = False,
-              segments: Optional[int] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              segments: Optional[int] = None,
+              chunk_states: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunk-wise forward through ``comba_chunk_fwd``. Returns (o, final_state).
 
     q and k may hold fewer heads than v (a divisor of H): consecutive value
@@ -189,7 +201,10 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     and k are L2-normalised per head and token inside the kernel. Either flag
     routes the call through ``comba_chunk_fwd_fused``. ``segments`` (an int,
     0 = automatic; fixed-length batches only) routes it through the
-    segment-parallel ``comba_chunk_fwd_segmented``."""
+    segment-parallel ``comba_chunk_fwd_segmented``. ``chunk_states`` (fp32,
+    at least ``chunk_states_size`` bytes; no fusion, segments or shared q / k)
+    routes it through ``comba_chunk_fwd_keep_states``, which also keeps every
+    chunk's incoming state there for ``chunk_bwd``."""
     B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     L = lib()
     if out is None:
@@ -213,6 +228,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
                 V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state), int(segments), _ptr(workspace),
                 0 if workspace is None else workspace.numel(), fusion, ctypes.c_void_p(stream)))
         return out, final_state
+    if chunk_states is not None:
+        if fusion or Hk != H:
+            raise ValueError("chunk_states goes with the plain forward (no fusion, one q / k head per value head)")
+        _require(chunk_states, "chunk_states", torch.float32)
+        if chunk_states.device != q.device:
+            raise ValueError("chunk_states must be on q's device")
     nws = int(L.comba_chunk_fwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0, _DT[q.dtype]))
     if nws > 0 and (workspace is None or workspace.numel() < nws):
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
@@ -222,7 +243,10 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
                 _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H)
         tail = (K, V, _DT[q.dtype], _DT[out_dtype], _ptr(out), _ptr(final_state), _ptr(workspace),
                 0 if workspace is None else workspace.numel())
-        if Hk != H:
+        if chunk_states is not None:
+            _check(L.comba_chunk_fwd_keep_states(*head, *tail, _ptr(chunk_states), chunk_states.numel() * 4,
+                                                 ctypes.c_void_p(stream)))
+        elif Hk != H:
             _check(L.comba_chunk_fwd_ex(*head, Hk, *tail, fusion, ctypes.c_void_p(stream)))
         elif fusion:
             _check(L.comba_chunk_fwd_fused(*head, *tail, fusion, ctypes.c_void_p(stream)))
@@ -275,10 +299,14 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
               d: torch.Tensor, do: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None,
               need_initial_state_grad: bool = True,
-              workspace: Optional[torch.Tensor] = None) -> dict:
+              workspace: Optional[torch.Tensor] = None,
+              chunk_states: Optional[torch.Tensor] = None) -> dict:
     """Gradients through ``comba_chunk_bwd`` for dL/do = ``do`` and dL/dS_final =
     ``d_final_state`` (None: 0). Returns a dict of fp32 tensors dq, dk, dv,
-    dalpha, dbeta, dd and (unless disabled) dinitial_state."""
+    dalpha, dbeta, dd and (unless disabled) dinitial_state. With
+    ``chunk_states`` (kept by ``chunk_fwd(..., chunk_states=...)`` on the same
+    inputs) the call goes through ``comba_chunk_bwd_cached``, which does not
+    recompute them."""
     B, T, H, Hk, K, V, N, _ = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, None)
     if Hk != H:
         raise ValueError("the backward takes one q / k head per value head")
@@ -291,17 +319,37 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
              dv=torch.empty((B, T, H, V), **f32), dalpha=torch.empty((B, T, H), **f32),
              dbeta=torch.empty((B, T, H), **f32), dd=torch.empty((H,), **f32))
     g["dinitial_state"] = torch.empty((N, H, V, K), **f32) if need_initial_state_grad else None
-    nws = int(L.comba_chunk_bwd_workspace_size(B, T, H, K, V, N if cu_seqlens is not None else 0))
+    nseq = N if cu_seqlens is not None else 0
+    if chunk_states is not None:
+        _require(chunk_states, "chunk_states", torch.float32)
+        if chunk_states.device != q.device:
+            raise ValueError("chunk_states must be on q's device")
+        nws = int(L.comba_chunk_bwd_cached_workspace_size(B, T, H, K, V, nseq))
+    else:
+        nws = int(L.comba_chunk_bwd_workspace_size(B, T, H, K, V, nseq))
     if workspace is None or workspace.numel() < nws:
         workspace = torch.empty((nws,), dtype=torch.uint8, device=q.device)
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state), _ptr(cu_seqlens),
+            nseq, B, T, H, K, V, _DT[q.dtype], _ptr(do), _ptr(d_final_state))
+    grads = (_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dd"]),
+             _ptr(g["dinitial_state"]), _ptr(workspace), workspace.numel())
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        _check(L.comba_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state),
-                                 _ptr(cu_seqlens), N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype],
-                                 _ptr(do), _ptr(d_final_state), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
-                                 _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g["dd"]), _ptr(g["dinitial_state"]),
-                                 _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream)))
+        if chunk_states is not None:
+            _check(L.comba_chunk_bwd_cached(*head, _ptr(chunk_states), chunk_states.numel() * 4, *grads,
+                                            ctypes.c_void_p(stream)))
+        else:
+            _check(L.comba_chunk_bwd(*head, *grads, ctypes.c_void_p(stream)))
     return g
+
+
+def chunk_states_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0) -> int:
+    """Bytes of the chunk-state buffer of ``chunk_fwd(..., chunk_states=...)``."""
+    return int(lib().comba_chunk_states_size(B, T, H, K, V, num_seqs))
+
+
+def bwd_cached_workspace_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0) -> int:
+    return int(lib().comba_chunk_bwd_cached_workspace_size(B, T, H, K, V, num_seqs))
 
 
 def bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, num_seqs: int = 0) -> int:

@@ -109,13 +109,14 @@ int32_t chunk_fwd_impl(const void* q, const void* k, const void* v, const float*
                        const float* d, const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
                        int32_t B, int32_t T, int32_t H, int32_t Hk, int32_t K, int32_t V, int32_t in_dtype,
                        int32_t out_dtype, void* o, float* final_state, void* workspace, size_t workspace_bytes,
-                       uint32_t fusion, void* stream) {
+                       uint32_t fusion, void* stream, float* chunk_states = nullptr) {
   if (fusion & ~kKnownFusion) return fail(COMBA_ERR_INVALID_ARG, "unknown bits in fusion");
   comba::FwdArgs a;
   int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, Hk, K, V,
                           in_dtype, out_dtype, o, final_state, a);
   if (rc != COMBA_OK) return rc;
   a.fusion = fusion;
+  a.hck = chunk_states;
   const size_t need = comba_chunk_fwd_workspace_size(B, T, H, K, V, cu_seqlens ? num_seqs : 0, in_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(COMBA_ERR_WORKSPACE, "workspace is NULL or smaller than comba_chunk_fwd_workspace_size()");
@@ -173,6 +174,28 @@ COMBA_API int32_t comba_chunk_fwd_ex(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, uint32_t fusion, void* stream) {
   return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, num_qk_heads, K, V,
                         in_dtype, out_dtype, o, final_state, workspace, workspace_bytes, fusion, stream);
+}
+
+COMBA_API size_t comba_chunk_states_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                         int32_t num_seqs) {
+  if (B < 1 || T < 0 || H < 1 || K < 1 || V < 1 || num_seqs < 0) return 0;
+  const bool packed = num_seqs > 0;
+  return static_cast<size_t>(comba::chunk_slots(packed, B, T, packed ? num_seqs : B)) * H * V * K * 4;
+}
+
+COMBA_API int32_t comba_chunk_fwd_keep_states(const void* q, const void* k, const void* v, const float* alpha,
+                                              const float* beta, const float* d, const float* initial_state,
+                                              const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                              int32_t H, int32_t K, int32_t V, int32_t in_dtype,
+                                              int32_t out_dtype, void* o, float* final_state, void* workspace,
+                                              size_t workspace_bytes, float* chunk_states,
+                                              size_t chunk_states_bytes, void* stream) {
+  if (!chunk_states) return fail(COMBA_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+  const size_t need = comba_chunk_states_size(B, T, H, K, V, cu_seqlens ? num_seqs : 0);
+  if (chunk_states_bytes < need)
+    return fail(COMBA_ERR_WORKSPACE, "chunk_states is smaller than comba_chunk_states_size()");
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
+                        out_dtype, o, final_state, workspace, workspace_bytes, 0u, stream, chunk_states);
 }
 
 COMBA_API int32_t comba_recurrent_step(const void* q, const void* k, const void* v, const float* alpha,
@@ -331,22 +354,25 @@ COMBA_API int32_t comba_chunk_fwd_segmented(const void* q, const void* k, const 
 
 namespace {
 
+// Backward workspace. The recomputed chunk states come last: the variant that
+// takes them from the forward needs everything before them (`cached`).
 struct BwdWorkspace {
-  size_t hck, dhck, tm, pm, kk, gt, dd, total;
+  size_t dhck, tm, pm, kk, gt, dd, hck, cached, total;
 };
 
 BwdWorkspace bwd_workspace(int64_t nslots, int32_t H, int32_t K, int32_t V) {
   BwdWorkspace w;
   const size_t state = align_up(static_cast<size_t>(nslots) * H * V * K * 4);
   const size_t mat = align_up(static_cast<size_t>(nslots) * H * 64 * 64 * 4);
-  w.hck = 0;
-  w.dhck = state;
-  w.tm = 2 * state;
+  w.dhck = 0;
+  w.tm = state;
   w.pm = w.tm + mat;
   w.kk = w.pm + mat;
   w.gt = w.kk + mat;
   w.dd = w.gt + align_up(static_cast<size_t>(nslots) * H * 7 * 64 * 4);
-  w.total = w.dd + align_up(static_cast<size_t>(nslots) * H * 4);
+  w.hck = w.dd + align_up(static_cast<size_t>(nslots) * H * 4);
+  w.cached = w.hck;
+  w.total = w.hck + state;
   return w;
 }
 
@@ -359,13 +385,14 @@ COMBA_API size_t comba_chunk_bwd_workspace_size(int32_t B, int32_t T, int32_t H,
   return bwd_workspace(comba::chunk_slots(packed, B, T, packed ? num_seqs : B), H, K, V).total;
 }
 
-COMBA_API int32_t comba_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
-                                  const float* beta, const float* d, const float* initial_state,
-                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
-                                  int32_t K, int32_t V, int32_t in_dtype, const void* d_o,
-                                  const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha,
-                                  float* dbeta, float* dd, float* d_initial_state, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+namespace {
+
+int32_t chunk_bwd_impl(const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                       const float* d, const float* initial_state, const int32_t* cu_seqlens, int32_t num_seqs,
+                       int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t in_dtype, const void* d_o,
+                       const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                       float* dd, float* d_initial_state, const float* chunk_states, size_t chunk_states_bytes,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (!d_o || !dq || !dk || !dv || !dalpha || !dbeta || !dd)
     return fail(COMBA_ERR_INVALID_ARG, "d_o, dq, dk, dv, dalpha, dbeta and dd must be non-NULL");
   comba::FwdArgs a;
@@ -376,26 +403,68 @@ COMBA_API int32_t comba_chunk_bwd(const void* q, const void* k, const void* v, c
   const int64_t nslots = comba::chunk_slots(packed, B, T, a.N);
   if (nslots * H > INT_MAX) return fail(COMBA_ERR_UNSUPPORTED, "too many (chunk, head) pairs for one launch");
   const BwdWorkspace w = bwd_workspace(nslots, H, K, V);
-  if (!workspace || workspace_bytes < w.total)
-    return fail(COMBA_ERR_WORKSPACE, "workspace is NULL or smaller than comba_chunk_bwd_workspace_size()");
+  const bool cached = chunk_states != nullptr;
+  if (cached && chunk_states_bytes < static_cast<size_t>(nslots) * H * V * K * 4)
+    return fail(COMBA_ERR_WORKSPACE, "chunk_states is smaller than comba_chunk_states_size()");
+  if (!workspace || workspace_bytes < (cached ? w.cached : w.total))
+    return fail(COMBA_ERR_WORKSPACE, cached ? "workspace is NULL or smaller than comba_chunk_bwd_cached_workspace_size()"
+                                            : "workspace is NULL or smaller than comba_chunk_bwd_workspace_size()");
   char* ws = static_cast<char*>(workspace);
-  float* hck = reinterpret_cast<float*>(ws + w.hck);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // forward pass that keeps every chunk's incoming state (no output)
-  comba::FwdArgs f = a;
-  f.o = hck;  // never written: no-output mode
-  f.sf = nullptr;
-  f.order = nullptr;
-  f.fusion = comba::kModeNoOutput;
-  f.hck = hck;
-  rc = launched(in_dtype == COMBA_BF16 ? comba::launch_chunk_bf16(f, st) : comba::launch_chunk_fp32(f, st));
-  if (rc != COMBA_OK) return rc;
+  float* hck = const_cast<float*>(chunk_states);
+  if (!cached) {
+    // forward pass that keeps every chunk's incoming state (no output)
+    hck = reinterpret_cast<float*>(ws + w.hck);
+    comba::FwdArgs f = a;
+    f.o = hck;  // never written: no-output mode
+    f.sf = nullptr;
+    f.order = nullptr;
+    f.fusion = comba::kModeNoOutput;
+    f.hck = hck;
+    rc = launched(in_dtype == COMBA_BF16 ? comba::launch_chunk_bf16(f, st) : comba::launch_chunk_fp32(f, st));
+    if (rc != COMBA_OK) return rc;
+  }
   comba::BwdArgs g{q, k, v, alpha, beta, d, d_o, cu_seqlens, a.N, a.B, a.T, H, K, V, in_dtype, d_final_state,
                    hck, reinterpret_cast<float*>(ws + w.dhck), reinterpret_cast<float*>(ws + w.dd),
                    reinterpret_cast<float*>(ws + w.tm), reinterpret_cast<float*>(ws + w.pm),
                    reinterpret_cast<float*>(ws + w.kk), reinterpret_cast<float*>(ws + w.gt), dq, dk, dv, dalpha,
                    dbeta, dd, d_initial_state};
   return launched(comba::launch_chunk_bwd(g, st));
+}
+
+}  // namespace
+
+COMBA_API int32_t comba_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                                  const float* beta, const float* d, const float* initial_state,
+                                  const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T, int32_t H,
+                                  int32_t K, int32_t V, int32_t in_dtype, const void* d_o,
+                                  const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha,
+                                  float* dbeta, float* dd, float* d_initial_state, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return chunk_bwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype, d_o,
+                        d_final_state, dq, dk, dv, dalpha, dbeta, dd, d_initial_state, nullptr, 0, workspace,
+                        workspace_bytes, stream);
+}
+
+COMBA_API size_t comba_chunk_bwd_cached_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                                       int32_t num_seqs) {
+  if (B < 1 || T < 0 || H < 1 || K < 1 || V < 1) return 0;
+  const bool packed = num_seqs > 0;
+  return bwd_workspace(comba::chunk_slots(packed, B, T, packed ? num_seqs : B), H, K, V).cached;
+}
+
+COMBA_API int32_t comba_chunk_bwd_cached(const void* q, const void* k, const void* v, const float* alpha,
+                                         const float* beta, const float* d, const float* initial_state,
+                                         const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                         int32_t H, int32_t K, int32_t V, int32_t in_dtype, const void* d_o,
+                                         const float* d_final_state, const float* chunk_states,
+                                         size_t chunk_states_bytes, float* dq, float* dk, float* dv,
+                                         float* dalpha, float* dbeta, float* dd, float* d_initial_state,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!chunk_states) return fail(COMBA_ERR_INVALID_ARG, "chunk_states must be non-NULL");
+  return chunk_bwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, K, V, in_dtype, d_o,
+                        d_final_state, dq, dk, dv, dalpha, dbeta, dd, d_initial_state, chunk_states,
+                        chunk_states_bytes, workspace, workspace_bytes, stream);
 }
 
 COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t* order,

@@ -286,6 +286,58 @@ int32_t comba_chunk_bwd(const void* q, const void* k, const void* v,
                         float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The backward that reuses the forward's chunk states instead of recomputing
+ * them (the write-up, section "硬件高效的分块并行计算", weighs exactly this
+ * choice: keep the chunk states from the forward, or recompute them in the
+ * backward). For training, where the forward runs anyway:
+ *
+ *   comba_chunk_states_size(B, T, H, K, V, num_seqs)
+ *       bytes of the chunk-state buffer: one fp32 V x K state per 64-token
+ *       chunk and head, laid out [slot, H, V, K]. Slots are the chunks of
+ *       every sequence in order (fixed-length batches: b * ceil(T / 64) + c;
+ *       packed batches: chunk c of sequence n at cu_seqlens[n] / 64 + n + c).
+ *       num_seqs as for comba_chunk_bwd_workspace_size (0 without cu_seqlens).
+ *   comba_chunk_fwd_keep_states(...)
+ *       comba_chunk_fwd (same arguments and results, no fusion) that also
+ *       writes every chunk's incoming state into chunk_states (device, at
+ *       least comba_chunk_states_size bytes, caller-owned). Costs one extra
+ *       write of the buffer.
+ *   comba_chunk_bwd_cached(...)
+ *       comba_chunk_bwd (same arguments and results) that reads the chunk
+ *       states written by comba_chunk_fwd_keep_states on the same inputs
+ *       instead of recomputing them, with a smaller workspace of
+ *       comba_chunk_bwd_cached_workspace_size bytes. The results are
+ *       bit-identical to comba_chunk_bwd's.
+ * Errors: as comba_chunk_fwd / comba_chunk_bwd; COMBA_ERR_INVALID_ARG for a
+ * NULL chunk_states, COMBA_ERR_WORKSPACE when chunk_states_bytes or the
+ * workspace is short.
+ */
+size_t comba_chunk_states_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V, int32_t num_seqs);
+
+int32_t comba_chunk_fwd_keep_states(const void* q, const void* k, const void* v,
+                                    const float* alpha, const float* beta, const float* d,
+                                    const float* initial_state,
+                                    const int32_t* cu_seqlens, int32_t num_seqs,
+                                    int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                    int32_t in_dtype, int32_t out_dtype,
+                                    void* o, float* final_state,
+                                    void* workspace, size_t workspace_bytes,
+                                    float* chunk_states, size_t chunk_states_bytes, void* stream);
+
+size_t comba_chunk_bwd_cached_workspace_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                             int32_t num_seqs);
+
+int32_t comba_chunk_bwd_cached(const void* q, const void* k, const void* v,
+                               const float* alpha, const float* beta, const float* d,
+                               const float* initial_state,
+                               const int32_t* cu_seqlens, int32_t num_seqs,
+                               int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                               int32_t in_dtype, const void* d_o, const float* d_final_state,
+                               const float* chunk_states, size_t chunk_states_bytes,
+                               float* dq, float* dk, float* dv, float* dalpha, float* dbeta, float* dd,
+                               float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Longest-first order of packed sequences (integer work, exact): writes into
  * order[0..N-1] the sequence indices sorted by decreasing length
  * cu_seqlens[n+1] - cu_seqlens[n], ties by increasing index. comba_chunk_fwd

@@ -196,6 +196,57 @@ def test_mfma_peak_probe_rejects_bad_arguments(sink, blocks, iters, code):
     assert api.last_error() != ""
 
 
+def fwd_keep(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=100, H=2, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None, ws=None, wsb=0, cs=FAKE, csb=1 << 40)
+    args.update(kw)
+    a = args
+    return comba.lib().comba_chunk_fwd_keep_states(
+        a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["d"], a["s0"], a["cu"], a["n"], a["B"], a["T"], a["H"],
+        a["K"], a["V"], a["idt"], a["odt"], a["o"], a["sf"], a["ws"], a["wsb"], a["cs"], a["csb"], None)
+
+
+def bwd_cached(**kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=100, H=2, K=64, V=64, idt=0, do=FAKE, dsf=None, cs=FAKE, csb=1 << 40, dq=FAKE, dk=FAKE,
+                dv=FAKE, da=FAKE, db=FAKE, dd=FAKE, ds0=None, ws=FAKE, wsb=1 << 40)
+    args.update(kw)
+    a = args
+    return comba.lib().comba_chunk_bwd_cached(
+        a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["d"], a["s0"], a["cu"], a["n"], a["B"], a["T"], a["H"],
+        a["K"], a["V"], a["idt"], a["do"], a["dsf"], a["cs"], a["csb"], a["dq"], a["dk"], a["dv"], a["da"], a["db"],
+        a["dd"], a["ds0"], a["ws"], a["wsb"], None)
+
+
+def test_chunk_state_sizes():
+    # one fp32 V x K state per 64-token chunk and head
+    assert comba.chunk_states_size(1, 100, 2, 64, 64) == 2 * 2 * 64 * 64 * 4
+    assert comba.chunk_states_size(8, 4096, 16, 128, 128) == 8 * 64 * 16 * 128 * 128 * 4
+    # packed: T / 64 + N + 1 slots
+    assert comba.chunk_states_size(1, 1000, 2, 64, 64, 5) == (1000 // 64 + 5 + 1) * 2 * 64 * 64 * 4
+    # the cached backward needs the plain backward's workspace less its own copy of the states
+    for args in [(8, 4096, 16, 128, 128), (1, 1000, 2, 64, 64, 5), (3, 65, 4, 64, 128)]:
+        assert comba.bwd_workspace_size(*args) - comba.bwd_cached_workspace_size(*args) == comba.chunk_states_size(*args)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), -1), (dict(csb=2 * 2 * 64 * 64 * 4 - 1), -3), (dict(q=None), -1), (dict(K=96), -2),
+    (dict(H=32769, K=128, V=128), -2),
+])
+def test_keep_states_forward_rejects_bad_arguments(kw, code):
+    assert fwd_keep(**kw) == code
+    assert api.last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cs=None), -1), (dict(csb=100), -3), (dict(do=None), -1), (dict(dq=None), -1), (dict(K=96), -2),
+    (dict(ws=None, wsb=0), -3), (dict(wsb=comba.api.lib().comba_chunk_bwd_cached_workspace_size(1, 100, 2, 64, 64, 0) - 1), -3),
+])
+def test_cached_backward_rejects_bad_arguments(kw, code):
+    assert bwd_cached(**kw) == code
+    assert api.last_error() != ""
+
+
 def test_backward_workspace_size():
     ws = comba.bwd_workspace_size
     # per chunk and head: two fp32 states, three fp32 64 x 64 matrices, seven

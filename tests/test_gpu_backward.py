@@ -154,6 +154,50 @@ def test_backward_extreme_gates(dtype):
     check(got, oracle_bwd(inp, do, dsf), inp)
 
 
+CACHED_CASES = [
+    ("layer_340m", dict(K=128, V=128, B=2, H=2), dict(T=300, s0_std=0.02), None),
+    ("layer_340m", dict(K=64, V=128, B=3, H=2), dict(T=65, s0_std=0.0), None),
+    ("tiny_fp32", dict(K=128, V=64, B=2, H=2), dict(T=150, s0_std=0.1), None),
+    ("varlen", dict(H=3), dict(s0_std=0.05), np.array([16, 70, 1, 0, 130, 64, 0, 63, 65])),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CACHED_CASES)))
+def test_cached_chunk_states_backward(case):
+    """The forward that keeps the chunk states writes the plain forward's
+    output and final state, and the backward that reads them gives the
+    recomputing backward's gradients, bit for bit (the same state chain
+    either way), and so passes the oracle gates."""
+    name, wkw, ikw, lengths = CACHED_CASES[case]
+    inp = make_inputs(wl(name, **wkw), lengths=lengths, seed=90 + case, **ikw)
+    print(f"cached states: {name} {wkw} {ikw} lengths={lengths}", flush=True)
+    do, do_bits, dsf = cotangents(inp, 95 + case)
+    t = dev_inputs(inp)
+    B, T, H, K = inp.q.shape
+    V = inp.v.shape[-1]
+    nseq = inp.num_seqs if inp.cu_seqlens is not None else 0
+    cs = torch.empty((comba.chunk_states_size(B, T, H, K, V, nseq) // 4,), dtype=torch.float32, device="cuda")
+    o1, s1 = comba.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], t["initial_state"],
+                             t["cu_seqlens"])
+    o2, s2 = comba.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], t["initial_state"],
+                             t["cu_seqlens"], chunk_states=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    dod = (torch.from_numpy(np.ascontiguousarray(do_bits).view(np.int16)).view(torch.bfloat16).cuda()
+           if do_bits is not None else torch.from_numpy(np.ascontiguousarray(do)).cuda())
+    dsfd = torch.from_numpy(dsf).cuda()
+    g1 = comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], dod, t["initial_state"],
+                         t["cu_seqlens"], dsfd)
+    g2 = comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], dod, t["initial_state"],
+                         t["cu_seqlens"], dsfd, chunk_states=cs)
+    torch.cuda.synchronize()
+    for key in g1:
+        assert torch.equal(g1[key], g2[key]), key
+    got = {key: to_np(x) for key, x in g2.items()}
+    got["ds0"] = got.pop("dinitial_state")
+    check(got, oracle_bwd(inp, do, dsf), inp)
+
+
 def test_backward_deterministic():
     inp = make_inputs(wl("layer_340m", B=2, H=2), T=333, s0_std=0.02, seed=81)
     do, do_bits, dsf = cotangents(inp, 82)
