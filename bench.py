@@ -376,14 +376,14 @@ def main():
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     # Two resident copies of the inputs and outputs (2 x 0.56 GB), used in turn, so
     # that the 256 MB last-level cache cannot carry one step's operands into the next.
-    copies = [device_inputs(inp, torch, dev) for _ in range(2)]
-    outs = [(torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev),
-             torch.empty((B, H, V, K), dtype=torch.float32, device=dev)) for _ in range(2)]
-    t = copies[0]
-    o, sf = outs[0]
+    fwd_copies = [device_inputs(inp, torch, dev) for _ in range(2)]
+    fwd_outs = [(torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev),
+                 torch.empty((B, H, V, K), dtype=torch.float32, device=dev)) for _ in range(2)]
+    t = fwd_copies[0]
+    o, sf = fwd_outs[0]
 
     def step(i):
-        c, (oo, ss) = copies[i % 2], outs[i % 2]
+        c, (oo, ss) = fwd_copies[i % 2], fwd_outs[i % 2]
         comba.chunk_fwd(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["d"], c["s0"], out=oo, final_state=ss)
 
     ms, wall = time_loop(torch, step, args.steps, args.warmup)
@@ -440,14 +440,14 @@ def main():
 
     if not args.no_decode:
         wd = WORKLOADS["decode"]
-        copies = []
+        dec_copies = []
         for c in range(2):  # two resident copies so the 256 MB last-level cache cannot serve the state
             di = make_inputs(wd, seed=wd.seed + c)
-            copies.append(device_inputs(di, torch, dev))
+            dec_copies.append(device_inputs(di, torch, dev))
         od = torch.empty((wd.B, 1, wd.H, wd.V), dtype=torch.bfloat16, device=dev)
 
         def dstep(i):
-            c = copies[i % 2]
+            c = dec_copies[i % 2]
             comba.recurrent_step(c["q"], c["k"], c["v"], c["alpha"], c["beta"], c["d"], c["s0"],
                                  in_place=True, out=od)
 
