@@ -52,15 +52,55 @@ __device__ __forceinline__ void chunk_gates(ChunkGates& gt, int lane, int nrows)
   gt.EGnG[lane] = expf(Gn - G);
 }
 
+// One level of the off-diagonal blocks of the 64x64 inverse below: every
+// block at distance L = i - j below the diagonal,
+//   T_ij = -T_ii sum_{j <= m < i} A_im T_mj,
+// from the diagonal blocks and the levels closer to it. The reduction lengths
+// are compile-time constants, so the LDS reads issue back to back (A rows as
+// 16-byte reads); the sums run over m in increasing order. The upper part of
+// a diagonal block T_ii is exactly zero, so its product runs over all 16
+// columns.
+template <int L, int NT>
+__device__ __forceinline__ void inverse_level(const float* Am, float* Tm, float* Ys, int tid) {
+  constexpr int nb = 4 - L;
+  for (int e = tid; e < nb * 256; e += NT) {
+    const int j = e >> 8, r = (e >> 4) & 15, c = e & 15, i = j + L;
+    const float* arow = Am + (16 * i + r) * kLdF + 16 * j;
+    const float* tcol = Tm + (16 * j) * kLdF + 16 * j + c;
+    float acc = 0.f;
+#pragma unroll
+    for (int m4 = 0; m4 < 4 * L; ++m4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(arow + 4 * m4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += a[u] * tcol[(4 * m4 + u) * kLdF];
+    }
+    Ys[e] = acc;
+  }
+  __syncthreads();
+  for (int e = tid; e < nb * 256; e += NT) {
+    const int j = e >> 8, r = (e >> 4) & 15, c = e & 15, i = j + L;
+    const float* trow = Tm + (16 * i + r) * kLdF + 16 * i;
+    const float* ycol = Ys + (j << 8) + c;
+    float acc = 0.f;
+#pragma unroll
+    for (int m4 = 0; m4 < 4; ++m4) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(trow + 4 * m4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += t[u] * ycol[(4 * m4 + u) << 4];
+    }
+    Tm[(16 * i + r) * kLdF + 16 * j + c] = -acc;
+  }
+  __syncthreads();
+}
+
 // Tm = (I + Am)^-1 for a 64x64 strictly lower Am (fp32, row stride kLdF).
 // Only the lower 16x16 blocks of Am are read; the lower blocks of Tm are
 // written (zeros above the diagonal inside diagonal blocks). Ys: 768 floats.
-// Diagonal blocks: column-wise forward substitution, one lane per column.
-// Off-diagonal blocks by block distance L = i - j:
-//   T_ij = -T_ii sum_{j <= m < i} A_im T_mj
+// Diagonal blocks: column-wise forward substitution, one lane per column;
+// then the off-diagonal blocks level by level (inverse_level).
 // Must be called by all NT threads; ends with a barrier.
 template <int NT>
-__device__ void unit_lower_inverse64(const float* Am, float* Tm, float* Ys, int tid) {
+__device__ __forceinline__ void unit_lower_inverse64(const float* Am, float* Tm, float* Ys, int tid) {
   if (tid < 64) {
     const int blk = tid >> 4, c = tid & 15;
     const float* Ab = Am + (16 * blk) * kLdF + 16 * blk;
@@ -77,25 +117,9 @@ __device__ void unit_lower_inverse64(const float* Am, float* Tm, float* Ys, int 
     for (int r = 0; r < 16; ++r) Tb[r * kLdF + c] = x[r];
   }
   __syncthreads();
-  for (int L = 1; L <= 3; ++L) {
-    const int nb = 4 - L;
-    for (int e = tid; e < nb * 256; e += NT) {
-      const int j = e >> 8, r = (e >> 4) & 15, c = e & 15, i = j + L;
-      const float* arow = Am + (16 * i + r) * kLdF;
-      float acc = 0.f;
-      for (int m = 16 * j; m < 16 * i; ++m) acc += arow[m] * Tm[m * kLdF + 16 * j + c];
-      Ys[e] = acc;
-    }
-    __syncthreads();
-    for (int e = tid; e < nb * 256; e += NT) {
-      const int j = e >> 8, r = (e >> 4) & 15, c = e & 15, i = j + L;
-      const float* trow = Tm + (16 * i + r) * kLdF + 16 * i;
-      float acc = 0.f;
-      for (int m = 0; m <= r; ++m) acc += trow[m] * Ys[(j << 8) + (m << 4) + c];
-      Tm[(16 * i + r) * kLdF + 16 * j + c] = -acc;
-    }
-    __syncthreads();
-  }
+  inverse_level<1, NT>(Am, Tm, Ys, tid);
+  inverse_level<2, NT>(Am, Tm, Ys, tid);
+  inverse_level<3, NT>(Am, Tm, Ys, tid);
 }
 
 // Work unit of a block: units are (sequence rank, head) pairs dealt

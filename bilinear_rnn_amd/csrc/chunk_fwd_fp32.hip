@@ -9,7 +9,7 @@
 namespace comba {
 
 template <int K>
-struct SmemF32 {
+struct alignas(16) SmemF32 {
   static constexpr int VT = 16;
   static constexpr int LDH = VT + 1;
   float Qs[64 * (K + 1)];
