@@ -524,7 +524,7 @@ def main():
             comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], do_, t["s0"], None, dsf_,
                             workspace=bws)
 
-        bms, _ = time_loop(torch, bstep, max(args.steps // 20, 3), 2)
+        bms, _ = time_loop(torch, bstep, max(args.steps // 10, 5), 5)
         # a training step: the forward, then the backward; either the backward
         # recomputes the chunk states, or the forward keeps them for it
         cs = torch.empty((comba.chunk_states_size(B, T, H, K, V) // 4,), dtype=torch.float32, device=dev)
@@ -539,8 +539,8 @@ def main():
             comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], do_, t["s0"], None, dsf_,
                             workspace=bws, chunk_states=cs)
 
-        trms, _ = time_loop(torch, train_recompute, max(args.steps // 20, 3), 2)
-        tcms, _ = time_loop(torch, train_cached, max(args.steps // 20, 3), 2)
+        trms, _ = time_loop(torch, train_recompute, max(args.steps // 10, 5), 5)
+        tcms, _ = time_loop(torch, train_cached, max(args.steps // 10, 5), 5)
         del cs
         bbytes, bflops = chunk_bwd_algorithmic(B, T, H, K, V)
         result["backward"] = {"workload": "layer_1p3b, chunk backward (dq, dk, dv, dalpha, dbeta, dd, dS0)",
