@@ -20,7 +20,8 @@ from typing import Optional
 
 import numpy as np
 
-from .reference import comba_backward, comba_forward, comba_forward_chunked, expand_shared_qk, fused_inputs, rel_l2  # noqa: F401
+from .reference import (comba_backward, comba_forward, comba_forward_chunked, expand_shared_qk,  # noqa: F401
+                        fused_inputs, rel_l2, row_rel_err)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "comba_oracle.c")
@@ -51,6 +52,11 @@ def _load():
                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                              dp, dp, ctypes.c_int32]
         lib.comba_oracle_forward.restype = ctypes.c_int
+        lib.comba_oracle_backward.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, i32p, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int32,
+                                              dp, dp, dp, dp, dp, dp, dp, ctypes.c_int32]
+        lib.comba_oracle_backward.restype = ctypes.c_int
         lib.comba_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -87,3 +93,41 @@ def comba_forward_c(q, k, v, alpha, beta, d, s0=None, cu_seqlens=None,
     if rc != 0:
         raise ValueError("comba_oracle_forward rejected its arguments")
     return o, sf
+
+
+def comba_backward_c(q, k, v, alpha, beta, d, do, s0=None, dsf=None, cu_seqlens=None, nthreads: int = 0):
+    """Same definition as :func:`oracle.reference.comba_backward`, in C fp64
+    (one OpenMP task per sequence and head). Returns the same dict of float64
+    arrays: dq, dk, dv, dalpha, dbeta, dd (summed over the sequences in order)
+    and ds0."""
+    lib = _load()
+
+    def f64(x):
+        return np.ascontiguousarray(x, dtype=np.float64)
+
+    q, k, v, alpha, beta, d, do = map(f64, (q, k, v, alpha, beta, d, do))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    cu = None if cu_seqlens is None else np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+    N = B if cu is None else len(cu) - 1
+    s0a = None if s0 is None else f64(s0)
+    dsfa = None if dsf is None else f64(dsf)
+    g = {"dq": np.zeros((B, T, H, K)), "dk": np.zeros((B, T, H, K)), "dv": np.zeros((B, T, H, V)),
+         "dalpha": np.zeros((B, T, H)), "dbeta": np.zeros((B, T, H)), "ds0": np.zeros((N, H, V, K))}
+    dd_part = np.zeros((N, H))
+    dp = ctypes.POINTER(ctypes.c_double)
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data_as(dp)
+
+    rc = lib.comba_oracle_backward(ptr(q), ptr(k), ptr(v), ptr(alpha), ptr(beta), ptr(d), ptr(do), ptr(s0a),
+                                   ptr(dsfa),
+                                   None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   N, B, T, H, K, V, ptr(g["dq"]), ptr(g["dk"]), ptr(g["dv"]), ptr(g["dalpha"]),
+                                   ptr(g["dbeta"]), ptr(dd_part), ptr(g["ds0"]), nthreads)
+    if rc != 0:
+        raise ValueError("comba_oracle_backward rejected its arguments")
+    g["dd"] = np.zeros((H,))
+    for n in range(N):
+        g["dd"] += dd_part[n]
+    return g

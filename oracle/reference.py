@@ -259,3 +259,31 @@ def rel_l2(x, ref) -> float:
     if not np.isfinite(num):
         return float("inf")
     return float(num / den) if den > 0 else float(num)
+
+
+def row_rel_err(x, ref, floor: float = 1e-2) -> float:
+    """Largest relative error of one row, rows being the last axis, in fp64.
+
+    Row i scores ||x_i - ref_i||_2 / max(||ref_i||_2, floor * r), where r is
+    the root mean square of the reference row norms: a row is judged against
+    its own norm unless that norm is below ``floor`` times the typical one.
+    A whole-tensor rel-L2 spreads one wrong row over all of them; this does not.
+    Any non-finite value in x gives inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if x.shape != ref.shape:
+        raise ValueError(f"shape mismatch {x.shape} vs {ref.shape}")
+    if x.size == 0:
+        return 0.0
+    if not np.isfinite(x).all():
+        return float("inf")
+    n = x.shape[-1]
+    xr, rr = x.reshape(-1, n), ref.reshape(-1, n)
+    rn = np.sqrt(np.sum(rr * rr, axis=1))
+    en = np.sqrt(np.sum((xr - rr) ** 2, axis=1))
+    typical = float(np.sqrt(np.mean(rn * rn)))
+    den = np.maximum(rn, floor * typical)
+    if typical == 0.0:
+        return float(np.max(en))
+    return float(np.max(en / den))

@@ -498,3 +498,110 @@ def test_backward_linear_in_output_weights():
     g0 = oracle.comba_backward(q, k, v, alpha, beta, d, 0 * do1, S0, None)
     for key in g0:
         assert np.all(g0[key] == 0)
+
+
+# --- the parity measures themselves -----------------------------------------------------
+
+def test_parity_measures_hand_computed():
+    """rel_l2 and row_rel_err against values computed by hand (golden/metrics.yaml):
+    a dropped square root, the wrong norm in the denominator or a lost floor
+    each gives a different number."""
+    with open(os.path.join(GOLDEN, "metrics.yaml")) as f:
+        g = yaml.safe_load(f)
+    for case in g["rel_l2"]:
+        got = rel_l2(np.array(case["x"]), np.array(case["ref"]))
+        assert abs(got - case["expect"]) <= 1e-15, (case, got)
+    for case in g["row_rel_err"]:
+        got = oracle.row_rel_err(np.array(case["x"]), np.array(case["ref"]), floor=case["floor"])
+        assert abs(got - case["expect"]) <= 1e-12, (case, got)
+    assert rel_l2(np.array([np.nan, 1.0]), np.array([1.0, 1.0])) == float("inf")
+    assert oracle.row_rel_err(np.array([[np.inf, 1.0]]), np.array([[1.0, 1.0]])) == float("inf")
+
+
+def test_row_bound_catches_one_wrong_row_that_rel_l2_misses():
+    """At the packed-sequence workload's output shape (about 41K tokens x 32
+    heads x 64 channels), bf16 rounding of a correct output plus one token-head
+    row replaced by an unrelated row of the same norm stays under the 2e-3
+    whole-tensor gate, but the per-row measure flags it."""
+    from bilinear_rnn_amd.inputs import bf16_bits, bf16_bits_to_f32
+    w = WORKLOADS["varlen"]
+    rng = np.random.default_rng(71)
+    T = 41_000
+    ref = rng.standard_normal((1, T, w.H, w.V))
+    got = bf16_bits_to_f32(bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    t, h = 12_345, 17
+    bad = rng.standard_normal(w.V)
+    got[0, t, h] = bad * np.linalg.norm(ref[0, t, h]) / np.linalg.norm(bad)
+    assert rel_l2(got, ref) <= 2e-3
+    assert oracle.row_rel_err(got, ref) > 0.5
+    got[0, t, h] = ref[0, t, h]
+    assert oracle.row_rel_err(got, ref) <= 2.0 ** -8
+
+
+@pytest.mark.parametrize("case", ["fixed", "packed", "no_states", "wide"])
+def test_c_backward_equals_numpy_backward(case):
+    """The C reverse mode (used at full size) against the numpy one (pinned by
+    central differences above), including empty packed sequences and
+    stretches of more than 64 tokens."""
+    rng = np.random.default_rng(91)
+    cu = None
+    if case == "packed":
+        B, T, H, K, V = 1, 230, 2, 6, 5
+        cu = np.array([0, 70, 70, 200, 201, 230])
+    elif case == "wide":
+        B, T, H, K, V = 1, 140, 1, 16, 24
+    else:
+        B, T, H, K, V = 2, 131, 3, 8, 5
+    N = B if cu is None else len(cu) - 1
+    q = rng.standard_normal((B, T, H, K))
+    k = rng.standard_normal((B, T, H, K))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((B, T, H, V))
+    a = rng.uniform(0.5, 1.0, (B, T, H))
+    b = rng.uniform(0.0, 1.0, (B, T, H))
+    d = rng.uniform(-1.0, 1.0, (H,))
+    do = rng.standard_normal((B, T, H, V))
+    s0 = None if case == "no_states" else rng.standard_normal((N, H, V, K)) * 0.3
+    dsf = None if case == "no_states" else rng.standard_normal((N, H, V, K))
+    g1 = oracle.comba_backward(q, k, v, a, b, d, do, s0, dsf, cu)
+    g2 = oracle.comba_backward_c(q, k, v, a, b, d, do, s0, dsf, cu, nthreads=3)
+    for key in g1:
+        np.testing.assert_allclose(g2[key], g1[key], rtol=1e-12, atol=1e-12, err_msg=key)
+
+
+def test_c_backward_matches_central_differences_of_c_forward():
+    """An independent route for the C reverse mode: central differences of the
+    C forward, for L = <o, Wo> + <S_final, Ws>, on a packed batch with an empty
+    sequence and a stretch boundary (T > 64)."""
+    rng = np.random.default_rng(93)
+    B, T, H, K, V = 1, 70, 1, 3, 2
+    cu = np.array([0, 66, 66, 70])
+    N = 3
+    x = dict(q=rng.standard_normal((B, T, H, K)), k=rng.standard_normal((B, T, H, K)) * 0.6,
+             v=rng.standard_normal((B, T, H, V)), alpha=rng.uniform(0.7, 1.0, (B, T, H)),
+             beta=rng.uniform(0.1, 1.0, (B, T, H)), d=rng.uniform(-1, 1, (H,)),
+             s0=rng.standard_normal((N, H, V, K)) * 0.5)
+    Wo = rng.standard_normal((B, T, H, V))
+    Ws = rng.standard_normal((N, H, V, K))
+
+    def loss(xx):
+        o, s = oracle.comba_forward_c(xx["q"], xx["k"], xx["v"], xx["alpha"], xx["beta"], xx["d"], xx["s0"], cu,
+                                      nthreads=1)
+        return float(np.sum(o * Wo) + np.sum(s * Ws))
+
+    g = oracle.comba_backward_c(x["q"], x["k"], x["v"], x["alpha"], x["beta"], x["d"], Wo, x["s0"], Ws, cu,
+                                nthreads=2)
+    names = dict(q="dq", k="dk", v="dv", alpha="dalpha", beta="dbeta", d="dd", s0="ds0")
+    eps = 1e-6
+    for name, gname in names.items():
+        # every gradient entry of the small tensors; a strided sample of the long ones
+        idxs = list(np.ndindex(x[name].shape))
+        if len(idxs) > 60:
+            idxs = idxs[::7]
+        for idx in idxs:
+            xp = {kk: vv.copy() for kk, vv in x.items()}
+            xm = {kk: vv.copy() for kk, vv in x.items()}
+            xp[name][idx] += eps
+            xm[name][idx] -= eps
+            fd = (loss(xp) - loss(xm)) / (2 * eps)
+            assert abs(g[gname][idx] - fd) <= 1e-6 * max(1.0, abs(fd)), (name, idx, g[gname][idx], fd)
