@@ -51,3 +51,59 @@ def oracle_of(inp, heads=None, seqs=None, nthreads=0, gate_logits=None, qk_l2nor
 
 def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+# --- parity gates ------------------------------------------------------------------------
+# Each gate is a pair: rel-L2 over the whole tensor, and the largest relative
+# error of one row (the last axis: one token-head row of o or of a gradient,
+# one value channel of a state; oracle.row_rel_err). Row gates:
+#   - bf16 output: rounding to nearest bf16 moves each element by at most
+#     2^-8 of its magnitude, so a row by at most 2^-8 of its norm; 1e-3 more
+#     covers the arithmetic before rounding (ten times its whole-tensor gate);
+#   - fp32 outputs: ten times the whole-tensor gate of the same arithmetic,
+#     room for the tail rows of a tensor of a million rows whose typical row
+#     sits at the whole-tensor figure.
+# A row that is wrong altogether scores about 1 and fails every one of them.
+import collections
+import functools
+
+Gates = collections.namedtuple("Gates", "whole row")
+BF16 = Gates(2e-3, 2.0 ** -8 + 1e-3)          # bf16 q/k/v, bf16 o
+FP32 = Gates(1e-5, 1e-4)                      # fp32 q/k/v, fp32 o and state
+BF16_IN_FP32_OUT = Gates(1e-4, 1e-3)          # bf16 q/k/v, fp32 o
+STATE_BF16 = Gates(2e-3, 1e-3)                # fp32 state from bf16 q/k/v
+
+
+def assert_close(got, ref, gates, what=""):
+    """Whole-tensor rel-L2 and per-row bound of ``got`` against the oracle's
+    ``ref``; non-finite values fail both."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    e = rel_l2(got, ref)
+    r = oracle.row_rel_err(got, ref)
+    print(f"{what}: rel-L2 {e:.3e} (gate {gates.whole:.1e}), worst row {r:.3e} (gate {gates.row:.1e})", flush=True)
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    assert e <= gates.whole, f"{what}: rel-L2 {e:.3e} > {gates.whole:.1e}"
+    assert r <= gates.row, f"{what}: worst row {r:.3e} > {gates.row:.1e}"
+
+
+_CACHE = {}
+
+
+def cached(key, make):
+    """A value computed once per test session (seeded full-size inputs and
+    their oracle results, shared by several tests)."""
+    if key not in _CACHE:
+        _CACHE[key] = make()
+    return _CACHE[key]
+
+
+def full_inputs(name, **kw):
+    from bilinear_rnn_amd.inputs import WORKLOADS, make_inputs
+    return cached(("inputs", name, tuple(sorted(kw.items()))), lambda: make_inputs(WORKLOADS[name], **kw))
+
+
+def full_oracle(name, **kw):
+    """Oracle (o, final_state) over the whole of a named workload."""
+    return cached(("oracle", name, tuple(sorted(kw.items()))), lambda: oracle_of(full_inputs(name, **kw)))
