@@ -239,8 +239,8 @@ struct alignas(16) SmemPrepMfma {
 template <bool kStoreKK>
 __device__ __forceinline__ void prep_entry(const ChunkGates& gt, int t, int s, float kk, float qtk, float* Am,
                                            float* Pg, float* KKg) {
-  Am[t * kLdF + s] = s < t ? gt.beta[t] * __expf(gt.Gx[t] - gt.G[s]) * kk : 0.f;
-  Pg[t * 64 + s] = s <= t ? qtk * __expf(fminf(gt.G[t] - gt.G[s], 0.f)) : 0.f;
+  Am[t * kLdF + s] = s < t ? gt.beta[t] * decay_Gx(gt, t, s) * kk : 0.f;
+  Pg[t * 64 + s] = s <= t ? qtk * decay_G(gt, t, s) : 0.f;
   if constexpr (kStoreKK) KKg[t * 64 + s] = kk;
 }
 

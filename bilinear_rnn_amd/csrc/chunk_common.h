@@ -33,6 +33,13 @@ struct ChunkGates {
   float EGnG[64];   // exp(G_n - G)
   float raw_a[64];  // staged alpha of the chunk
   float raw_b[64];  // staged beta of the chunk
+  // G and Gx again, summed in double. A decay factor is the exponential of a
+  // difference of two cumulative sums; taken in float, that difference loses
+  // ulp(|G|) to cancellation once earlier tokens of the chunk have decayed
+  // strongly (|G| in the thousands when alpha is near zero), which the
+  // double sums avoid.
+  double Gd[64];
+  double Gxd[64];
 };
 
 // Run by one wavefront: lane = row of the chunk.
@@ -40,16 +47,28 @@ __device__ __forceinline__ void chunk_gates(ChunkGates& gt, int lane, int nrows)
   const bool valid = lane < nrows;
   const float a = valid ? gt.raw_a[lane] : 1.f;
   const float be = valid ? gt.raw_b[lane] : 0.f;
-  const float g = logf(a);
-  const float G = wave_inclusive_scan(g, lane);
-  const float Gn = __shfl(G, 63, kWave);
-  const float Gx = G - g;
-  gt.G[lane] = G;
-  gt.Gx[lane] = Gx;
+  // alpha below the smallest normal float is taken as that float, so that
+  // log alpha stays finite (the state is then forgotten within the token).
+  const float g = logf(fmaxf(a, 1.17549435e-38f));
+  const double G = wave_inclusive_scan_f64(static_cast<double>(g), lane);
+  const double Gn = __shfl(G, 63, kWave);
+  const double Gx = G - static_cast<double>(g);
+  gt.Gd[lane] = G;
+  gt.Gxd[lane] = Gx;
+  gt.G[lane] = static_cast<float>(G);
+  gt.Gx[lane] = static_cast<float>(Gx);
   gt.beta[lane] = be;
-  gt.bEGx[lane] = be * expf(Gx);
-  gt.EG[lane] = expf(G);
-  gt.EGnG[lane] = expf(Gn - G);
+  gt.bEGx[lane] = be * expf(static_cast<float>(Gx));
+  gt.EG[lane] = expf(static_cast<float>(G));
+  gt.EGnG[lane] = expf(static_cast<float>(Gn - G));
+}
+
+// exp(G_t - G_s) and exp(Gx_t - G_s) with the difference taken in double.
+__device__ __forceinline__ float decay_G(const ChunkGates& gt, int t, int s) {
+  return expf(static_cast<float>(gt.Gd[t] - gt.Gd[s]));
+}
+__device__ __forceinline__ float decay_Gx(const ChunkGates& gt, int t, int s) {
+  return expf(static_cast<float>(gt.Gxd[t] - gt.Gd[s]));
 }
 
 // One level of the off-diagonal blocks of the 64x64 inverse below: every

@@ -94,11 +94,12 @@ struct alignas(16) ProdScratch {  // one per producer wave, fp32 16x16 blocks, r
   float Aoff[16 * kSS];           // A_{p,p-1} (odd p)
   float Town[16 * kSS];           // T_pp
   // Per-token decay factors of this wave's blocks, indexed by token in chunk:
-  // diagonal block: G_t (cumulative log2 alpha), beta_t, 1/alpha_t and, when q and k are
-  // normalised in the kernel, G_t - log2 r_k(t) (column factor); off-diagonal block j (column
+  // diagonal block: G_t and Gx_t (inclusive and exclusive cumulative log2 alpha), beta_t and,
+  // when q and k are normalised in the kernel, G_t - log2 r_k(t) (column factor); off-diagonal
+  // block j (column
   // block C, last token r = 16 C + 15): beta_t e^(Gx_t - G_r), e^(G_t - G_r)
   // (rows) and e^(G_r - G_s) (columns).
-  float dG[64], dB[64], dR[64], dGk[64];
+  float dG[64], dB[64], dGx[64], dGk[64];
   float oA[2][64], oP[2][64], oS[2][64];
 };
 
@@ -251,13 +252,14 @@ __device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps
   const int t = 16 * R + l16;
   f32x4 av, pv;
   if constexpr (B == 0) {
-    // diagonal block: masks and one exp per element (both tokens in one block).
-    // With normalisation the column factor r_k(s) rides in the exponent
+    // diagonal block: masks and two exps per element (both tokens in one block):
+    // e^(G_t - G_s) for P and e^(Gx_t - G_s) for A, so that A never divides by
+    // alpha_t. With normalisation the column factor r_k(s) rides in the exponent
     // (G_s - log2 r_k(s)) and the row factors in per-row constants; the clamp
-    // only matters for the masked entries s > t.
-    const float Gt = ps.dG[t];
+    // only matters for the masked entries.
+    const float Gt = ps.dG[t], Gxt = ps.dGx[t];
     const f32x4 Gs = lds_f4(&(NORM ? ps.dGk : ps.dG)[16 * C + 4 * g]);
-    float ca = ps.dB[t] * ps.dR[t], cq = 1.f, ck = dh;  // beta_t / alpha_t, then r_k(t), r_q(t), d r_k(t)
+    float ca = ps.dB[t], cq = 1.f, ck = dh;  // beta_t, then r_k(t), r_q(t), d r_k(t)
     if constexpr (NORM) {
       const float rqt = bf.rn[0][t], rkt = bf.rn[1][t];
       ca *= rkt;
@@ -267,9 +269,10 @@ __device__ __forceinline__ void scale_block(ChunkBuf<K, VT>& bf, ProdScratch& ps
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s_ = 16 * C + 4 * g + i;
-      const float M = exp2_fast(fminf(Gt - Gs[i], NORM ? 64.f : 0.f));  // e^(G_t - G_s) [r_k(s)], s <= t
+      const float M = exp2_fast(fminf(Gt - Gs[i], NORM ? 64.f : 0.f));    // e^(G_t - G_s) [r_k(s)], s <= t
+      const float Mx = exp2_fast(fminf(Gxt - Gs[i], NORM ? 64.f : 0.f));  // e^(Gx_t - G_s) [r_k(s)], s < t
       const float kk = kk4[i];
-      av[i] = (s_ < t) ? ca * M * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
+      av[i] = (s_ < t) ? ca * Mx * kk : 0.f;  // beta_t e^(Gx_t - G_s) k_t.k_s
       pv[i] = (s_ <= t) ? (NORM ? qk[i] * cq - ck * kk : qk[i] - dh * kk) * M : 0.f;
     }
   } else {
@@ -355,7 +358,7 @@ __device__ __forceinline__ void offdiag_inverse(ChunkBuf<K, VT>& bf, const ProdS
 template <int D, int NB, int R1, int C1, int R2, int C2, bool NORM, bool SO, int K, int VT>
 __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch& ps, const ProdScratch& prev,
                                                 int* pair_flag, int chunk_tag, int lane, float dh,
-                                                float G, float lg, float rinv, float be, float rk) {
+                                                float G, float lg, float be, float rk) {
   constexpr int Rb[3] = {D, R1, R2};
   constexpr int Cb[3] = {D, C1, C2};
   const int g = lane >> 4, l16 = lane & 15;
@@ -364,7 +367,7 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
   // block's last token r: both factors lie in (0, 1], so no per-element exp.
   ps.dG[lane] = G;
   ps.dB[lane] = be;
-  ps.dR[lane] = rinv;
+  ps.dGx[lane] = G - lg;
   if constexpr (NORM) ps.dGk[lane] = G - __builtin_amdgcn_logf(rk);
 #pragma unroll
   for (int b = 1; b < NB; ++b) {
@@ -477,9 +480,9 @@ template <int K, int V, int VT, typename OutT, bool NORM, bool SO, bool PAIR>
 __device__ __forceinline__ void chunk_fwd_bf16_body(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
-    const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
-    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck, float* __restrict__ sf2) {
+    const float* s0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* o,
+    float* sf, unsigned fusion, float* hck, float* sf2) {
   static_assert(VT == 64, "four consumer wavefronts of 16 channels");
   static_assert(!PAIR || (SO && K == V), "the paired pass is state-only, with K == V");
   constexpr int NVT = V / VT, NT = PAIR ? 768 : 512;
@@ -644,7 +647,6 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
         // smallest normal float so that the hardware log stays finite.
         const float lg = __builtin_amdgcn_logf(fmaxf(a, 1.17549435e-38f));
         const float G = wave_scan_dpp(lg);
-        const float rinv = __builtin_amdgcn_rcpf(a);
         const float rql = NORM ? bf.rn[0][lane] : 1.f, rkl = NORM ? bf.rn[1][lane] : 1.f;
         if (p == 0) {
           const float Gn = __shfl(G, 63, kWave);
@@ -665,10 +667,10 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
         __builtin_amdgcn_s_setprio(2);
         const int tag = it + 1;
         switch (p) {
-          case 0: producer_blocks<0, 3, 3, 0, 3, 1, NORM, SO>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
-          case 1: producer_blocks<1, 2, 1, 0, 0, 0, NORM, SO>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, rinv, be, rkl); break;
-          case 2: producer_blocks<2, 3, 2, 0, 2, 1, NORM, SO>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
-          default: producer_blocks<3, 2, 3, 2, 0, 0, NORM, SO>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, rinv, be, rkl); break;
+          case 0: producer_blocks<0, 3, 3, 0, 3, 1, NORM, SO>(bf, sm.ps[0], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, be, rkl); break;
+          case 1: producer_blocks<1, 2, 1, 0, 0, 0, NORM, SO>(bf, sm.ps[1], sm.ps[0], &sm.pair_flag[0], tag, olane, dh, G, lg, be, rkl); break;
+          case 2: producer_blocks<2, 3, 2, 0, 2, 1, NORM, SO>(bf, sm.ps[2], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, be, rkl); break;
+          default: producer_blocks<3, 2, 3, 2, 0, 0, NORM, SO>(bf, sm.ps[3], sm.ps[2], &sm.pair_flag[1], tag, olane, dh, G, lg, be, rkl); break;
         }
         __builtin_amdgcn_s_setprio(0);
       }
@@ -940,9 +942,9 @@ template <int K, int V, int VT, typename OutT, bool NORM, bool SO>
 __global__ __launch_bounds__(512) void chunk_fwd_bf16_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
-    const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
-    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck) {
+    const float* s0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* o,
+    float* sf, unsigned fusion, float* hck) {
   chunk_fwd_bf16_body<K, V, VT, OutT, NORM, SO, false>(q, k, v, alpha, beta, d, s0, cu_seqlens, order, T, H, Hk, N,
                                                         o, sf, fusion, hck, nullptr);
 }
@@ -953,8 +955,8 @@ template <int K, int VT, bool NORM>
 __global__ __launch_bounds__(768) void chunk_fwd_bf16_pair_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
-    const int32_t* __restrict__ cu_seqlens, int T, int H, int Hk, int N, float* __restrict__ sf, unsigned fusion,
-    float* __restrict__ sf2) {
+    const int32_t* __restrict__ cu_seqlens, int T, int H, int Hk, int N, float* sf, unsigned fusion,
+    float* sf2) {
   chunk_fwd_bf16_body<K, K, VT, u16, NORM, true, true>(q, k, v, alpha, beta, d, nullptr, cu_seqlens, nullptr, T, H,
                                                        Hk, N, nullptr, sf, fusion, nullptr, sf2);
 }

@@ -29,9 +29,9 @@ template <int K, int V, typename OutT>
 __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const float* __restrict__ d,
-    const float* __restrict__ s0, const int32_t* __restrict__ cu_seqlens,
-    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* __restrict__ o,
-    float* __restrict__ sf, unsigned fusion, float* __restrict__ hck) {
+    const float* s0, const int32_t* __restrict__ cu_seqlens,
+    const int32_t* __restrict__ order, int T, int H, int Hk, int N, OutT* o,
+    float* sf, unsigned fusion, float* hck) {
   constexpr int NT = 256, VT = SmemF32<K>::VT, LDH = SmemF32<K>::LDH, NVT = V / VT, LQ = K + 1;
   __shared__ SmemF32<K> sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void chunk_fwd_fp32_kernel(
         qk += sm.Qs[t * LQ + c] * sm.Ks[s * LQ + c];
         kk += sm.Ks[t * LQ + c] * sm.Ks[s * LQ + c];
       }
-      sm.Am[t * kLdF + s] = (s < t) ? sm.gt.beta[t] * expf(sm.gt.Gx[t] - sm.gt.G[s]) * kk : 0.f;
-      sm.Pm[t * kLdF + s] = (s <= t) ? (qk - dh * kk) * expf(sm.gt.G[t] - sm.gt.G[s]) : 0.f;
+      sm.Am[t * kLdF + s] = (s < t) ? sm.gt.beta[t] * decay_Gx(sm.gt, t, s) * kk : 0.f;
+      sm.Pm[t * kLdF + s] = (s <= t) ? (qk - dh * kk) * decay_G(sm.gt, t, s) : 0.f;
     }
     __syncthreads();
     unit_lower_inverse64<NT>(sm.Am, sm.Tm, sm.Ys, tid);

@@ -71,6 +71,16 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
+// The same in double.
+__device__ __forceinline__ double wave_inclusive_scan_f64(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    double y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static float load(const float* p, int64_t i) { return p[i]; }

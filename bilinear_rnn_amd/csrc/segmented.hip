@@ -38,9 +38,9 @@ __global__ __launch_bounds__(256) void segment_bounds_kernel(int B, int T, int L
 // 16-byte loads into registers, then into the other half of a double-buffered
 // LDS copy. After the last segment X_S is the sequence's final state.
 template <int K>
-__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ s0, const float* __restrict__ bst,
+__global__ __launch_bounds__(256) void segment_scan_kernel(const float* s0, const float* __restrict__ bst,
                                                            const float* __restrict__ phi, float* __restrict__ X,
-                                                           float* __restrict__ sf, int H, int V, int S) {
+                                                           float* sf, int H, int V, int S) {
   typedef float f4 __attribute__((ext_vector_type(4)));
   constexpr int RB = 8, RG = 256 / K, RPT = RB / RG, PP = K * K / 4 / 256;
   static_assert(RPT >= 1 && PP * 4 * 256 == K * K, "whole pieces per thread");
