@@ -93,7 +93,7 @@ def test_single_fusion_flags(dtype, gate_logits, qk_l2norm):
     ro, rs = oracle_of(inp, gate_logits=gate_logits, qk_l2norm=qk_l2norm)
     flags = dict(gate_logits=gate_logits, qk_l2norm=qk_l2norm)
     o, s = run_chunk(inp, out_dtype=torch.float32, **flags)
-    gate = GATE_FP32 if dtype == "fp32" else GATE_BF16_IN_FP32_OUT
+    gate = FP32 if dtype == "fp32" else BF16_IN_FP32_OUT
     assert_close(o, ro, gate, "o")
     assert_close(s, rs, gate, "state")
     o, s = run_step(inp, out_dtype=torch.float32, **flags)

@@ -59,7 +59,6 @@ def test_most_heads_forward_recurrent_backward(dtype):
     print(f"max heads: H={MAX_H} K=V=128 T=100 {dtype}", flush=True)
     w = dataclasses.replace(WORKLOADS["layer_1p3b"], dtype=dtype)
     inp = make_inputs(w, B=1, T=100, H=MAX_H, s0_std=0.02, seed=2201)
-    gate = GATE_BF16 if dtype == "bf16" else GATE_FP32
     t = dev_inputs(inp)
     o, sf = comba.chunk_fwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], t["initial_state"])
     ro_, rs_ = comba.recurrent_step(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], t["initial_state"])
