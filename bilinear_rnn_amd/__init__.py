@@ -6,6 +6,7 @@ correction, as hand-written HIP kernels behind a C ABI (include/comba.h).
 This package is the thin Python binding over that library.
 """
 from .api import (CombaError, bwd_cached_workspace_size, bwd_workspace_size, chunk_bwd, chunk_fwd,  # noqa: F401
+                  chunk_fwd_noalloc,
                   chunk_states_size, lib, library_path,
                   mfma_peak_probe, recurrent_step, segmented_workspace_size, varlen_order, workspace_size)
 

@@ -33,7 +33,7 @@ EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_chunk_fwd_segmented_workspace_size",
             "comba_chunk_fwd_segmented", "comba_chunk_bwd_workspace_size", "comba_chunk_bwd",
             "comba_varlen_order", "comba_mfma_peak_probe", "comba_chunk_states_size", "comba_chunk_fwd_keep_states",
-            "comba_chunk_bwd_cached_workspace_size", "comba_chunk_bwd_cached")
+            "comba_chunk_bwd_cached_workspace_size", "comba_chunk_bwd_cached", "comba_chunk_fwd_noalloc")
 
 
 class CombaError(RuntimeError):
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
         L.comba_chunk_bwd_cached.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32, i32, vp,
                                              fp, fp, sz, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
         L.comba_chunk_bwd_cached.restype = i32
+        L.comba_chunk_fwd_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, ip, i32, i32, i32, i32, i32, i32,
+                                              i32, i32, vp, fp, vp]
+        L.comba_chunk_fwd_noalloc.restype = i32
         L.comba_mfma_peak_probe.argtypes = [fp, i32, i32, vp]
         L.comba_mfma_peak_probe.restype = i32
         _lib = L
@@ -252,6 +255,35 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
             _check(L.comba_chunk_fwd_fused(*head, *tail, fusion, ctypes.c_void_p(stream)))
         else:
             _check(L.comba_chunk_fwd(*head, *tail, ctypes.c_void_p(stream)))
+    return out, final_state
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                      beta: torch.Tensor, d: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+                      cu_seqlens: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                      output_final_state: bool = True, out: Optional[torch.Tensor] = None,
+                      final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunk-wise forward through ``comba_chunk_fwd_noalloc``: no workspace; the
+    library keeps the packed-sequence order in its own device array (at most
+    16384 sequences; calls that overlap in time on one GPU race). Pass ``out``
+    and ``final_state`` to keep the call itself free of allocations."""
+    B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    if Hk != H:
+        raise ValueError("chunk_fwd_noalloc takes one q / k head per value head")
+    L = lib()
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
+    _require(out, "out", out_dtype, (B, T, H, V))
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+    if final_state is not None:
+        _require(final_state, "final_state", torch.float32, (N, H, V, K))
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        _check(L.comba_chunk_fwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(d), _ptr(initial_state), _ptr(cu_seqlens),
+            N if cu_seqlens is not None else 0, B, T, H, K, V, _DT[q.dtype], _DT[out_dtype], _ptr(out),
+            _ptr(final_state), ctypes.c_void_p(stream)))
     return out, final_state
 
 

@@ -1,7 +1,9 @@
 // C ABI entry points (declared in include/comba.h): host-side validation,
 // workspace carving and kernel launches on the caller's stream.
+#include <atomic>
 #include <climits>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "comba.h"
@@ -17,6 +19,21 @@ thread_local std::string g_last_error;
 // Above this many packed sequences the longest-first order (quadratic in N)
 // is skipped and sequences run in their given order.
 constexpr int kMaxOrderedSeqs = 16384;
+
+}  // namespace
+
+// Device scratch of comba_chunk_fwd_noalloc: the longest-first order of up to
+// kMaxOrderedSeqs packed sequences (64 KiB). Each GPU holds its own copy until
+// the process ends, and every call on that GPU shares it. In host code this
+// name is only a stand-in for the symbol: kernels and copies take the address
+// that hipGetSymbolAddress returns for the device (scratch_on below).
+__device__ __align__(256) int32_t scratch[kMaxOrderedSeqs];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
 
 int32_t fail(int32_t code, const char* what) {
   g_last_error = what;
@@ -174,6 +191,73 @@ COMBA_API int32_t comba_chunk_fwd_ex(const void* q, const void* k, const void* v
                                      size_t workspace_bytes, uint32_t fusion, void* stream) {
   return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, num_qk_heads, K, V,
                         in_dtype, out_dtype, o, final_state, workspace, workspace_bytes, fusion, stream);
+}
+
+namespace {
+
+// Device address of `scratch` on the GPU that runs `stream` (the current
+// device for the null stream): looked up once per device with that device
+// current, then kept.
+int32_t scratch_on(void* stream, int32_t** out) {
+  int dev = -1;
+  hipError_t e;
+  if (stream) {
+    hipDevice_t d = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &d);
+    dev = static_cast<int>(d);
+  } else {
+    e = hipGetDevice(&dev);
+  }
+  if (e != hipSuccess) return fail(COMBA_ERR_HIP, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(COMBA_ERR_UNSUPPORTED, "device ordinal beyond 63");
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+      void* addr = nullptr;
+      if (e == hipSuccess) e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (cur >= 0 && cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess || !addr)
+        return fail(COMBA_ERR_HIP, e != hipSuccess ? hipGetErrorString(e) : "no device address for the scratch array");
+      p = static_cast<int32_t*>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return COMBA_OK;
+}
+
+}  // namespace
+
+COMBA_API int32_t comba_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* alpha,
+                                          const float* beta, const float* d, const float* initial_state,
+                                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t B, int32_t T,
+                                          int32_t H, int32_t K, int32_t V, int32_t in_dtype, int32_t out_dtype,
+                                          void* o, float* final_state, void* stream) {
+  comba::FwdArgs a;  // host-side checks first, so that bad arguments never reach the device lookup
+  int32_t rc = check_args(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V,
+                          in_dtype, out_dtype, o, final_state, a);
+  if (rc != COMBA_OK) return rc;
+  int32_t* order = nullptr;
+  size_t order_bytes = 0;
+  if (cu_seqlens) {
+    if (num_seqs > kMaxOrderedSeqs)
+      return fail(COMBA_ERR_UNSUPPORTED,
+                  "comba_chunk_fwd_noalloc takes at most 16384 packed sequences (its device scratch holds the "
+                  "order of 16384); use comba_chunk_fwd with a workspace");
+    rc = scratch_on(stream, &order);
+    if (rc != COMBA_OK) return rc;
+    order_bytes = sizeof(int32_t) * kMaxOrderedSeqs;
+  }
+  return chunk_fwd_impl(q, k, v, alpha, beta, d, initial_state, cu_seqlens, num_seqs, B, T, H, H, K, V, in_dtype,
+                        out_dtype, o, final_state, order, order_bytes, 0u, stream);
 }
 
 COMBA_API size_t comba_chunk_states_size(int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,

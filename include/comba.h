@@ -117,6 +117,29 @@ int32_t comba_chunk_fwd(const void* q, const void* k, const void* v,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * comba_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, results and errors as
+ * comba_chunk_fwd, which it runs with the same kernels.
+ *
+ * The longest-first order of packed sequences goes to a device array inside
+ * the library instead of a workspace: 64 KiB per GPU, held until the process
+ * ends, for at most 16384 sequences (more return COMBA_ERR_UNSUPPORTED). Its
+ * device address is looked up on the first call per GPU. Every call on one
+ * GPU shares that array, so calls that overlap in time on one GPU (on two
+ * streams without ordering between them) race and give unspecified values;
+ * calls ordered on one stream are safe. The call never allocates, frees or
+ * synchronises.
+ */
+int32_t comba_chunk_fwd_noalloc(const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* d,
+                                const float* initial_state,
+                                const int32_t* cu_seqlens, int32_t num_seqs,
+                                int32_t B, int32_t T, int32_t H, int32_t K, int32_t V,
+                                int32_t in_dtype, int32_t out_dtype,
+                                void* o, float* final_state, void* stream);
+
+/*
  * Recurrent form (write-up, section "硬件高效的分块并行计算": the token-by-
  * token recurrence), one token after another from the initial state. With
  * T == 1 this is the single-token decode step of generation. Per value row i:

@@ -86,6 +86,17 @@ def segmented(fusion=0, nseg=4, **kw):
                                        args["wsb"], fusion, None)
 
 
+def chunk_noalloc(fusion=None, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, alpha=FAKE, beta=FAKE, d=FAKE, s0=None, cu=None, n=0,
+                B=1, T=1, H=2, K=64, V=64, idt=0, odt=0, o=FAKE, sf=None)
+    args.update(kw)
+    if fusion is not None:  # no fusion argument on this entry point: map onto an invalid call
+        args["q"] = None
+    return comba.lib().comba_chunk_fwd_noalloc(
+        args["q"], args["k"], args["v"], args["alpha"], args["beta"], args["d"], args["s0"], args["cu"], args["n"],
+        args["B"], args["T"], args["H"], args["K"], args["V"], args["idt"], args["odt"], args["o"], args["sf"], None)
+
+
 def chunk_fused(**kw):
     return chunk(fusion=api.COMBA_FUSE_GATE_LOGITS | api.COMBA_FUSE_QK_L2NORM, **kw)
 
@@ -94,7 +105,7 @@ def step_fused(**kw):
     return step(fusion=api.COMBA_FUSE_QK_L2NORM, **kw)
 
 
-@pytest.mark.parametrize("fn", [chunk, step, chunk_fused, step_fused, segmented])
+@pytest.mark.parametrize("fn", [chunk, step, chunk_fused, step_fused, segmented, chunk_noalloc])
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(alpha=None), -1),
     (dict(beta=None), -1), (dict(d=None), -1), (dict(o=None), -1),
@@ -274,3 +285,10 @@ def test_python_binding_rejects_host_tensors():
     a = torch.ones(1, 4, 2)
     with pytest.raises(ValueError):
         comba.chunk_fwd(x, x, x, a, a, torch.zeros(2))
+
+
+def test_noalloc_rejects_more_packed_sequences_than_its_scratch():
+    """The allocation-free forward keeps the packed-sequence order in a device
+    array of 16384 entries: more sequences are refused on the host."""
+    assert chunk_noalloc(cu=FAKE, n=16385, T=16385) == api.COMBA_ERR_UNSUPPORTED
+    assert "16384" in api.last_error()
