@@ -14,7 +14,9 @@ from typing import Optional, Tuple
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcomba.so")
+# COMBA_LIBRARY names another build of the same library (the host-sanitizer build of
+# the CPU checks); by default the in-tree libcomba.so.
+_LIB_PATH = os.environ.get("COMBA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcomba.so")
 _lib = None
 
 COMBA_OK = 0

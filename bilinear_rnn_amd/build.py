@@ -72,5 +72,45 @@ def build(verbose: bool = True) -> str:
     return LIB
 
 
+# Host-side address and undefined-behaviour sanitizers for the CPU checks of
+# the C ABI (argument validation, workspace carving): each -fsanitize flag
+# applies to the host pass only, device code is built as usual.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build_sanitized(out_dir: str) -> str:
+    """libcomba.so with the host code under ASan and UBSan, written to
+    out_dir/libcomba_san.so. Load it through COMBA_LIBRARY with the compiler's
+    ASan runtime preloaded (sanitizer_runtime())."""
+    os.makedirs(out_dir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-O3"] + ["-O1", "-g"] + SANITIZE_HOST
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src).replace(".hip", ".o"))
+        res = subprocess.run([_hipcc(), *flags, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj],
+                             stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{res.stdout}")
+        return obj
+
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(sources()))) as ex:
+        objs = list(ex.map(one, sources()))
+    lib = os.path.join(out_dir, "libcomba_san.so")
+    subprocess.check_call([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", lib, *objs])
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's shared ASan runtime (it carries the UBSan handlers too)."""
+    out = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                         stderr=subprocess.DEVNULL, text=True).stdout.strip()
+    if not out or not os.path.isabs(out) or not os.path.exists(out):
+        import glob
+        hits = glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so")
+        out = hits[0] if hits else ""
+    return out
+
+
 if __name__ == "__main__":
     build()

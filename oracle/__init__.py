@@ -25,18 +25,31 @@ from .reference import (comba_backward, comba_forward, comba_forward_chunked, ex
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "comba_oracle.c")
-_LIB = os.path.join(_HERE, "libcomba_oracle.so")
+# COMBA_ORACLE_LIBRARY names another build of comba_oracle.c (the sanitizer build of
+# the CPU checks); by default the one build_c() writes here.
+_DEFAULT_LIB = os.path.join(_HERE, "libcomba_oracle.so")
+_LIB = os.environ.get("COMBA_ORACLE_LIBRARY") or _DEFAULT_LIB
 _lib = None
 
 
 def build_c(force: bool = True) -> str:
     """Compile the C oracle with gcc (-O2, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+    if force or not os.path.exists(_DEFAULT_LIB):
+        tmp = _DEFAULT_LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11",
                                "-Wall", "-Wextra", "-o", tmp, _SRC])
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, _DEFAULT_LIB)
+    return _DEFAULT_LIB
+
+
+def build_c_sanitized(path: str) -> str:
+    """The same source under gcc's address and undefined-behaviour sanitizers
+    (any undefined behaviour aborts), for the CPU checks. Load it through
+    COMBA_ORACLE_LIBRARY with gcc's libasan and libubsan preloaded."""
+    subprocess.check_call(["gcc", "-O1", "-g", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall", "-Wextra",
+                           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                           "-fno-omit-frame-pointer", "-o", path, _SRC])
+    return path
 
 
 def _load():
