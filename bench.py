@@ -196,6 +196,43 @@ def record_traffic(fetch_dir, write_dir):
     _record_one(frows, wrows, _is_decode, DECODE_COUNTERS_JSON,
                 f"recurrent_kernel<{wd.K},{wd.V},32,bf16,bf16> on the decode workload ({wd.B} x {wd.H} heads, K={wd.K} V={wd.V})",
                 kernel_source_hash(DECODE_SOURCES), 2 * ht * wd.V * wd.K * 4 + ht * (2 * wd.K * 2 + 2 * wd.V * 2 + 8))
+    record_bwd_traffic(frows, wrows)
+
+
+BWD_COUNTERS_JSON = os.path.join(ROOT, "profiles", "chunk_bwd_layer_1p3b_counters.json")
+BWD_SOURCES = ("chunk_bwd.hip", "chunk_fwd_bf16.hip", "chunk_common.h", "device_common.h", "bf16_tiles.h",
+               "launch.h")
+BWD_KERNELS = (("checkpointing forward", "chunk_fwd_bf16_kernel<128, 128, 64, unsigned short, false, true>"),
+               ("prep", "chunk_bwd_prep_kernel<128, unsigned short>"),
+               ("reverse scan", "chunk_bwd_dh_bf16_kernel<128, 128>"),
+               ("gradient pass", "chunk_bwd_grad_bf16_kernel<128, 128>"),
+               ("dd reduction", "dd_reduce_kernel"))
+
+
+def record_bwd_traffic(frows, wrows):
+    """Calibrated HBM bytes per launch of each kernel of the 1.3B-layer
+    backward, and their sum against the backward's algorithmic floor."""
+    out = {"kernels": {}, "kernel_source_hash": kernel_source_hash(BWD_SOURCES)}
+    total = 0.0
+    for label, pat in BWD_KERNELS:
+        f = _kernel_and_copy(frows, "FETCH_SIZE", lambda n, p=pat: p in n)
+        w = _kernel_and_copy(wrows, "WRITE_SIZE", lambda n, p=pat: p in n)
+        if f is None or w is None:
+            continue
+        rd = f[0] * 1024.0 * COPY_CAL_BYTES / (f[2] * 1024.0)
+        wr = w[0] * 1024.0 * COPY_CAL_BYTES / (w[2] * 1024.0)
+        out["kernels"][label] = {"kernel": pat, "hbm_read_bytes": rd, "hbm_write_bytes": wr, "dispatches": [f[1], w[1]]}
+        total += rd + wr
+    if not out["kernels"]:
+        print("no backward dispatches in the counted runs")
+        return
+    out["hbm_bytes_per_backward"] = total
+    out["algorithmic_bytes"] = chunk_bwd_algorithmic(8, 4096, 16, 128, 128)[0]
+    out["traffic_over_algorithmic"] = total / out["algorithmic_bytes"]
+    with open(BWD_COUNTERS_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def _record_one(frows, wrows, is_kernel, path, label, src_hash, nbytes):
@@ -271,24 +308,25 @@ def summarize_counters(dirs, kernel_regex, out_md, title, command):
                 lines.append(f"- VALU other than MFMA: {(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / w:,.0f}")
         g = m.get("GRBM_GUI_ACTIVE")
         if g:
-            lines += ["", "Rates (GRBM_GUI_ACTIVE = kernel duration in GPU clock cycles):", ""]
+            cyc = g / 8.0  # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+            lines += ["", f"Derived (kernel length = GRBM_GUI_ACTIVE / 8 XCDs = {cyc:,.0f} cycles; 1024 SIMDs):", ""]
             if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
-                lines.append(f"- MFMA busy: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (g * 1024):.1%} of SIMD cycles "
-                             "(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs))")
-            if "SQ_WAVE_CYCLES" in m and "SQ_WAIT_INST_ANY" in m:
-                lines.append(f"- waiting for an instruction dependency: {m['SQ_WAIT_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1%} "
-                             "of wave cycles (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)")
-            if "SQ_WAVE_CYCLES" in m and "SQ_WAIT_ANY" in m:
-                lines.append(f"- waiting for anything: {m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.1%} of wave cycles")
-            if "SQ_WAVE_CYCLES" in m and "SQ_ACTIVE_INST_ANY" in m:
-                lines.append(f"- issuing: {m['SQ_ACTIVE_INST_ANY'] / m['SQ_WAVE_CYCLES']:.1%} of wave cycles "
-                             "(SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES)")
-            if "SQ_WAVE_CYCLES" in m and "SQ_ACTIVE_INST_VALU" in m:
-                lines.append(f"- VALU (incl. MFMA issue) active: {m['SQ_ACTIVE_INST_VALU'] / m['SQ_WAVE_CYCLES']:.1%} "
-                             "of wave cycles")
-            if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m:
+                lines.append(f"- matrix cores busy: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.1%} of SIMD cycles "
+                             "(SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024))")
+            if "SQ_ACTIVE_INST_VALU" in m:
+                lines.append(f"- VALU issue (MFMA issue included) busy: "
+                             f"{4 * m['SQ_ACTIVE_INST_VALU'] / (cyc * 1024):.1%} of SIMD cycles "
+                             "(4 x SQ_ACTIVE_INST_VALU quad-cycles / (cycles x 1024))")
+            if m.get("SQ_WAVE_CYCLES"):
+                for c, what in (("SQ_ACTIVE_INST_ANY", "issuing an instruction"),
+                                ("SQ_WAIT_INST_ANY", "waiting for an instruction's operands (s_waitcnt)"),
+                                ("SQ_WAIT_ANY", "waiting for anything else (barriers, sleeps)")):
+                    if c in m:
+                        lines.append(f"- wavefronts {what}: {m[c] / m['SQ_WAVE_CYCLES']:.1%} of wave cycles "
+                                     f"({c} / SQ_WAVE_CYCLES)")
+            if m.get("SQ_LDS_IDX_ACTIVE"):
                 lines.append(f"- LDS bank-conflict cycles: {m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.1%} "
-                             "of LDS-active cycles")
+                             "of LDS-active cycles (SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE)")
         lines.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
@@ -322,11 +360,11 @@ def time_loop(torch, fn, steps, warmup, floor_s=None):
     calls."""
     floor_s = WARMUP_FLOOR_S if floor_s is None else floor_s
     t_w = time.perf_counter()
-    i = 0
-    while i < warmup or time.perf_counter() - t_w < floor_s:
-        fn(i)
-        i += 1
-        if i % 10 == 0:
+    nwarm = 0
+    while nwarm < warmup or time.perf_counter() - t_w < floor_s:
+        fn(nwarm)
+        nwarm += 1
+        if nwarm % 10 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -338,7 +376,7 @@ def time_loop(torch, fn, steps, warmup, floor_s=None):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    time_loop.last_warmup = i
+    time_loop.last_warmup = nwarm
     return start.elapsed_time(end) / steps, wall
 
 
