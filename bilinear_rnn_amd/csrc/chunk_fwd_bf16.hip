@@ -57,13 +57,31 @@ namespace comba {
 constexpr int kTP = 32 * 32 + 32 * 64;  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
 
 __device__ __forceinline__ int tp_off(int row, int pos) {
-  // rows 0-31: 32 per row, chunks swizzled by row & 3; rows 32-63: 64 per row
-  // after the first 1024, swizzled by row & 7 (arithmetic, no branch)
+  // rows 0-31: 32 per row (64 bytes: four rows per 256-byte bank span), 16-byte
+  // chunks swizzled by (row >> 2) & 3; rows 32-63: 64 per row after the first
+  // 1024 (two rows per span), swizzled by (row >> 1) & 7. Sixteen consecutive
+  // rows then cover all 64 banks once for a fixed logical chunk.
   const int big = row >> 5;
   const int base = row * (32 << big) - 1024 * big;
-  const int mask = 3 | (big << 2);
-  return base + (((pos >> 3) ^ (row & mask)) << 3) + (pos & 7);
+  const int sw = big ? (row >> 1) & 7 : (row >> 2) & 3;
+  return base + (((pos >> 3) ^ sw) << 3) + (pos & 7);
 }
+
+// Offset of position pos of row `row` in a q / k tile (K bf16 per row). K = 128:
+// the 16-byte chunk is XOR-ed with the row's low two bits moved up and its next
+// two bits moved down, so that sixteen consecutive rows at one chunk (a row
+// fragment) and four consecutive rows at four consecutive chunks (a transposed
+// read) both land on distinct banks; K = 64 keeps the plain row swizzle.
+template <int K>
+__device__ __forceinline__ int qk_off(int row, int pos) {
+  if constexpr (K == 128) {
+    const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+    return row * K + (((pos >> 3) ^ sw) << 3) + (pos & 7);
+  } else {
+    return swz<K>(row, pos);
+  }
+}
+
 // Position of row t of a chunk in the lane-ordered gate arrays: lane group g
 // of a consumer reads its 16 rows t = 16 r4 + 4 g + i as four float4.
 __device__ __forceinline__ int gate_pos(int t) { return ((t >> 2) & 3) * 16 + (t >> 4) * 4 + (t & 3); }
@@ -167,8 +185,8 @@ template <int K>
 __device__ __forceinline__ bf16x8 kt_frag(const u16* Kc, int kb, int s2, int g, int l16) {
   const int pos = perm_col(16 * kb + 4 * (l16 & 3));
   const int row0 = 32 * s2 + 4 * g + (l16 >> 2);
-  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(Kc + swz<K>(row0, pos)));
-  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(Kc + swz<K>(row0 + 16, pos)));
+  const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(Kc + qk_off<K>(row0, pos)));
+  const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(Kc + qk_off<K>(row0 + 16, pos)));
   // Whole-vector reinterpretation: element-wise short -> __bf16 casts of the
   // transposed-read result are folded into a splat of element 0 by this compiler.
   const s8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -390,10 +408,10 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
   for (int s = 0; s < K / 32; ++s) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const bf16x8 ak = lds8(&bf.Kc[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
-      const bf16x8 bk = lds8(&bf.Kc[swz<K>(16 * Cb[b] + l16, 32 * s + 8 * g)]);
+      const bf16x8 ak = lds8(&bf.Kc[qk_off<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
+      const bf16x8 bk = lds8(&bf.Kc[qk_off<K>(16 * Cb[b] + l16, 32 * s + 8 * g)]);
       if constexpr (!SO) {  // q k^T only feeds P, which a state-only pass does not form
-        const bf16x8 aq = lds8(&bf.Q[swz<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
+        const bf16x8 aq = lds8(&bf.Q[qk_off<K>(16 * Rb[b] + l16, 32 * s + 8 * g)]);
         aqk[b] = mfma16x16x32(bk, aq, aqk[b]);
       }
       akk[b] = mfma16x16x32(bk, ak, akk[b]);
@@ -537,11 +555,15 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
     // arithmetic. Rows past the end of the sequence lie beyond the chunk's
     // buffer range and load as zeros (the padding the chunk algebra needs).
     int qkoff[QPT], voff[VPT];
+    // Row of this thread's q / k piece j (column ptid % KP): for K = 128 the four
+    // 16-lane groups of a wavefront take rows four apart, which keeps each
+    // 32-lane phase of the 8-byte LDS writes on distinct banks.
+    auto qk_row = [&](int j) {
+      if constexpr (K == 128) return 16 * j + 4 * ((ptid >> 4) & 3) + (ptid >> 6);
+      else return (ptid + j * 256) / KP;
+    };
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int piece = ptid + j * 256, row = piece / KP, c8 = piece % KP;
-      qkoff[j] = (row * Hk * K + c8 * 8) * 2;
-    }
+    for (int j = 0; j < QPT; ++j) qkoff[j] = (qk_row(j) * Hk * K + ptid % KP * 8) * 2;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR;
@@ -578,6 +600,12 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
         }
       }
     };
+    // LDS offsets of this thread's first q / k pieces (two 8-byte halves in perm32
+    // order) and first v piece; 256 is a multiple of the pieces per row, so every
+    // later piece keeps the column and the row's swizzle phase
+    static_assert(256 % KP == 0 && 256 % VPR == 0, "a thread's pieces share their column");
+    const int sq0 = qk_off<K>(qk_row(0), perm_col(ptid % KP * 8)), sq1 = qk_off<K>(qk_row(0), perm_col(ptid % KP * 8 + 4));
+    const int sv0 = swz<VT>(ptid / VPR, ptid % VPR * 8);
     if (nchunks > 0) fetch(t0);
     for (int it = 0; it <= nchunks; ++it) {
       if (it < nchunks) {
@@ -587,19 +615,20 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
         // variants out of the loop (which exhausts the registers and spills).
         int olane;
         asm volatile("v_mov_b32 %0, %1" : "=v"(olane) : "v"(lane));
+        // Piece j of a thread lies 256 / KP (q, k) or 256 / VPR (v) rows below its
+        // piece 0, in the same column and swizzle phase: a fixed offset each.
 #pragma unroll
         for (int j = 0; j < QPT; ++j) {
-          const int piece = ptid + j * 256, row = piece / KP, c8 = piece % KP;
-          const int p0 = perm_col(c8 * 8), p1 = perm_col(c8 * 8 + 4);
-          *reinterpret_cast<uint2*>(&bf.Q[swz<K>(row, p0)]) = make_uint2(rq[j].x, rq[j].y);
-          *reinterpret_cast<uint2*>(&bf.Q[swz<K>(row, p1)]) = make_uint2(rq[j].z, rq[j].w);
-          *reinterpret_cast<uint2*>(&bf.Kc[swz<K>(row, p0)]) = make_uint2(rk[j].x, rk[j].y);
-          *reinterpret_cast<uint2*>(&bf.Kc[swz<K>(row, p1)]) = make_uint2(rk[j].z, rk[j].w);
+          constexpr int dr = 256 / KP * K;
+          *reinterpret_cast<uint2*>(&bf.Q[sq0 + j * dr]) = make_uint2(rq[j].x, rq[j].y);
+          *reinterpret_cast<uint2*>(&bf.Q[sq1 + j * dr]) = make_uint2(rq[j].z, rq[j].w);
+          *reinterpret_cast<uint2*>(&bf.Kc[sq0 + j * dr]) = make_uint2(rk[j].x, rk[j].y);
+          *reinterpret_cast<uint2*>(&bf.Kc[sq1 + j * dr]) = make_uint2(rk[j].z, rk[j].w);
         }
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-          const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR;
-          *reinterpret_cast<u32x4*>(&bf.Vv[swz<VT>(row, c8 * 8)]) = rv[j];
+          constexpr int dr = 256 / VPR * VT;
+          *reinterpret_cast<u32x4*>(&bf.Vv[sv0 + j * dr]) = rv[j];
         }
         const int nrows_c = min(64, t1 - (t0 + it * 64));
         if (ptid < 64) {
@@ -636,7 +665,7 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
           const float tot = group_sums_scatter<KP>(ss, ptid);
           const int idx = (ptid >> 1) & (2 * QPT - 1), j = idx % QPT;
           if ((ptid & 1) == 0)
-            bf.rn[idx / QPT][ptid / KP + j * (256 / KP)] = __builtin_amdgcn_rsqf(tot + kL2NormEps);
+            bf.rn[idx / QPT][qk_row(j)] = __builtin_amdgcn_rsqf(tot + kL2NormEps);
         }
         producer_sync(&sm.prod_bar, epoch, lane);
 
@@ -718,8 +747,8 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
         // scheduling barriers keep that order, so the products rarely wait on
         // LDS latency.
         constexpr int NS = K / 32;  // 32-wide reduction steps over the key dimension
-        auto kfrag = [&](int r4, int s_) { return lds8(&bf.Kc[swz<K>(16 * r4 + l16, 32 * s_ + 8 * g)]); };
-        auto qfrag = [&](int r4, int s_) { return lds8(&bf.Q[swz<K>(16 * r4 + l16, 32 * s_ + 8 * g)]); };
+        auto kfrag = [&](int r4, int s_) { return lds8(&bf.Kc[qk_off<K>(16 * r4 + l16, 32 * s_ + 8 * g)]); };
+        auto qfrag = [&](int r4, int s_) { return lds8(&bf.Q[qk_off<K>(16 * r4 + l16, 32 * s_ + 8 * g)]); };
 
         bf16x8 hbh[NS], hbl[NS];
 #pragma unroll
