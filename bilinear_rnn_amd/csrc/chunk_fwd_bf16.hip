@@ -67,19 +67,18 @@ __device__ __forceinline__ int tp_off(int row, int pos) {
   return base + (((pos >> 3) ^ sw) << 3) + (pos & 7);
 }
 
-// Offset of position pos of row `row` in a q / k tile (K bf16 per row). K = 128:
-// the 16-byte chunk is XOR-ed with the row's low two bits moved up and its next
-// two bits moved down, so that sixteen consecutive rows at one chunk (a row
-// fragment) and four consecutive rows at four consecutive chunks (a transposed
-// read) both land on distinct banks; K = 64 keeps the plain row swizzle.
+// Offset of position pos of row `row` in a q / k tile (K bf16 per row): the
+// 16-byte chunk is XOR-ed with row bits chosen so that sixteen consecutive rows
+// at one chunk (a row fragment) cover all banks, and four consecutive rows at
+// four consecutive chunks (a transposed read) two-way at most. K = 128 (one row
+// per 256-byte bank span): row bits 0-1 moved up, bits 2-3 moved down. K = 64
+// (two rows per span, so row bit 0 already picks the half): bit 1 to the top,
+// bits 2-3 down.
 template <int K>
 __device__ __forceinline__ int qk_off(int row, int pos) {
-  if constexpr (K == 128) {
-    const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
-    return row * K + (((pos >> 3) ^ sw) << 3) + (pos & 7);
-  } else {
-    return swz<K>(row, pos);
-  }
+  static_assert(K == 128 || K == 64, "64 or 128 keys");
+  const int sw = K == 128 ? ((row & 3) << 2) | ((row >> 2) & 3) : (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  return row * K + (((pos >> 3) ^ sw) << 3) + (pos & 7);
 }
 
 // Position of row t of a chunk in the lane-ordered gate arrays: lane group g
@@ -555,12 +554,18 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
     // arithmetic. Rows past the end of the sequence lie beyond the chunk's
     // buffer range and load as zeros (the padding the chunk algebra needs).
     int qkoff[QPT], voff[VPT];
-    // Row of this thread's q / k piece j (column ptid % KP): for K = 128 the four
-    // 16-lane groups of a wavefront take rows four apart, which keeps each
-    // 32-lane phase of the 8-byte LDS writes on distinct banks.
+    // Row of this thread's q / k piece j (column ptid % KP), chosen so that each
+    // 32-lane phase of the 8-byte LDS writes below lands on distinct banks: for
+    // K = 128 the four 16-lane groups of a wavefront take rows four apart; for
+    // K = 64 the four 8-lane groups of a phase take rows {0, 1, 4, 5} above a
+    // base (the four combinations of row bits 0 and 2).
     auto qk_row = [&](int j) {
-      if constexpr (K == 128) return 16 * j + 4 * ((ptid >> 4) & 3) + (ptid >> 6);
-      else return (ptid + j * 256) / KP;
+      if constexpr (K == 128) {
+        return 16 * j + 4 * ((ptid >> 4) & 3) + (ptid >> 6);
+      } else {
+        const int ph = ptid >> 5, grp = (ptid >> 3) & 3;
+        return 32 * j + (ph & 1) * 2 + (ph >> 1) * 8 + (grp & 1) + 4 * (grp >> 1);
+      }
     };
 #pragma unroll
     for (int j = 0; j < QPT; ++j) qkoff[j] = (qk_row(j) * Hk * K + ptid % KP * 8) * 2;
