@@ -57,10 +57,12 @@ namespace comba {
 constexpr int kTP = 32 * 32 + 32 * 64;  // packed 64x64: rows 0-31 keep 32 columns, rows 32-63 keep 64
 
 __device__ __forceinline__ int tp_off(int row, int pos) {
-  // rows 0-31: 32 per row (64 bytes: four rows per 256-byte bank span), 16-byte
-  // chunks swizzled by (row >> 2) & 3; rows 32-63: 64 per row after the first
-  // 1024 (two rows per span), swizzled by (row >> 1) & 7. Sixteen consecutive
-  // rows then cover all 64 banks once for a fixed logical chunk.
+  // rows 0-31: 32 per row (64 bytes, four rows per 256 bytes), 16-byte chunks
+  // swizzled by (row >> 2) & 3; rows 32-63: 64 per row after the first 1024 (two
+  // rows per 256 bytes), swizzled by (row >> 1) & 7. Measured with the LDS
+  // bank-conflict counter: fragment reads of rows 32-63 are conflict-free; those
+  // of rows 0-31, and the producers' 8-byte writes, are two-way under every XOR
+  // swizzle of the four (or eight) chunks of a row.
   const int big = row >> 5;
   const int base = row * (32 << big) - 1024 * big;
   const int sw = big ? (row >> 1) & 7 : (row >> 2) & 3;
@@ -68,16 +70,22 @@ __device__ __forceinline__ int tp_off(int row, int pos) {
 }
 
 // Offset of position pos of row `row` in a q / k tile (K bf16 per row): the
-// 16-byte chunk is XOR-ed with row bits chosen so that sixteen consecutive rows
-// at one chunk (a row fragment) cover all banks, and four consecutive rows at
-// four consecutive chunks (a transposed read) two-way at most. K = 128 (one row
-// per 256-byte bank span): row bits 0-1 moved up, bits 2-3 moved down. K = 64
-// (two rows per span, so row bit 0 already picks the half): bit 1 to the top,
-// bits 2-3 down.
+// 16-byte chunk index is XOR-ed with a linear function of the row bits. The
+// functions were chosen against the LDS bank-conflict counter, measured on
+// gfx950 for each access pattern of the kernel: the 16-byte row fragments of
+// sixteen consecutive rows (K h, Q h and the producers' blocks) and the
+// producers' 8-byte staging writes are conflict-free, and the transposed K^T
+// reads of the state update two-way, the least for 8-byte pieces that all sit
+// in the same half of their chunks. The bank mapping of 16-byte reads on this
+// part is not the plain one (address bits 2-7): the obvious swizzles (row
+// bits 0-3 reversed or rotated) measure two-way on the fragments.
+//   K = 128: row bits 0, 1, 2 -> chunk bits {1}, {2}, {0, 3}.
+//   K = 64:  row bits 1, 2, 3 -> chunk bits {2}, {0, 1}, {1, 2}.
 template <int K>
 __device__ __forceinline__ int qk_off(int row, int pos) {
   static_assert(K == 128 || K == 64, "64 or 128 keys");
-  const int sw = K == 128 ? ((row & 3) << 2) | ((row >> 2) & 3) : (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
+  const int sw = K == 128 ? ((row & 3) << 1) ^ (9 * b2) : (4 * b1) ^ (3 * b2) ^ (6 * b3);
   return row * K + (((pos >> 3) ^ sw) << 3) + (pos & 7);
 }
 
