@@ -7,9 +7,9 @@ This package is the thin Python binding over that library.
 """
 from .api import (CombaError, bwd_cached_workspace_size, bwd_workspace_size, chunk_bwd, chunk_fwd,  # noqa: F401
                   chunk_fwd_noalloc,
-                  chunk_states_size, lib, library_path,
+                  chunk_states_size, lds_probe, lib, library_path,
                   mfma_peak_probe, recurrent_step, segmented_workspace_size, varlen_order, workspace_size)
 
 __all__ = ["chunk_fwd", "chunk_bwd", "bwd_workspace_size", "bwd_cached_workspace_size", "chunk_states_size",
            "recurrent_step", "varlen_order", "workspace_size", "segmented_workspace_size", "mfma_peak_probe",
-           "CombaError"]
+           "lds_probe", "CombaError"]

@@ -35,7 +35,8 @@ EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_chunk_fwd_segmented_workspace_size",
             "comba_chunk_fwd_segmented", "comba_chunk_bwd_workspace_size", "comba_chunk_bwd",
             "comba_varlen_order", "comba_mfma_peak_probe", "comba_chunk_states_size", "comba_chunk_fwd_keep_states",
-            "comba_chunk_bwd_cached_workspace_size", "comba_chunk_bwd_cached", "comba_chunk_fwd_noalloc")
+            "comba_chunk_bwd_cached_workspace_size", "comba_chunk_bwd_cached", "comba_chunk_fwd_noalloc",
+            "comba_lds_probe")
 
 
 class CombaError(RuntimeError):
@@ -110,6 +111,8 @@ def lib() -> ctypes.CDLL:
         L.comba_chunk_fwd_noalloc.restype = i32
         L.comba_mfma_peak_probe.argtypes = [fp, i32, i32, vp]
         L.comba_mfma_peak_probe.restype = i32
+        L.comba_lds_probe.argtypes = [i32, ip, i32, vp, i32, vp]
+        L.comba_lds_probe.restype = i32
         _lib = L
     return _lib
 
@@ -406,6 +409,27 @@ def varlen_order(cu_seqlens: torch.Tensor) -> torch.Tensor:
 
 
 PEAK_PROBE_FLOPS_PER_BLOCK_ITER = 4 * 4 * 16384   # wavefronts x MFMAs per iteration x flops per MFMA
+
+
+LDS_PROBE_KINDS = {"read16": 0, "read8": 1, "read4": 2, "read8_tr": 3,
+                   "write16": 4, "write8": 5, "write4": 6, "write2": 7}
+
+
+def lds_probe(kind: str, lane_offsets, iters: int, sink: torch.Tensor) -> None:
+    """One launch of ``comba_lds_probe``: ``sink.numel() // 256`` workgroups
+    repeating one LDS access whose 64 per-lane byte offsets are given."""
+    if kind not in LDS_PROBE_KINDS:
+        raise ValueError(f"kind must be one of {sorted(LDS_PROBE_KINDS)}")
+    offs = [int(o) for o in lane_offsets]
+    if len(offs) != 64:
+        raise ValueError("64 lane offsets")
+    if not (isinstance(sink, torch.Tensor) and sink.is_cuda and sink.dtype == torch.int32 and sink.is_contiguous()):
+        raise TypeError("sink must be a contiguous int32 CUDA tensor")
+    arr = (ctypes.c_int32 * 64)(*offs)
+    with torch.cuda.device(sink.device):
+        stream = torch.cuda.current_stream(sink.device).cuda_stream
+        _check(lib().comba_lds_probe(LDS_PROBE_KINDS[kind], arr, int(iters), ctypes.c_void_p(sink.data_ptr()),
+                                     sink.numel() // 256, ctypes.c_void_p(stream)))
 
 
 def mfma_peak_probe(sink: torch.Tensor, iters: int) -> int:

@@ -565,3 +565,22 @@ COMBA_API int32_t comba_mfma_peak_probe(float* sink, int32_t blocks, int32_t ite
     return fail(COMBA_ERR_UNSUPPORTED, "blocks * 256 must fit 31 bits");
   return launched(comba::launch_mfma_peak_probe(sink, blocks, iters, static_cast<hipStream_t>(stream)));
 }
+
+COMBA_API int32_t comba_lds_probe(int32_t kind, const int32_t* lane_offsets, int32_t iters, uint32_t* sink,
+                                  int32_t blocks, void* stream) {
+  if (!lane_offsets || !sink) return fail(COMBA_ERR_INVALID_ARG, "lane_offsets and sink must be non-NULL");
+  if (kind < 0 || kind > 7) return fail(COMBA_ERR_INVALID_ARG, "kind must be 0..7");
+  if (blocks < 1 || iters < 1) return fail(COMBA_ERR_INVALID_ARG, "blocks and iters must be >= 1");
+  if (static_cast<int64_t>(blocks) * comba::kLdsProbeThreads > INT_MAX)
+    return fail(COMBA_ERR_UNSUPPORTED, "blocks * 256 must fit 31 bits");
+  static constexpr int kWidth[8] = {16, 8, 4, 8, 16, 8, 4, 2};
+  const int width = kWidth[kind];
+  comba::LdsLaneOffsets offs;
+  for (int l = 0; l < 64; ++l) {
+    const int32_t o = lane_offsets[l];
+    if (o < 0 || o > comba::kLdsProbeBytes - width || o % width != 0)
+      return fail(COMBA_ERR_INVALID_ARG, "every lane offset must be aligned to the access width and lie inside 64 KiB");
+    offs.v[l] = o;
+  }
+  return launched(comba::launch_lds_probe(kind, offs, iters, sink, blocks, static_cast<hipStream_t>(stream)));
+}

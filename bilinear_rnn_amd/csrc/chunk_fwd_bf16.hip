@@ -71,21 +71,21 @@ __device__ __forceinline__ int tp_off(int row, int pos) {
 
 // Offset of position pos of row `row` in a q / k tile (K bf16 per row): the
 // 16-byte chunk index is XOR-ed with a linear function of the row bits. The
-// functions were chosen against the LDS bank-conflict counter, measured on
-// gfx950 for each access pattern of the kernel: the 16-byte row fragments of
-// sixteen consecutive rows (K h, Q h and the producers' blocks) and the
-// producers' 8-byte staging writes are conflict-free, and the transposed K^T
-// reads of the state update two-way, the least for 8-byte pieces that all sit
-// in the same half of their chunks. The bank mapping of 16-byte reads on this
-// part is not the plain one (address bits 2-7): the obvious swizzles (row
-// bits 0-3 reversed or rotated) measure two-way on the fragments.
+// functions (and the producers' staging rows below) were chosen against the
+// LDS bank-conflict counter, measured on gfx950 for each access pattern of
+// the kernel: the 16-byte row fragments of sixteen consecutive rows (K h, Q h
+// and the producers' blocks) and the producers' 8-byte staging writes are
+// conflict-free, and the transposed K^T reads of the state update two-way, the
+// least for 8-byte pieces that all sit in the same half of their chunks. The
+// part's bank mapping is not the plain one on address bits 2-7: swizzles that
+// are conflict-free under it (row bits 0-3 reversed or rotated) measure
+// two-way on the fragments.
 //   K = 128: row bits 0, 1, 2 -> chunk bits {1}, {2}, {0, 3}.
-//   K = 64:  row bits 1, 2, 3 -> chunk bits {2}, {0, 1}, {1, 2}.
+//   K = 64:  row bits 0-2 -> chunk bits 0-2 (chunk c of row r at c ^ (r mod 8)).
 template <int K>
 __device__ __forceinline__ int qk_off(int row, int pos) {
   static_assert(K == 128 || K == 64, "64 or 128 keys");
-  const int b1 = (row >> 1) & 1, b2 = (row >> 2) & 1, b3 = (row >> 3) & 1;
-  const int sw = K == 128 ? ((row & 3) << 1) ^ (9 * b2) : (4 * b1) ^ (3 * b2) ^ (6 * b3);
+  const int sw = K == 128 ? ((row & 3) << 1) ^ (9 * ((row >> 2) & 1)) : row & 7;
   return row * K + (((pos >> 3) ^ sw) << 3) + (pos & 7);
 }
 
@@ -562,13 +562,19 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
     // arithmetic. Rows past the end of the sequence lie beyond the chunk's
     // buffer range and load as zeros (the padding the chunk algebra needs).
     int qkoff[QPT], voff[VPT];
-    // Row of this thread's q / k piece j (column ptid % KP), chosen so that each
-    // 32-lane phase of the 8-byte LDS writes below lands on distinct banks: for
-    // K = 128 the four 16-lane groups of a wavefront take rows four apart; for
-    // K = 64 the four 8-lane groups of a phase take rows {0, 1, 4, 5} above a
-    // base (the four combinations of row bits 0 and 2).
+    // Column (16-byte piece of a row) of this thread's q / k pieces, and the row
+    // of its piece j; together a bijection onto the tile's pieces. Each 16-lane
+    // group of the 8-byte LDS writes below spans two rows, which keeps the
+    // writes conflict-free (measured; one row per group is two-way whatever the
+    // swizzle). For K = 128 the two rows' pieces are not on consecutive lanes,
+    // which the in-kernel normalisation's row sums need: that instantiation
+    // keeps one row per 16 consecutive lanes (two-way writes).
+    constexpr bool SPREAD = K == 128 && !NORM;
+    const int qk_col = SPREAD ? (ptid & 7) | (((ptid >> 4) & 1) << 3) : ptid % KP;
     auto qk_row = [&](int j) {
-      if constexpr (K == 128) {
+      if constexpr (SPREAD) {
+        return 16 * j + ((ptid >> 6) & 1) + (((ptid >> 5) & 1) << 1) + (((ptid >> 3) & 1) << 2) + ((ptid >> 7) << 3);
+      } else if constexpr (K == 128) {
         return 16 * j + 4 * ((ptid >> 4) & 3) + (ptid >> 6);
       } else {
         const int ph = ptid >> 5, grp = (ptid >> 3) & 3;
@@ -576,7 +582,7 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
       }
     };
 #pragma unroll
-    for (int j = 0; j < QPT; ++j) qkoff[j] = (qk_row(j) * Hk * K + ptid % KP * 8) * 2;
+    for (int j = 0; j < QPT; ++j) qkoff[j] = (qk_row(j) * Hk * K + qk_col * 8) * 2;
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int piece = ptid + j * 256, row = piece / VPR, c8 = piece % VPR;
@@ -617,7 +623,7 @@ __device__ __forceinline__ void chunk_fwd_bf16_body(
     // order) and first v piece; 256 is a multiple of the pieces per row, so every
     // later piece keeps the column and the row's swizzle phase
     static_assert(256 % KP == 0 && 256 % VPR == 0, "a thread's pieces share their column");
-    const int sq0 = qk_off<K>(qk_row(0), perm_col(ptid % KP * 8)), sq1 = qk_off<K>(qk_row(0), perm_col(ptid % KP * 8 + 4));
+    const int sq0 = qk_off<K>(qk_row(0), perm_col(qk_col * 8)), sq1 = qk_off<K>(qk_row(0), perm_col(qk_col * 8 + 4));
     const int sv0 = swz<VT>(ptid / VPR, ptid % VPR * 8);
     if (nchunks > 0) fetch(t0);
     for (int it = 0; it <= nchunks; ++it) {

@@ -385,6 +385,25 @@ int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t*
  */
 int32_t comba_mfma_peak_probe(float* sink, int32_t blocks, int32_t iters, void* stream);
 
+/*
+ * Measurement aid, not part of the recurrence: one LDS access pattern in
+ * isolation, for reading a profiler's LDS bank-conflict counters
+ * (SQ_LDS_BANK_CONFLICT, SQ_LDS_IDX_ACTIVE) for that pattern alone. The
+ * chunk kernels' LDS layouts were chosen with it. Launches `blocks`
+ * workgroups of four wavefronts over a 64 KiB LDS array; lane l of every
+ * wavefront accesses byte offset lane_offsets[l] once per iteration, `iters`
+ * times. kind: 0, 1, 2 read 16, 8, 4 bytes; 3 is the 8-byte transposing
+ * read (ds_read_b64_tr_b16); 4, 5, 6, 7 write 16, 8, 4, 2 bytes.
+ * lane_offsets: host, 64 int32; sink: device, blocks * 256 uint32 (written,
+ * values meaningless), owned by the caller.
+ * Errors: COMBA_ERR_INVALID_ARG for NULL pointers, kind outside 0..7,
+ * blocks or iters < 1, or an offset that is negative, not a multiple of the
+ * access width or past 64 KiB minus the width; COMBA_ERR_UNSUPPORTED when
+ * blocks * 256 exceeds 2^31 - 1.
+ */
+int32_t comba_lds_probe(int32_t kind, const int32_t* lane_offsets, int32_t iters, uint32_t* sink, int32_t blocks,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -292,3 +292,43 @@ def test_noalloc_rejects_more_packed_sequences_than_its_scratch():
     array of 16384 entries: more sequences are refused on the host."""
     assert chunk_noalloc(cu=FAKE, n=16385, T=16385) == api.COMBA_ERR_UNSUPPORTED
     assert "16384" in api.last_error()
+
+
+LDS_OFFS = (ctypes.c_int32 * 64)(*[16 * i for i in range(64)])
+
+
+@pytest.mark.parametrize("kind,offs,iters,sink,blocks,code", [
+    (0, None, 1, FAKE, 1, -1), (0, LDS_OFFS, 1, None, 1, -1), (8, LDS_OFFS, 1, FAKE, 1, -1),
+    (-1, LDS_OFFS, 1, FAKE, 1, -1), (0, LDS_OFFS, 0, FAKE, 1, -1), (0, LDS_OFFS, 1, FAKE, 0, -1),
+    (0, (ctypes.c_int32 * 64)(*([8] + [0] * 63)), 1, FAKE, 1, -1),        # 16-byte access at an 8-byte offset
+    (0, (ctypes.c_int32 * 64)(*([65536 - 8] + [0] * 63)), 1, FAKE, 1, -1),  # past 64 KiB
+    (7, (ctypes.c_int32 * 64)(*([-2] + [0] * 63)), 1, FAKE, 1, -1),
+    (0, LDS_OFFS, 1, FAKE, 1 << 30, -2),
+])
+def test_lds_probe_rejects_bad_arguments(kind, offs, iters, sink, blocks, code):
+    assert comba.lib().comba_lds_probe(kind, offs, iters, sink, blocks, None) == code
+    assert api.last_error() != ""
+
+
+def test_lds_patterns_are_aligned_and_inside_the_probe_array():
+    from bilinear_rnn_amd import lds_patterns
+    width = {"read16": 16, "read8": 8, "read4": 4, "read8_tr": 8, "write16": 16, "write8": 8, "write4": 4, "write2": 2}
+    pats = lds_patterns.patterns()
+    assert len(pats) > 100
+    for name, kind, offs in pats:
+        assert len(offs) == 64, name
+        assert all(o % width[kind] == 0 and 0 <= o <= 65536 - width[kind] for o in offs), name
+
+
+def test_lds_pattern_layouts_cover_each_tile_once():
+    # the q / k swizzles and staging rows address every 16-byte piece of a tile exactly once
+    from bilinear_rnn_amd import lds_patterns as lp
+    for K in (128, 64):
+        for sw in lp.QK_ALTERNATIVES.values():
+            pieces = sorted(lp.qk_off(K, sw, r, 8 * c) // 8 for r in range(64) for c in range(K // 8))
+            assert pieces == list(range(64 * K // 8))
+        kp = K // 8
+        for spread in (True, False):
+            rows = sorted((lp.qk_row(K, p, j, spread), lp.qk_col(K, p, spread))
+                          for p in range(256) for j in range(64 * kp // 256))
+            assert rows == [(r, c) for r in range(64) for c in range(kp)]
