@@ -41,13 +41,17 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 }
 
 // Row-major tile of L bf16 per row: 16-byte chunk c of row r is stored at
-// chunk c ^ (r mod L/8). Sixteen consecutive rows then start on sixteen
-// different bank groups (L = 128), so 16-byte fragment reads of 16 rows are
-// free of bank conflicts.
+// chunk c ^ s(r). For L = 64 and 32, s(r) = r mod L/8. For L = 128 (one row per
+// 256 bytes) s maps row bits 0, 1, 2 to chunk bits {1}, {2}, {0, 3}: measured
+// with the LDS bank-conflict counter on gfx950, the 16-byte fragment reads of 16
+// consecutive rows are conflict-free with either, and the transposing reads of
+// four consecutive rows at four consecutive 8-byte pieces are two-way with this
+// one against four-way with r mod 16.
 template <int L>
 __device__ __forceinline__ int swz(int row, int pos) {
   constexpr int mask = L / 8 - 1;
-  return row * L + (((pos >> 3) ^ (row & mask)) << 3) + (pos & 7);
+  const int s = L == 128 ? ((row & 3) << 1) ^ (9 * ((row >> 2) & 1)) : row & mask;
+  return row * L + (((pos >> 3) ^ s) << 3) + (pos & 7);
 }
 
 __device__ __forceinline__ bf16x8 lds8(const u16* p) { return *reinterpret_cast<const bf16x8*>(p); }
