@@ -431,19 +431,12 @@ __device__ __forceinline__ void grad_scalars(const ChunkGates& gt, const float (
   const float x1 = gt.EG[t] * (vec[8][t] + vec[9][t]);
   const float t2 = gt.EGnG[t] * vec[3][t];
   const float x3 = gt.bEGx[t] * vec[2][t];
-  // sum_{s>=t} x1 and sum_{s>t} x3: scans over the reversed lane order. Every
-  // cross-lane read runs in all 64 lanes (never under a lane condition, where
-  // an inactive source lane would not supply its value); the exclusive sums
-  // are the inclusive ones moved up by one lane, lane 0 then set to zero.
-  const float s1 = wave_inclusive_scan(__shfl(x1, 63 - t, kWave), t);
-  const float s3 = wave_inclusive_scan(__shfl(x3, 63 - t, kWave), t);
-  const float s3up = __shfl_up(s3, 1, kWave);
-  const float s3x = t == 0 ? 0.f : s3up;  // reversed exclusive
-  const float suf1 = __shfl(s1, 63 - t, kWave), suf3 = __shfl(s3x, 63 - t, kWave);
-  // sum_{s<t} t2
-  const float p2 = wave_inclusive_scan(t2, t);
-  const float p2up = __shfl_up(p2, 1, kWave);
-  const float pre2 = t == 0 ? 0.f : p2up;
+  // sum_{s>=t} x1, sum_{s>t} x3 and sum_{s<t} t2 by DPP scans; the exclusive
+  // sums are the inclusive ones moved by one lane (the end lane reads zero).
+  // Every cross-lane read runs in all 64 lanes.
+  const float suf1 = wave_suffix_scan_dpp(x1);
+  const float suf3 = wave_from_higher(wave_suffix_scan_dpp(x3));
+  const float pre2 = wave_from_lower(wave_scan_dpp(t2));
   const float dlog = suf1 + vec[10][t] + vec[11][t] + gt.EG[63] * hd + pre2 - suf3;
   if (t < nrows) {
     const int64_t off = tok0 + static_cast<int64_t>(t) * H;
@@ -457,48 +450,75 @@ __device__ __forceinline__ void grad_scalars(const ChunkGates& gt, const float (
   }
 }
 
+// Value of the lane D places before this one in its group of four (DPP
+// quad_perm [0,0,1,2] or [0,1,0,1]); lanes at the start of the group read
+// their own value.
+template <int D>
+__device__ __forceinline__ float quad_up(float x) {
+  constexpr int ctrl = D == 1 ? 0x90 : 0x44;
+  static_assert(D == 1 || D == 2, "shift by one or two lanes");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+
 // The rectangle sums of grad_scalars from two 64 x 64 fp32 products in LDS
 // (row stride kLdT): X = dP (.) P and Z = W (.) k_t.k_s, whose rows scaled by
-// beta_s give Y = dA (.) A. Two passes by the first 128 threads, with a
-// workgroup barrier between them:
-//   rect_row_prefix: row s of X (threads 0-63) or of Y (64-127) becomes its
-//     exclusive prefix sum_{r<t}, formed by running sums; the Z threads also
+// beta_s give Y = dA (.) A. Two passes over all 512 threads of the workgroup,
+// with a workgroup barrier between them:
+//   rect_row_prefix: row s of X (threads 0-255) or of Y (256-511) becomes its
+//     exclusive prefix sum_{r<t}; four neighbouring lanes take 16 columns each
+//     and add the running sums of the lanes before them; the Z lanes also
 //     write the plain row sum of Z (vec row 5, for dbeta);
-//   rect_column_sums: R_P(t) = sum_{s>=t} X'[s][t], R_A(t) = sum_{s>t} Y'[s][t].
+//   rect_column_sums: R_P(t) = sum_{s>=t} X'[s][t], R_A(t) = sum_{s>t} Y'[s][t],
+//     four neighbouring lanes per column taking the rows s = 4 m + part.
 __device__ __forceinline__ void rect_row_prefix(float (*X)[kLdT], float (*Z)[kLdT], const float* beta,
                                                 float (*vec)[64], int tid) {
-  if (tid < 64) {
-    float acc = 0.f;
-    for (int r = 0; r < 64; ++r) {
-      const float x = X[tid][r];
-      X[tid][r] = acc;
-      acc += x;
+  const bool isz = tid >= 256;
+  const int row = (tid >> 2) & 63, part = tid & 3;
+  float* p = (isz ? Z[row] : X[row]) + 16 * part;
+  const float b = isz ? beta[row] : 1.f;
+  f32x4 x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = ld4(p + 4 * j);
+  f32x4 pre[4];
+  float acc = 0.f, raw = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pre[j][i] = acc;
+      acc += b * x[j][i];
+      raw += x[j][i];
     }
-  } else if (tid < 128) {
-    const int s_ = tid - 64;
-    const float b = beta[s_];
-    float acc = 0.f, raw = 0.f;
-    for (int r = 0; r < 64; ++r) {
-      const float z = Z[s_][r];
-      Z[s_][r] = acc;
-      acc += b * z;
-      raw += z;
-    }
-    vec[5][s_] = raw;
-  }
+  // running sums of the lanes holding the columns before this lane's
+  float incl = acc;
+  const float u1 = quad_up<1>(incl);
+  if (part >= 1) incl += u1;
+  const float u2 = quad_up<2>(incl);
+  if (part >= 2) incl += u2;
+  const float u3 = quad_up<1>(incl);
+  const float before = part >= 1 ? u3 : 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) st4(p + 4 * j, pre[j] + before);
+  raw += dpp_flip<0>(raw);
+  raw += dpp_flip<1>(raw);
+  if (isz && part == 0) vec[5][row] = raw;
 }
 __device__ __forceinline__ void rect_column_sums(const float (*X)[kLdT], const float (*Y)[kLdT], float (*vec)[64],
                                                  int tid) {
-  if (tid < 64) {
-    float acc = 0.f;
-    for (int s_ = tid; s_ < 64; ++s_) acc += X[s_][tid];
-    vec[10][tid] = acc;
-  } else if (tid < 128) {
-    const int t = tid - 64;
-    float acc = 0.f;
-    for (int s_ = t + 1; s_ < 64; ++s_) acc += Y[s_][t];
-    vec[11][t] = acc;
+  const bool isy = tid >= 256;
+  const int t = (tid >> 2) & 63, part = tid & 3;
+  const float (*A)[kLdT] = isy ? Y : X;
+  const int first = isy ? t + 1 : t;  // rows s >= first
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int s_ = 4 * m + part;
+    const float a = A[s_][t];
+    acc += s_ >= first ? a : 0.f;
   }
+  acc += dpp_flip<0>(acc);
+  acc += dpp_flip<1>(acc);
+  if (part == 0) vec[isy ? 11 : 10][t] = acc;
 }
 
 // Gradients of one (chunk, head). Wavefront w owns token block tb = w % 4
@@ -1425,47 +1445,39 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   }
   __syncthreads();
 
-  // channel sums: reduce over the 16 lanes of a row group
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      sbR[i] += __shfl_xor(sbR[i], m, kWave);
-      sKhdR[i] += __shfl_xor(sKhdR[i], m, kWave);
-      st2[i] += __shfl_xor(st2[i], m, kWave);
-    }
-  }
-  if (l16 == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * tb + 4 * g + i;
-      if (hw == 0) {
-        sm.vec[1][t] = sbR[i];
-        sm.vec[2][t] = sKhdR[i];
-      } else {
-        sm.vec[3][t] = st2[i];
-      }
-    }
-  }
   // q~_t . (dO h^T)_t summed over this wave's keys; q~ = q - d k from the bf16 tiles
   f32x4 kv[KBW];
-  {
-    f32x4 x{0.f, 0.f, 0.f, 0.f};
+  f32x4 x{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int cc = 0; cc < KBW; ++cc) {
-      const int pk = perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3));
-      kv[cc] = tr4<K>(sm.Kc, 16 * tb, pk, g, l16);
-      x += (tr4<K>(sm.Qc, 16 * tb, pk, g, l16) - dd_ * kv[cc]) * accQ[cc];
-    }
+  for (int cc = 0; cc < KBW; ++cc) {
+    const int pk = perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3));
+    kv[cc] = tr4<K>(sm.Kc, 16 * tb, pk, g, l16);
+    x += (tr4<K>(sm.Qc, 16 * tb, pk, g, l16) - dd_ * kv[cc]) * accQ[cc];
+  }
+  // Sums over the 16 lanes (channels or keys) of each row group, eight per
+  // wavefront in one DPP reduce-scatter: value j ends in lanes 2 j, 2 j + 1 of
+  // the group. hw = 0: sbR, sKhdR, then x alone; hw = 1: st2 and x.
+  {
+    float v8[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      v8[i] = hw == 0 ? sbR[i] : st2[i];
+      v8[4 + i] = hw == 0 ? sKhdR[i] : x[i];
+    }
+    const float sum = group_sums_scatter<16>(v8, lane);
+    const int j = l16 >> 1;
+    if ((l16 & 1) == 0) sm.vec[hw == 0 ? 1 + (j >> 2) : (j < 4 ? 3 : 9)][16 * tb + 4 * g + (j & 3)] = sum;
+    if (hw == 0) {
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) x[i] += __shfl_xor(x[i], m, kWave);
-      if (l16 == 0) sm.vec[8 + hw][16 * tb + 4 * g + i] = x[i];
+      for (int i = 0; i < 4; ++i) v8[i] = x[i];
+      halve_dpp<3, 2>(v8, lane);
+      halve_dpp<2, 1>(v8, lane);
+      const float r = v8[0] + dpp_flip<1>(v8[0]);
+      const float sx = r + dpp_flip<0>(r);  // value (l16 >> 2) of x
+      if ((l16 & 3) == 0) sm.vec[8][16 * tb + 4 * g + (l16 >> 2)] = sx;
     }
   }
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) shdh += __shfl_xor(shdh, m, kWave);
+  shdh = wave_sum(shdh);
   if (lane == 0) sm.red[wave] = shdh;
   // k_t.k_s of the blocks (tb, 2 hw + cc) from the exact bf16 k tile
   f32x4 kkv[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -1479,6 +1491,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   // masks and elementwise products of the 64 x 64 blocks (tb, 2 hw + cc):
   // dP (.) M and beta W as hi / lo bf16 for the products below, dP (.) P and
   // W (.) k_t.k_s in fp32 for the rectangle sums
+  const f32x4 Gt = ld4(&sm.gt.G[16 * tb + 4 * g]), Gxt = ld4(&sm.gt.Gx[16 * tb + 4 * g]);
+  const f32x4 btt = ld4(&sm.gt.beta[16 * tb + 4 * g]);
 #pragma unroll
   for (int cc = 0; cc < 2; ++cc) {
     const int s_ = 16 * (2 * hw + cc) + l16;
@@ -1490,14 +1504,14 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * tb + 4 * g + i;
-      const float M = s_ <= t ? __expf(fminf(sm.gt.G[t] - Gs, 0.f)) : 0.f;
-      const float E = s_ < t ? __expf(fminf(sm.gt.Gx[t] - Gs, 0.f)) : 0.f;
+      const float M = s_ <= t ? __expf(fminf(Gt[i] - Gs, 0.f)) : 0.f;
+      const float E = s_ < t ? __expf(fminf(Gxt[i] - Gs, 0.f)) : 0.f;
       const float dpv = s_ <= t ? accP[cc][i] : 0.f, dav = s_ < t ? -accA[cc][i] : 0.f;
       const float w = dav * E;
       sm.u.p.dPP[t][s_] = dpv * pv[i];
       sm.u.p.Z[t][s_] = w * kkv[cc][i];
       dpm[i] = dpv * M;
-      wb[i] = sm.gt.beta[t] * w;
+      wb[i] = btt[i] * w;
     }
     const int off = swz<64>(s_, perm_col(16 * tb + 4 * g));
     put_split4(sm.u.p.dPMh, sm.u.p.dPMl, off, dpm);
@@ -1567,8 +1581,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
       }
     }
   }
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) ddp += __shfl_xor(ddp, m, kWave);
+  ddp = wave_sum(ddp);
   __syncthreads();
   if (lane == 0) sm.red[8 + wave] = ddp;
   rect_column_sums(sm.u.p.dPP, sm.u.p.Z, sm.vec, tid);

@@ -168,24 +168,6 @@ __device__ __forceinline__ void producer_sync(int* bar, int& epoch, int lane) {
     __builtin_amdgcn_s_sleep(1);
 }
 
-// x += (x moved by the DPP control CTRL); lanes without a source add 0.
-#define COMBA_DPP_ADD(x, CTRL, ROWMASK, BOUND)                                                        \
-  (x) += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), CTRL, \
-                                                               ROWMASK, 0xf, BOUND))
-
-// Wavefront inclusive prefix sum: shifts by 1, 2, 4, 8 inside each row of 16
-// lanes, then the last lane of row 0 / 2 into rows 1 / 3, then lane 31 into
-// rows 2 and 3.
-__device__ __forceinline__ float wave_scan_dpp(float x) {
-  COMBA_DPP_ADD(x, 0x111, 0xf, true);  // row_shr:1
-  COMBA_DPP_ADD(x, 0x112, 0xf, true);  // row_shr:2
-  COMBA_DPP_ADD(x, 0x114, 0xf, true);  // row_shr:4
-  COMBA_DPP_ADD(x, 0x118, 0xf, true);  // row_shr:8
-  COMBA_DPP_ADD(x, 0x142, 0xa, false); // row_bcast:15 into rows 1, 3
-  COMBA_DPP_ADD(x, 0x143, 0xc, false); // row_bcast:31 into rows 2, 3
-  return x;
-}
-
 // K^T operand (rows = key channels 16kb..16kb+15, reduction = tokens
 // 32s2 + {4g..4g+3, 16+4g..16+4g+3}) from the row-major K tile.
 template <int K>
@@ -264,7 +246,6 @@ __device__ __forceinline__ void invert16(ChunkBuf<K, VT>& bf, const float* Ab, f
     bf.Tl[off] = static_cast<u16>(lw[r]);
   }
 }
-
 
 // Scale one transposed block (see producer_blocks) into P and A and write
 // them: this lane holds row t = 16 R + l16, columns s = 16 C + 4 g + i.
@@ -437,45 +418,6 @@ __device__ __forceinline__ void producer_blocks(ChunkBuf<K, VT>& bf, ProdScratch
     static_assert(NB == 2 && R1 == D && C1 == D - 1, "odd waves hold (D, D) and (D, D-1)");
     offdiag_inverse<D>(bf, ps, prev, pair_flag, chunk_tag, lane);
   }
-}
-
-// Value of the lane whose position in the group differs in bit B (the lane
-// mirrored within its 16, 8 or 4 lanes, or its neighbour): DPP row_mirror,
-// row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2].
-template <int B>
-__device__ __forceinline__ float dpp_flip(float x) {
-  constexpr int ctrl = B == 3 ? 0x140 : B == 2 ? 0x141 : B == 1 ? 0x4e : 0xb1;
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
-}
-
-// One reduce-scatter step over lane bit B: lanes with the bit clear keep the
-// lower N of their 2N partial sums, lanes with it set the upper N, and each
-// adds the partner lane's copy of the half it keeps.
-template <int B, int N>
-__device__ __forceinline__ void halve_dpp(float* v, int lane) {
-  const bool hi = (lane >> B) & 1;
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const float keep = hi ? v[i + N] : v[i], send = hi ? v[i] : v[i + N];
-    v[i] = keep + dpp_flip<B>(send);
-  }
-}
-
-// Sums each of L values v[0 .. L/2 - 1] over its group of L consecutive lanes
-// (L = 16 or 8). Returns in every lane one complete sum: that of value
-// (lane >> 1) & (L/2 - 1), the same in both lanes of a pair.
-template <int L>
-__device__ __forceinline__ float group_sums_scatter(float* v, int lane) {
-  if constexpr (L == 16) {
-    halve_dpp<3, 4>(v, lane);
-    halve_dpp<2, 2>(v, lane);
-    halve_dpp<1, 1>(v, lane);
-  } else {
-    static_assert(L == 8, "groups of 16 or 8 lanes");
-    halve_dpp<2, 2>(v, lane);
-    halve_dpp<1, 1>(v, lane);
-  }
-  return v[0] + dpp_flip<0>(v[0]);
 }
 
 // Sum of squares of the eight bf16 values in a 16-byte piece: four bf16-pair

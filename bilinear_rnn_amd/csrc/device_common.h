@@ -61,17 +61,105 @@ __host__ __device__ constexpr int perm32(int p) {
 }
 __host__ __device__ constexpr int perm_col(int c) { return (c & ~31) | perm32(c & 31); }
 
-// Wavefront-wide inclusive prefix sum.
-__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    float y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
+// x summed over the 16 lanes of each DPP row, result in all 16 lanes:
+// swap neighbours, swap pairs, mirror the 8-lane halves, mirror the row.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));
   return x;
 }
 
-// The same in double.
+// x summed over the wavefront, the same value in every lane: the sums of the
+// four DPP rows, then those four read lane by lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row16_sum(x);
+  auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l)); };
+  return (at(0) + at(16)) + (at(32) + at(48));
+}
+
+// Value of the lane whose position in the group differs in bit B (the lane
+// mirrored within its 16, 8 or 4 lanes, or its neighbour): DPP row_mirror,
+// row_half_mirror, quad_perm [2,3,0,1], quad_perm [1,0,3,2].
+template <int B>
+__device__ __forceinline__ float dpp_flip(float x) {
+  constexpr int ctrl = B == 3 ? 0x140 : B == 2 ? 0x141 : B == 1 ? 0x4e : 0xb1;
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+
+// One reduce-scatter step over lane bit B: lanes with the bit clear keep the
+// lower N of their 2N partial sums, lanes with it set the upper N, and each
+// adds the partner lane's copy of the half it keeps.
+template <int B, int N>
+__device__ __forceinline__ void halve_dpp(float* v, int lane) {
+  const bool hi = (lane >> B) & 1;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float keep = hi ? v[i + N] : v[i], send = hi ? v[i] : v[i + N];
+    v[i] = keep + dpp_flip<B>(send);
+  }
+}
+
+// Sums each of L values v[0 .. L/2 - 1] over its group of L consecutive lanes
+// (L = 16 or 8). Returns in every lane one complete sum: that of value
+// (lane >> 1) & (L/2 - 1), the same in both lanes of a pair.
+template <int L>
+__device__ __forceinline__ float group_sums_scatter(float* v, int lane) {
+  if constexpr (L == 16) {
+    halve_dpp<3, 4>(v, lane);
+    halve_dpp<2, 2>(v, lane);
+    halve_dpp<1, 1>(v, lane);
+  } else {
+    static_assert(L == 8, "groups of 16 or 8 lanes");
+    halve_dpp<2, 2>(v, lane);
+    halve_dpp<1, 1>(v, lane);
+  }
+  return v[0] + dpp_flip<0>(v[0]);
+}
+
+// x += (x moved by the DPP control CTRL); lanes without a source add 0.
+#define COMBA_DPP_ADD(x, CTRL, ROWMASK, BOUND)                                                        \
+  (x) += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (x)), CTRL, \
+                                                               ROWMASK, 0xf, BOUND))
+
+// Wavefront inclusive prefix sum: shifts by 1, 2, 4, 8 inside each row of 16
+// lanes, then the last lane of row 0 / 2 into rows 1 / 3, then lane 31 into
+// rows 2 and 3.
+__device__ __forceinline__ float wave_scan_dpp(float x) {
+  COMBA_DPP_ADD(x, 0x111, 0xf, true);  // row_shr:1
+  COMBA_DPP_ADD(x, 0x112, 0xf, true);  // row_shr:2
+  COMBA_DPP_ADD(x, 0x114, 0xf, true);  // row_shr:4
+  COMBA_DPP_ADD(x, 0x118, 0xf, true);  // row_shr:8
+  COMBA_DPP_ADD(x, 0x142, 0xa, false); // row_bcast:15 into rows 1, 3
+  COMBA_DPP_ADD(x, 0x143, 0xc, false); // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Wavefront inclusive suffix sum (lane t: the sum over lanes t .. 63): shifts
+// by 1, 2, 4, 8 towards lane 0 inside each row of 16 lanes, then the totals of
+// the rows above (read from their first lanes) added.
+__device__ __forceinline__ float wave_suffix_scan_dpp(float x) {
+  COMBA_DPP_ADD(x, 0x101, 0xf, true);  // row_shl:1
+  COMBA_DPP_ADD(x, 0x102, 0xf, true);  // row_shl:2
+  COMBA_DPP_ADD(x, 0x104, 0xf, true);  // row_shl:4
+  COMBA_DPP_ADD(x, 0x108, 0xf, true);  // row_shl:8
+  auto at = [&](int l) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l)); };
+  const float r3 = at(48), r23 = at(32) + r3, r123 = at(16) + r23;
+  const int row = static_cast<int>(__lane_id()) >> 4;
+  return x + (row == 0 ? r123 : row == 1 ? r23 : row == 2 ? r3 : 0.f);
+}
+
+// Value of the next lower (wave_shr:1) or next higher (wave_shl:1) lane of the
+// wavefront; lane 0, respectively lane 63, reads 0.
+__device__ __forceinline__ float wave_from_lower(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x138, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float wave_from_higher(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x130, 0xf, 0xf, true));
+}
+
+// Wavefront-wide inclusive prefix sum in double.
 __device__ __forceinline__ double wave_inclusive_scan_f64(double x, int lane) {
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {

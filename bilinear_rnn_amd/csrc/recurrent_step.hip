@@ -33,16 +33,6 @@ template <> struct Load4<u16> {
   }
 };
 
-// x summed over the 16 lanes of each DPP row, result in all 16 lanes:
-// swap neighbours, swap pairs, mirror the 8-lane halves, mirror the row.
-__device__ __forceinline__ float row16_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));
-  return x;
-}
-
 // One workgroup per (sequence, head, block of VB value rows).
 template <int K, int V, int VB, typename InT, typename OutT>
 __global__ __launch_bounds__(256) void recurrent_kernel(
