@@ -75,6 +75,14 @@ __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ __forceinline__ float hsum(f32x4 x) { return (x[0] + x[1]) + (x[2] + x[3]); }
 
+// Tinv and P are lower triangular: the prep kernel stores only their 16x16
+// blocks on or below the diagonal (the rest of the 64x64 buffers is never
+// written), and the readers load those blocks and zero the others.
+__device__ __forceinline__ bool tri_block_live(int row, int col) { return (col >> 4) <= (row >> 4); }
+__device__ __forceinline__ f32x4 ld4_lower(const float* m, int row, int c4) {
+  return tri_block_live(row, c4) ? ld4(m + row * 64 + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
 // ---- row loads through buffer resources ---------------------------------------------------
 // A chunk's rows are read with unconditional 16- or 8-byte buffer loads whose
 // resource ends after the chunk's last valid row: loads past it return zeros,
@@ -227,9 +235,18 @@ struct alignas(16) SmemPrepValu {
   ChunkGates gt;
 };
 
+template <int K>
 struct alignas(16) SmemPrepMfma {
-  float Am[64 * kLdF];
-  float Tm[64 * kLdF];
+  union {
+    struct {
+      float Am[64 * kLdF];
+      float Tm[64 * kLdF];
+    };
+    struct {  // q and k rows for the score products, read before A is formed
+      u16 Qc[64 * K];
+      u16 Kc[64 * K];
+    };
+  };
   float Ys[768];
   ChunkGates gt;
 };
@@ -240,19 +257,19 @@ template <bool kStoreKK>
 __device__ __forceinline__ void prep_entry(const ChunkGates& gt, int t, int s, float kk, float qtk, float* Am,
                                            float* Pg, float* KKg) {
   Am[t * kLdF + s] = s < t ? gt.beta[t] * decay_Gx(gt, t, s) * kk : 0.f;
-  Pg[t * 64 + s] = s <= t ? qtk * decay_G(gt, t, s) : 0.f;
+  if (tri_block_live(t, s)) Pg[t * 64 + s] = s <= t ? qtk * decay_G(gt, t, s) : 0.f;
   if constexpr (kStoreKK) KKg[t * 64 + s] = kk;
 }
 
 template <int K, typename InT>
-__global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
+__global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 1) void chunk_bwd_prep_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
     const float* __restrict__ beta, const float* __restrict__ d, const int32_t* __restrict__ cu_seqlens, int T,
     int H, int N, int64_t nslots, float* __restrict__ Tg, float* __restrict__ Pg, float* __restrict__ KKg,
     float* __restrict__ Gg) {
   constexpr int NT = 256;
   constexpr bool kMfma = sizeof(InT) == 2;  // bf16 q / k: exact matrix-core operands
-  using Smem = typename std::conditional<kMfma, SmemPrepMfma, SmemPrepValu<K>>::type;
+  using Smem = typename std::conditional<kMfma, SmemPrepMfma<K>, SmemPrepValu<K>>::type;
   __shared__ Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x % H;
@@ -264,7 +281,13 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
   const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
   const float dh = d[h];
   const int64_t mb = (slot * H + h) * 64 * 64;
-  if constexpr (!kMfma) {
+  if constexpr (kMfma) {
+    // q and k rows in flight while the gates are staged and formed
+    RowPieces<K, NT, u16> rqk;
+    rqk.load(reinterpret_cast<const u16*>(q), reinterpret_cast<const u16*>(k), tok0, H, nrows, tid);
+    stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
+    rqk.store_bf16(sm.Qc, sm.Kc, tid);
+  } else {
     for (int e = tid; e < 64 * K; e += NT) {
       const int row = e / K, cc = e % K;
       float kv = 0.f, qv = 0.f;
@@ -276,8 +299,8 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
       sm.KT[cc][row] = kv;
       sm.QtT[cc][row] = qv - dh * kv;
     }
+    stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
   }
-  stage_gates(sm.gt, alpha, beta, tok0, H, nrows, tid);
   __syncthreads();
   if (wave == 0) chunk_gates(sm.gt, lane, nrows);
   __syncthreads();
@@ -285,34 +308,26 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
   if (tid < kGateWords / 4) st4(Gg + (slot * H + h) * kGateWords + 4 * tid, ld4(&sm.gt.G[0] + 4 * tid));
   if constexpr (kMfma) {
     // wavefront w: token rows 16 w .. 16 w + 15 against all 64 columns. Lane l
-    // supplies row (l % 16) of a block and the 8 keys 32 j + 8 (l / 16) + 0..7
-    // (the same keys for both operands), loaded straight from HBM; the
-    // accumulator gives rows 4 (l / 16) + i of column (l % 16).
+    // supplies row (l % 16) of a block and 8 keys of each 32-block (the same
+    // keys for both operands) from the q / k tiles; the accumulator gives rows
+    // 4 (l / 16) + i of column (l % 16).
     const int l16 = lane & 15, g = lane >> 4, rb = wave;
-    const bf16x8 zero8 = {};
     f32x4 akk[4], aqk[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) akk[cb] = aqk[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ra = 16 * rb + l16;
-    const u16* kb_ = reinterpret_cast<const u16*>(k);
-    const u16* qb_ = reinterpret_cast<const u16*>(q);
 #pragma unroll
     for (int j = 0; j < K / 32; ++j) {
       const int kofs = 32 * j + 8 * g;
-      const bf16x8 ak = ra < nrows ? *reinterpret_cast<const bf16x8*>(kb_ + (tok0 + static_cast<int64_t>(ra) * H) * K + kofs)
-                                   : zero8;
-      const bf16x8 aq = ra < nrows ? *reinterpret_cast<const bf16x8*>(qb_ + (tok0 + static_cast<int64_t>(ra) * H) * K + kofs)
-                                   : zero8;
+      const bf16x8 ak = lds8(&sm.Kc[swz<K>(ra, kofs)]), aq = lds8(&sm.Qc[swz<K>(ra, kofs)]);
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
-        const int rcol = 16 * cb + l16;
-        const bf16x8 bk = rcol < nrows
-                              ? *reinterpret_cast<const bf16x8*>(kb_ + (tok0 + static_cast<int64_t>(rcol) * H) * K + kofs)
-                              : zero8;
+        const bf16x8 bk = lds8(&sm.Kc[swz<K>(16 * cb + l16, kofs)]);
         akk[cb] = mfma16x16x32(ak, bk, akk[cb]);
         aqk[cb] = mfma16x16x32(aq, bk, aqk[cb]);
       }
     }
+    __syncthreads();  // the q / k tiles share A's space
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
@@ -345,7 +360,7 @@ __global__ __launch_bounds__(256) void chunk_bwd_prep_kernel(
   unit_lower_inverse64<NT>(sm.Am, sm.Tm, sm.Ys, tid);
   for (int e = tid; e < 64 * 64; e += NT) {
     const int t = e >> 6, s_ = e & 63;
-    Tg[mb + e] = s_ <= t ? sm.Tm[t * kLdF + s_] : 0.f;
+    if (tri_block_live(t, s_)) Tg[mb + e] = s_ <= t ? sm.Tm[t * kLdF + s_] : 0.f;
   }
 }
 
@@ -568,8 +583,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_kernel(
 #pragma unroll
   for (int j = 0; j < MPT; ++j) {
     const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-    rt[j] = ld4(&Tg[mb + row * 64 + c4]);
-    rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+    rt[j] = ld4_lower(Tg + mb, row, c4);
+    rp[j] = ld4_lower(Pg + mb, row, c4);
   }
   f32x4 rg{};
   if (tid < kGateWords / 4) rg = ld4(Gg + (slot * H + h) * kGateWords + 4 * tid);
@@ -878,8 +893,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-      rt[j] = ld4(&Tg[mb + row * 64 + c4]);
-      rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+      rt[j] = ld4_lower(Tg + mb, row, c4);
+      rp[j] = ld4_lower(Pg + mb, row, c4);
     }
     if (tid < kGateWords / 4) rg = ld4(Gg + (chunk_slot(packed, t0, n, ci, T) * H + h) * kGateWords + 4 * tid);
   };
@@ -1062,8 +1077,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-      rt[j] = ld4(&Tg[sl * 64 * 64 + row * 64 + c4]);
-      rp[j] = ld4(&Pg[sl * 64 * 64 + row * 64 + c4]);
+      rt[j] = ld4_lower(Tg + sl * 64 * 64, row, c4);
+      rp[j] = ld4_lower(Pg + sl * 64 * 64, row, c4);
     }
     if (tid < kGateWords / 4) rg = ld4(Gg + sl * kGateWords + 4 * tid);
   };
@@ -1263,8 +1278,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < MPT; ++j) {
     const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-    rt[j] = ld4(&Tg[mb + row * 64 + c4]);
-    rp[j] = ld4(&Pg[mb + row * 64 + c4]);
+    rt[j] = ld4_lower(Tg + mb, row, c4);
+    rp[j] = ld4_lower(Pg + mb, row, c4);
   }
   f32x4 rg{};
   if (tid < kGateWords / 4) rg = ld4(Gg + (slot * H + h) * kGateWords + 4 * tid);
