@@ -1061,29 +1061,42 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
       dhr[j][c] = dsf ? ld4(dsf + (crow0 + 16 * (cb0 + j)) * K + key4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-  // next chunk's operands, one chunk ahead in registers
+  // next chunk's operands, one chunk ahead in registers, fetched in three
+  // parts over the chunk's three compute stages: issued together, the 16-byte
+  // loads of all eight wavefronts queue in the CU's memory unit and stall the
+  // wavefronts behind them for about 1,500 cycles (the state-gradient stores,
+  // moved out of the staging stage, do the same)
   RowPieces<K, NT, u16> rqk;
   u32x4 ro;
   f32x4 rg{};
   f32x4 rt[MPT], rp[MPT];
   const int orow = tid / (VT / 8), ocol = 8 * (tid % (VT / 8));
-  auto fetch = [&](int ci) {
+  auto fetch_qk = [&](int ci) {
     const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+    rqk.load(q, k, (static_cast<int64_t>(b) * T + c0) * H + h, H, nrows, tid);
+  };
+  auto fetch_tp = [&](int ci) {
     const int64_t sl = chunk_slot(packed, t0, n, ci, T) * H + h;
-    rqk.load(q, k, tok0, H, nrows, tid);
-    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
-    ro = load16(orsrc, (orow * H * V + vt * VT + ocol) * 2);
 #pragma unroll
     for (int j = 0; j < MPT; ++j) {
       const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
       rt[j] = ld4_lower(Tg + sl * 64 * 64, row, c4);
       rp[j] = ld4_lower(Pg + sl * 64 * 64, row, c4);
     }
-    if (tid < kGateWords / 4) rg = ld4(Gg + sl * kGateWords + 4 * tid);
+  };
+  auto fetch_og = [&](int ci) {
+    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
+    ro = load16(orsrc, (orow * H * V + vt * VT + ocol) * 2);
+    if (tid < kGateWords / 4) rg = ld4(Gg + (chunk_slot(packed, t0, n, ci, T) * H + h) * kGateWords + 4 * tid);
   };
 
-  if (nch > 0) fetch(nch - 1);
+  if (nch > 0) {
+    fetch_qk(nch - 1);
+    fetch_tp(nch - 1);
+    fetch_og(nch - 1);
+  }
   for (int ci = nch - 1; ci >= 0; --ci) {
     const int64_t slot = chunk_slot(packed, t0, n, ci, T);
     __syncthreads();
@@ -1110,7 +1123,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
       }
     }
     __syncthreads();
-    if (ci > 0) fetch(ci - 1);  // in flight during this chunk's work
+    if (ci > 0) fetch_qk(ci - 1);  // in flight during this chunk's work
 
     // dUbar of the blocks (tb, cb): diag(e^(Gn - G)) K dh, then + P^T dO
     {
@@ -1141,6 +1154,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
       }
     }
     __syncthreads();
+    if (ci > 0) fetch_tp(ci - 1);
 
     // dR = Tinv^T dUbar, then X and Z of the blocks (tb, cb)
     {
@@ -1165,6 +1179,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
       }
     }
     __syncthreads();
+    if (ci > 0) fetch_og(ci - 1);
 
     // dh <- e^Gn dh + q^T X + k^T Z for the wavefront's blocks
     const float eGn = sm.gt.EG[63];
