@@ -1304,19 +1304,31 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrsrc = rows_rsrc(v + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
   f32x4 pS[HP], pdS[HP];
   u32x2 pO, pV;
-  auto fetch_tile = [&](int jt) {
-    const int v0 = jt * VT;
+  // in three parts, spread over a tile's stages: issued together, the loads
+  // of all eight wavefronts queue in the CU's memory unit and hold up the
+  // wavefronts behind them
+  auto fetch_h = [&](int jt) {
 #pragma unroll
     for (int j = 0; j < HP; ++j) {
       const int e = tid + j * NT, row = e / (K / 4), k4 = 4 * (e % (K / 4));
-      pS[j] = ld4(hsrc + static_cast<int64_t>(v0 + row) * K + k4);
-      pdS[j] = ld4(dhsrc + static_cast<int64_t>(v0 + row) * K + k4);
+      pS[j] = ld4(hsrc + static_cast<int64_t>(jt * VT + row) * K + k4);
     }
-    const int off = (orow * H * V + v0 + ocol) * 2;
+  };
+  auto fetch_dh = [&](int jt) {
+#pragma unroll
+    for (int j = 0; j < HP; ++j) {
+      const int e = tid + j * NT, row = e / (K / 4), k4 = 4 * (e % (K / 4));
+      pdS[j] = ld4(dhsrc + static_cast<int64_t>(jt * VT + row) * K + k4);
+    }
+  };
+  auto fetch_ov = [&](int jt) {
+    const int off = (orow * H * V + jt * VT + ocol) * 2;
     pO = __builtin_amdgcn_raw_buffer_load_b64(orsrc, off, 0, 0);
     pV = __builtin_amdgcn_raw_buffer_load_b64(vrsrc, off, 0, 0);
   };
-  fetch_tile(0);
+  fetch_h(0);
+  fetch_dh(0);
+  fetch_ov(0);
 
   rqk.store_bf16(sm.Qc, sm.Kc, tid);
 #pragma unroll
@@ -1348,8 +1360,8 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     }
     *reinterpret_cast<u32x2*>(&sm.u.t.dO[swz<VT>(orow, perm_col(ocol))]) = pO;
     *reinterpret_cast<u32x2*>(&sm.u.t.Vt[swz<VT>(orow, ocol)]) = pV;
-    if (jt + 1 < NTILE) fetch_tile(jt + 1);  // in flight during this tile's work
     __syncthreads();
+    if (jt + 1 < NTILE) fetch_h(jt + 1);  // in flight during this tile's work
     // Opaque per-tile copies of the lane coordinates: the LDS addresses below
     // are then formed inside the loop instead of being hoisted out of it,
     // which exhausts the registers.
@@ -1386,6 +1398,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
       }
     }
     __syncthreads();
+    if (jt + 1 < NTILE) fetch_dh(jt + 1);
     if (hw == 0) {  // Ubar = Tinv R (Tinv[t][s] = 0 for s > t)
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
@@ -1414,6 +1427,7 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
       }
     }
     __syncthreads();
+    if (jt + 1 < NTILE) fetch_ov(jt + 1);
     if (hw == 0) {  // dR = Tinv^T dUbar, dv = beta dR, and the channel sums of dR
       f32x4 eGx;
 #pragma unroll
