@@ -1304,6 +1304,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrsrc = rows_rsrc(v + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
   f32x4 pS[HP], pdS[HP];
   u32x2 pO, pV;
+  // fp32 gradient rows of the chunk; stores to rows past its end fall outside
+  // the resource and are dropped
+  const __amdgpu_buffer_rsrc_t dvrsrc = rows_rsrc(dv + tok0 * V, static_cast<int64_t>(nrows) * H * V * 4);
   // in three parts, spread over a tile's stages: issued together, the loads
   // of all eight wavefronts queue in the CU's memory unit and hold up the
   // wavefronts behind them
@@ -1348,9 +1351,14 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
   f32x4 sbR{0.f, 0.f, 0.f, 0.f}, sKhdR{0.f, 0.f, 0.f, 0.f}, st2{0.f, 0.f, 0.f, 0.f};
   float shdh = 0.f;
 
+  f32x4 eGx;  // e^Gx of this lane's four token rows
   for (int jt = 0; jt < NTILE; ++jt) {
     const int v0 = jt * VT;
     __syncthreads();
+    if (jt == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eGx[i] = __expf(sm.gt.Gx[16 * tb + 4 * g + i]);
+    }
 #pragma unroll
     for (int j = 0; j < HP; ++j) {
       const int e = tid + j * NT, row = e / (K / 4), k4 = 4 * (e % (K / 4));
@@ -1429,9 +1437,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     __syncthreads();
     if (jt + 1 < NTILE) fetch_ov(jt + 1);
     if (hw == 0) {  // dR = Tinv^T dUbar, dv = beta dR, and the channel sums of dR
-      f32x4 eGx;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) eGx[i] = __expf(sm.gt.Gx[16 * tb + 4 * g + i]);
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb) {
         f32x4 dr{0.f, 0.f, 0.f, 0.f};
@@ -1444,10 +1449,9 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
         }
         put_split4(sm.u.t.dRh, sm.u.t.dRl, swz<64>(16 * cb + l16, perm_col(16 * tb + 4 * g)), dr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * tb + 4 * g + i;
-          if (t < nrows) dv[(tok0 + static_cast<int64_t>(t) * H) * V + v0 + 16 * cb + l16] = bt[i] * dr[i];
-        }
+        for (int i = 0; i < 4; ++i)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(bt[i] * dr[i]), dvrsrc,
+                                                ((16 * tb + 4 * g + i) * H * V + v0 + 16 * cb + l16) * 4, 0, 0);
         sbR += dr * (vv[cb] - eGx * kx[cb]);
         sKhdR += kx[cb] * dr;
       }
@@ -1577,16 +1581,36 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
     xk[cc] = en * accUd[cc] - b1 * accRh[cc];
     xd[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // dq first, so that its stores drain while the dk products run
 #pragma unroll
   for (int s_ = 0; s_ < 2; ++s_) {
     if (s_ == 1 && tb < 2) continue;  // columns s <= t
     const bf16x8 mh = tr_frag<64>(sm.u.p.dPMh, 32 * s_, pt, g, l16), ml = tr_frag<64>(sm.u.p.dPMl, 32 * s_, pt, g, l16);
-    const bf16x8 wh = tr_frag<64>(sm.u.p.WBh, 32 * s_, pt, g, l16), wl = tr_frag<64>(sm.u.p.WBl, 32 * s_, pt, g, l16);
 #pragma unroll
     for (int cc = 0; cc < KBW; ++cc) {
       const bf16x8 bk = tr_frag<K>(sm.Kc, 32 * s_, perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3)), g, l16);
       xq[cc] = mfma16x16x32(mh, bk, xq[cc]);
       xq[cc] = mfma16x16x32(ml, bk, xq[cc]);
+    }
+  }
+  float ddp = 0.f;
+  const __amdgpu_buffer_rsrc_t dqrsrc = rows_rsrc(dq + tok0 * K, static_cast<int64_t>(nrows) * H * K * 4);
+  const __amdgpu_buffer_rsrc_t dkrsrc = rows_rsrc(dk + tok0 * K, static_cast<int64_t>(nrows) * H * K * 4);
+#pragma unroll
+  for (int cc = 0; cc < KBW; ++cc) {
+    ddp -= hsum(xq[cc] * kv[cc]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xq[cc][i]), dqrsrc,
+                                            ((16 * tb + 4 * g + i) * H * K + 16 * (KBW * hw + cc) + l16) * 4, 0, 0);
+  }
+#pragma unroll
+  for (int s_ = 0; s_ < 2; ++s_) {
+    if (s_ == 1 && tb < 2) continue;  // columns s <= t
+    const bf16x8 wh = tr_frag<64>(sm.u.p.WBh, 32 * s_, pt, g, l16), wl = tr_frag<64>(sm.u.p.WBl, 32 * s_, pt, g, l16);
+#pragma unroll
+    for (int cc = 0; cc < KBW; ++cc) {
+      const bf16x8 bk = tr_frag<K>(sm.Kc, 32 * s_, perm_col(16 * (KBW * hw + cc) + 4 * (l16 & 3)), g, l16);
       xk[cc] = mfma16x16x32(wh, bk, xk[cc]);
       xk[cc] = mfma16x16x32(wl, bk, xk[cc]);
     }
@@ -1609,21 +1633,13 @@ __global__ __launch_bounds__(512) void chunk_bwd_grad_bf16_kernel(
       xd[cc] = mfma16x16x32(ml, bk, xd[cc]);
     }
   }
-  float ddp = 0.f;
 #pragma unroll
   for (int cc = 0; cc < KBW; ++cc) {
-    const int kc = 16 * (KBW * hw + cc) + l16;
     xk[cc] -= dd_ * (xd[cc] + xq[cc]);
-    ddp -= hsum(xq[cc] * kv[cc]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * tb + 4 * g + i;
-      if (t < nrows) {
-        const int64_t off = (tok0 + static_cast<int64_t>(t) * H) * K + kc;
-        dq[off] = xq[cc][i];
-        dk[off] = xk[cc][i];
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(xk[cc][i]), dkrsrc,
+                                            ((16 * tb + 4 * g + i) * H * K + 16 * (KBW * hw + cc) + l16) * 4, 0, 0);
   }
   ddp = wave_sum(ddp);
   __syncthreads();
