@@ -93,7 +93,7 @@ def chunk_bwd_algorithmic(B, T, H, K, V):
 
 
 # the sources the counted chunk-forward kernel is compiled from
-FWD_SOURCES = ("chunk_fwd_bf16.hip", "chunk_common.h", "device_common.h", "launch.h")
+FWD_SOURCES = ("chunk_fwd_bf16.hip", "bf16_tiles.h", "chunk_common.h", "device_common.h", "launch.h")
 
 
 # the sources the counted decode kernel is compiled from
