@@ -223,6 +223,67 @@ __device__ __forceinline__ void stage_gates(ChunkGates& gt, const float* alpha, 
   }
 }
 
+// D += A (16 x 4) B (4 x 16) in fp32 on the matrix cores. Lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16]; D holds rows 4 (l / 16) + i of
+// column (l % 16).
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Tinv = (I + A)^-1 for the prep kernel: the diagonal 16x16 blocks by
+// column-wise forward substitution as in unit_lower_inverse64, the
+// off-diagonal levels on the fp32 matrix cores (exact fp32 products). Block
+// (i, j) of level L = i - j goes to wavefront j (3, 2, 1 blocks):
+//   Y = sum_{j <= m < i} A_im T_mj  (4 L products over four columns of A),
+//   T_ij = -T_ii Y,
+// where Y passes from the accumulator layout to the operand layout through the
+// wavefront's own 256 floats of Ys (one wavefront's LDS accesses complete in
+// order). Called by all 256 threads; ends with a barrier.
+__device__ __forceinline__ void unit_lower_inverse64_mfma(const float* Am, float* Tm, float* Ys, int tid) {
+  if (tid < 64) {
+    const int blk = tid >> 4, c = tid & 15;
+    const float* Ab = Am + (16 * blk) * kLdF + 16 * blk;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (r == c) ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+#pragma unroll
+      for (int r = j + 1; r < 16; ++r) x[r] -= Ab[r * kLdF + j] * x[j];
+    }
+    float* Tb = Tm + (16 * blk) * kLdF + 16 * blk;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Tb[r * kLdF + c] = x[r];
+  }
+  __syncthreads();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, c = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int L = 1; L <= 3; ++L) {
+    if (wave < 4 - L) {
+      const int j = wave, i = j + L;
+      f32x4 y{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mm = 0; mm < L; ++mm) {
+        const int m = j + mm;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          y = mma4(Am[(16 * i + c) * kLdF + 16 * m + 4 * s4 + g], Tm[(16 * m + 4 * s4 + g) * kLdF + 16 * j + c], y);
+      }
+      float* ys = Ys + 256 * wave;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ys[(4 * g + r) * 16 + c] = y[r];
+      __builtin_amdgcn_wave_barrier();
+      f32x4 t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        t = mma4(Tm[(16 * i + c) * kLdF + 16 * i + 4 * s4 + g], ys[(4 * s4 + g) * 16 + c], t);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tm[(16 * i + 4 * g + r) * kLdF + 16 * j + c] = -t[r];
+    }
+    __syncthreads();
+  }
+}
+
 // ---- prep: Tinv, P and k_t.k_s of every chunk -------------------------------------------
 
 template <int K>
@@ -261,6 +322,62 @@ __device__ __forceinline__ void prep_entry(const ChunkGates& gt, int t, int s, f
   if constexpr (kStoreKK) KKg[t * 64 + s] = kk;
 }
 
+// Scores of NB of the ten 16x16 blocks (R_b, C_b), C_b <= R_b, of a chunk for
+// bf16 q and k: k_t.k_s and q_t.k_s on the matrix cores. Lane l supplies row
+// (l % 16) of a block and 8 keys of each 32-block (the same keys for both
+// operands) from the q / k tiles; the accumulator holds rows 4 (l / 16) + i of
+// column (l % 16).
+template <int NB, int R0, int C0, int R1, int C1, int R2, int C2, int K>
+__device__ __forceinline__ void prep_score_blocks(const u16* Qc, const u16* Kc, int lane, f32x4* akk, f32x4* aqk) {
+  constexpr int Rb[3] = {R0, R1, R2}, Cb[3] = {C0, C1, C2};
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) akk[b] = aqk[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < K / 32; ++j) {
+    const int kofs = 32 * j + 8 * g;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const bf16x8 ak = lds8(&Kc[swz<K>(16 * Rb[b] + l16, kofs)]), aq = lds8(&Qc[swz<K>(16 * Rb[b] + l16, kofs)]);
+      const bf16x8 bk = lds8(&Kc[swz<K>(16 * Cb[b] + l16, kofs)]);
+      akk[b] = mfma16x16x32(ak, bk, akk[b]);
+      aqk[b] = mfma16x16x32(aq, bk, aqk[b]);
+    }
+  }
+}
+
+// A (to LDS) and P (to the chunk's buffer) of the same blocks. Diagonal blocks
+// take each decay directly; in a block below the diagonal every s <= r < t
+// for r = 16 C + 15, its last column, so the decays factor into a row part
+// e^(G_t - G_r) (or e^(Gx_t - G_r)) and a column part e^(G_r - G_s), each at
+// most 1: nine exponentials per lane instead of 32.
+template <int NB, int R0, int C0, int R1, int C1, int R2, int C2>
+__device__ __forceinline__ void prep_score_entries(const ChunkGates& gt, int lane, float dh, const f32x4* akk,
+                                                   const f32x4* aqk, float* Am, float* Pg) {
+  constexpr int Rb[3] = {R0, R1, R2}, Cb[3] = {C0, C1, C2};
+  const int l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int s_ = 16 * Cb[b] + l16;
+    if (Rb[b] == Cb[b]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        prep_entry<false>(gt, 16 * Rb[b] + 4 * g + i, s_, akk[b][i], aqk[b][i] - dh * akk[b][i], Am, Pg, nullptr);
+    } else {
+      const int r = 16 * Cb[b] + 15;
+      const float cs = expf(static_cast<float>(gt.Gd[r] - gt.Gd[s_]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * Rb[b] + 4 * g + i;
+        const float eg = expf(static_cast<float>(gt.Gd[t] - gt.Gd[r]));
+        const float ex = expf(static_cast<float>(gt.Gxd[t] - gt.Gd[r]));
+        Am[t * kLdF + s_] = gt.beta[t] * (ex * cs) * akk[b][i];
+        Pg[t * 64 + s_] = (aqk[b][i] - dh * akk[b][i]) * (eg * cs);
+      }
+    }
+  }
+}
+
 template <int K, typename InT>
 __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 1) void chunk_bwd_prep_kernel(
     const InT* __restrict__ q, const InT* __restrict__ k, const float* __restrict__ alpha,
@@ -271,7 +388,7 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 1) void chunk_bwd_prep_
   constexpr bool kMfma = sizeof(InT) == 2;  // bf16 q / k: exact matrix-core operands
   using Smem = typename std::conditional<kMfma, SmemPrepMfma<K>, SmemPrepValu<K>>::type;
   __shared__ Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x % H;
   const int64_t slot = blockIdx.x / H;
   if (slot >= nslots) return;
@@ -307,34 +424,21 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 1) void chunk_bwd_prep_
   // the gates, for the scan and the gradient kernel
   if (tid < kGateWords / 4) st4(Gg + (slot * H + h) * kGateWords + 4 * tid, ld4(&sm.gt.G[0] + 4 * tid));
   if constexpr (kMfma) {
-    // wavefront w: token rows 16 w .. 16 w + 15 against all 64 columns. Lane l
-    // supplies row (l % 16) of a block and 8 keys of each 32-block (the same
-    // keys for both operands) from the q / k tiles; the accumulator gives rows
-    // 4 (l / 16) + i of column (l % 16).
-    const int l16 = lane & 15, g = lane >> 4, rb = wave;
-    f32x4 akk[4], aqk[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) akk[cb] = aqk[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ra = 16 * rb + l16;
-#pragma unroll
-    for (int j = 0; j < K / 32; ++j) {
-      const int kofs = 32 * j + 8 * g;
-      const bf16x8 ak = lds8(&sm.Kc[swz<K>(ra, kofs)]), aq = lds8(&sm.Qc[swz<K>(ra, kofs)]);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 bk = lds8(&sm.Kc[swz<K>(16 * cb + l16, kofs)]);
-        akk[cb] = mfma16x16x32(ak, bk, akk[cb]);
-        aqk[cb] = mfma16x16x32(aq, bk, aqk[cb]);
-      }
+    // The ten blocks on or below the diagonal in balanced sets, one diagonal
+    // block per wavefront (the blocks above it are zero and never formed).
+    f32x4 akk[3], aqk[3];
+    switch (wave) {
+      case 0: prep_score_blocks<3, 0, 0, 3, 0, 2, 1, K>(sm.Qc, sm.Kc, lane, akk, aqk); break;
+      case 1: prep_score_blocks<3, 1, 1, 1, 0, 3, 2, K>(sm.Qc, sm.Kc, lane, akk, aqk); break;
+      case 2: prep_score_blocks<2, 2, 2, 2, 0, 0, 0, K>(sm.Qc, sm.Kc, lane, akk, aqk); break;
+      default: prep_score_blocks<2, 3, 3, 3, 1, 0, 0, K>(sm.Qc, sm.Kc, lane, akk, aqk); break;
     }
     __syncthreads();  // the q / k tiles share A's space
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * rb + 4 * g + i, s_ = 16 * cb + l16;
-        prep_entry<false>(sm.gt, t, s_, akk[cb][i], aqk[cb][i] - dh * akk[cb][i], sm.Am, Pg + mb, KKg + mb);
-      }
+    switch (wave) {
+      case 0: prep_score_entries<3, 0, 0, 3, 0, 2, 1>(sm.gt, lane, dh, akk, aqk, sm.Am, Pg + mb); break;
+      case 1: prep_score_entries<3, 1, 1, 1, 0, 3, 2>(sm.gt, lane, dh, akk, aqk, sm.Am, Pg + mb); break;
+      case 2: prep_score_entries<2, 2, 2, 2, 0, 0, 0>(sm.gt, lane, dh, akk, aqk, sm.Am, Pg + mb); break;
+      default: prep_score_entries<2, 3, 3, 3, 1, 0, 0>(sm.gt, lane, dh, akk, aqk, sm.Am, Pg + mb); break;
     }
   } else {
     // 4 x 4 block of (t, s) per thread: k_t.k_s and q~_t.k_s
@@ -357,10 +461,15 @@ __global__ __launch_bounds__(256, sizeof(InT) == 2 ? 4 : 1) void chunk_bwd_prep_
       for (int j = 0; j < 4; ++j) prep_entry<true>(sm.gt, tb + i, sb + j, kk[i][j], qk[i][j], sm.Am, Pg + mb, KKg + mb);
   }
   __syncthreads();
-  unit_lower_inverse64<NT>(sm.Am, sm.Tm, sm.Ys, tid);
-  for (int e = tid; e < 64 * 64; e += NT) {
+  unit_lower_inverse64_mfma(sm.Am, sm.Tm, sm.Ys, tid);
+  for (int e = 4 * tid; e < 64 * 64; e += 4 * NT) {  // four entries of a row per thread
     const int t = e >> 6, s_ = e & 63;
-    if (tri_block_live(t, s_)) Tg[mb + e] = s_ <= t ? sm.Tm[t * kLdF + s_] : 0.f;
+    if (tri_block_live(t, s_)) {
+      f32x4 x = ld4(&sm.Tm[t * kLdF + s_]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = s_ + i <= t ? x[i] : 0.f;
+      st4(Tg + mb + e, x);
+    }
   }
 }
 
@@ -388,12 +497,6 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_kernel(
 
 // ---- per-chunk gradients ------------------------------------------------------------------
 
-// D += A (16 x 4) B (4 x 16) in fp32 on the matrix cores. Lane l supplies
-// A[l % 16][l / 16] and B[l / 16][l % 16]; D holds rows 4 (l / 16) + i of
-// column (l % 16).
-__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 constexpr int kGrVT = 16;  // value channels per tile of the gradient kernel
 constexpr int kLdV = kGrVT + 4;

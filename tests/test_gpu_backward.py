@@ -231,3 +231,40 @@ def test_backward_layer_1p3b_full_size():
     got = run_bwd(inp, do, do_bits, dsf)
     assert all(np.isfinite(x).all() for x in got.values())
     check(got, oracle_bwd(inp, do, dsf), inp)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_backward_workspace_contents_do_not_matter(dtype):
+    """The prep kernel stores only the 16x16 blocks of Tinv and P on or below
+    the diagonal, and every buffer of the workspace is written before it is
+    read: a workspace filled with NaN bytes gives the same gradients, bit for
+    bit, as a zeroed one (ragged tail, packed batch with an empty sequence)."""
+    for case in ("ragged", "packed"):
+        if case == "ragged":
+            inp = make_inputs(wl("layer_340m", B=2, H=2, dtype=dtype), T=150, s0_std=0.02, seed=91)
+        else:
+            inp = make_inputs(wl("varlen", H=2, dtype=dtype), lengths=np.array([70, 0, 129, 1]), s0_std=0.02,
+                              seed=92)
+        do, do_bits, dsf = cotangents(inp, 93)
+        t = dev_inputs(inp)
+        if do_bits is not None:
+            dod = torch.from_numpy(np.ascontiguousarray(do_bits).view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            dod = torch.from_numpy(np.ascontiguousarray(do)).cuda()
+        dsfd = torch.from_numpy(dsf).cuda()
+        B, T, H, K = inp.q.shape
+        V = inp.v.shape[3]
+        nseq = inp.num_seqs if inp.cu_seqlens is not None else 0
+        nws = int(comba.lib().comba_chunk_bwd_workspace_size(B, T, H, K, V, nseq))
+        out = []
+        for fill in (0x00, 0xFF):
+            ws = torch.full((nws,), fill, dtype=torch.uint8, device="cuda")
+            g = comba.chunk_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], t["d"], dod, t["initial_state"],
+                                t["cu_seqlens"], dsfd, workspace=ws)
+            torch.cuda.synchronize()
+            out.append({key: x.clone() for key, x in g.items()})
+        for key in out[0]:
+            assert torch.equal(out[0][key], out[1][key]), (case, key)
+        got = {key: to_np(x) for key, x in out[1].items()}
+        got["ds0"] = got.pop("dinitial_state")
+        check(got, oracle_bwd(inp, do, dsf), inp)
