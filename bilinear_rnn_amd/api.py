@@ -28,6 +28,14 @@ COMBA_BF16 = 0
 COMBA_FP32 = 1
 COMBA_FUSE_GATE_LOGITS = 1
 COMBA_FUSE_QK_L2NORM = 2
+COMBA_CHECK_ALPHA_RANGE = 1
+COMBA_CHECK_CU_ORDER = 2
+COMBA_CHECK_CU_BOUNDS = 4
+
+# COMBA_DEBUG_CHECKS=1: every forward, decode and backward call first checks the
+# device-side preconditions (comba_check_inputs), waits for the result and
+# raises CombaError when one fails. Off by default: it synchronises the stream.
+DEBUG_CHECKS = os.environ.get("COMBA_DEBUG_CHECKS", "") not in ("", "0")
 
 EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_chunk_fwd_workspace_size", "comba_chunk_fwd", "comba_chunk_fwd_fused", "comba_chunk_fwd_ex",
@@ -36,7 +44,7 @@ EXPORTED = ("comba_abi_version", "comba_status_string", "comba_last_error",
             "comba_chunk_fwd_segmented", "comba_chunk_bwd_workspace_size", "comba_chunk_bwd",
             "comba_varlen_order", "comba_mfma_peak_probe", "comba_chunk_states_size", "comba_chunk_fwd_keep_states",
             "comba_chunk_bwd_cached_workspace_size", "comba_chunk_bwd_cached", "comba_chunk_fwd_noalloc",
-            "comba_lds_probe")
+            "comba_lds_probe", "comba_check_inputs")
 
 
 class CombaError(RuntimeError):
@@ -113,6 +121,8 @@ def lib() -> ctypes.CDLL:
         L.comba_mfma_peak_probe.restype = i32
         L.comba_lds_probe.argtypes = [i32, ip, i32, vp, i32, vp]
         L.comba_lds_probe.restype = i32
+        L.comba_check_inputs.argtypes = [fp, ctypes.c_int64, ip, i32, i32, vp, vp]
+        L.comba_check_inputs.restype = i32
         _lib = L
     return _lib
 
@@ -214,6 +224,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     routes it through ``comba_chunk_fwd_keep_states``, which also keeps every
     chunk's incoming state there for ``chunk_bwd``."""
     B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    if DEBUG_CHECKS:
+        _debug_check(alpha, cu_seqlens, T, check_alpha=not gate_logits)
     L = lib()
     if out is None:
         out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
@@ -275,6 +287,8 @@ def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: 
     B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
     if Hk != H:
         raise ValueError("chunk_fwd_noalloc takes one q / k head per value head")
+    if DEBUG_CHECKS:
+        _debug_check(alpha, cu_seqlens, T)
     L = lib()
     if out is None:
         out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
@@ -305,6 +319,8 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: tor
     ``gate_logits`` and ``qk_l2norm`` as in ``chunk_fwd`` (through
     ``comba_recurrent_step_fused``)."""
     B, T, H, Hk, K, V, N, out_dtype = _prepare(q, k, v, alpha, beta, d, initial_state, cu_seqlens, out_dtype)
+    if DEBUG_CHECKS:
+        _debug_check(alpha, cu_seqlens, T, check_alpha=not gate_logits)
     L = lib()
     if out is None:
         out = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
@@ -348,6 +364,8 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Te
     if Hk != H:
         raise ValueError("the backward takes one q / k head per value head")
     _require(do, "do", q.dtype, (B, T, H, V))
+    if DEBUG_CHECKS:
+        _debug_check(alpha, cu_seqlens, T)
     if d_final_state is not None:
         _require(d_final_state, "d_final_state", torch.float32, (N, H, V, K))
     L = lib()
@@ -406,6 +424,39 @@ def varlen_order(cu_seqlens: torch.Tensor) -> torch.Tensor:
         stream = torch.cuda.current_stream(cu_seqlens.device).cuda_stream
         _check(lib().comba_varlen_order(_ptr(cu_seqlens), N, _ptr(order), ctypes.c_void_p(stream)))
     return order
+
+
+_CHECK_NAMES = ((COMBA_CHECK_ALPHA_RANGE, "an alpha outside (0, 1] or NaN"),
+                (COMBA_CHECK_CU_ORDER, "cu_seqlens decreases"),
+                (COMBA_CHECK_CU_BOUNDS, "cu_seqlens does not start at 0 and end at T"))
+
+
+def check_inputs(alpha: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None, T: Optional[int] = None,
+                 check_alpha: bool = True) -> int:
+    """Device-side preconditions through ``comba_check_inputs``: returns the OR of
+    the COMBA_CHECK_* bits of the violated ones (0: all hold). Waits for the
+    stream. ``T`` is the packed length cu_seqlens must end at (default: the
+    token axis of alpha)."""
+    _require(alpha, "alpha", torch.float32)
+    N = 0
+    if cu_seqlens is not None:
+        _require(cu_seqlens, "cu_seqlens", torch.int32)
+        N = cu_seqlens.numel() - 1
+        if T is None:
+            T = alpha.shape[1] if alpha.dim() >= 2 else alpha.numel()
+    flags = torch.empty((1,), dtype=torch.int32, device=alpha.device)
+    with torch.cuda.device(alpha.device):
+        stream = torch.cuda.current_stream(alpha.device).cuda_stream
+        _check(lib().comba_check_inputs(_ptr(alpha), alpha.numel() if check_alpha else 0, _ptr(cu_seqlens), N,
+                                        0 if T is None else int(T), _ptr(flags), ctypes.c_void_p(stream)))
+    return int(flags.item())
+
+
+def _debug_check(alpha: torch.Tensor, cu_seqlens: Optional[torch.Tensor], T: int, check_alpha: bool = True):
+    bad = check_inputs(alpha, cu_seqlens, T, check_alpha)
+    if bad:
+        raise CombaError(COMBA_ERR_INVALID_ARG, "device-side preconditions violated: " +
+                         "; ".join(name for bit, name in _CHECK_NAMES if bad & bit))
 
 
 PEAK_PROBE_FLOPS_PER_BLOCK_ITER = 4 * 4 * 16384   # wavefronts x MFMAs per iteration x flops per MFMA

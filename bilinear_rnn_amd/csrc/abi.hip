@@ -558,6 +558,16 @@ COMBA_API int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs
   return launched(comba::launch_varlen_order(cu_seqlens, num_seqs, order, static_cast<hipStream_t>(stream)));
 }
 
+COMBA_API int32_t comba_check_inputs(const float* alpha, int64_t n_alpha, const int32_t* cu_seqlens,
+                                     int32_t num_seqs, int32_t T, uint32_t* flags, void* stream) {
+  if (!alpha || !flags) return fail(COMBA_ERR_INVALID_ARG, "alpha and flags must be non-NULL");
+  if (n_alpha < 0) return fail(COMBA_ERR_INVALID_ARG, "n_alpha must be >= 0");
+  if (cu_seqlens && (num_seqs < 1 || T < 0))
+    return fail(COMBA_ERR_INVALID_ARG, "with cu_seqlens, num_seqs must be >= 1 and T >= 0");
+  return launched(comba::launch_check_inputs(alpha, n_alpha, cu_seqlens, cu_seqlens ? num_seqs : 0, T, flags,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 COMBA_API int32_t comba_mfma_peak_probe(float* sink, int32_t blocks, int32_t iters, void* stream) {
   if (!sink) return fail(COMBA_ERR_INVALID_ARG, "sink must be non-NULL");
   if (blocks < 1 || iters < 1) return fail(COMBA_ERR_INVALID_ARG, "blocks and iters must be >= 1");

@@ -77,6 +77,8 @@ hipError_t launch_chunk_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_chunk_bf16_pair(const FwdArgs& a, float* sf2, hipStream_t st);
 hipError_t launch_chunk_fp32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_varlen_order(const int32_t* cu_seqlens, int N, int32_t* order, hipStream_t st);
+hipError_t launch_check_inputs(const float* alpha, int64_t n_alpha, const int32_t* cu_seqlens, int N, int T,
+                               uint32_t* flags, hipStream_t st);
 hipError_t launch_segment_bounds(int B, int T, int L, int S, int32_t* cu, hipStream_t st);
 hipError_t launch_segment_scan(const float* s0, const float* bst, const float* phi, float* X, float* sf, int B,
                                int H, int K, int V, int S, hipStream_t st);

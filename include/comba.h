@@ -372,6 +372,33 @@ int32_t comba_varlen_order(const int32_t* cu_seqlens, int32_t num_seqs, int32_t*
                            void* stream);
 
 /*
+ * Device-side preconditions, checked on demand (a debug aid: no other entry
+ * point runs it). Comba's gate alpha is the scalar part of the
+ * scalar-plus-low-rank transition (the recurrence at the top of this header;
+ * write-up, section "Comba架构：基于闭环控制理论") and the chunk form takes its
+ * logarithm (write-up, section "硬件高效的分块并行计算"), so every alpha must
+ * lie in (0, 1]; a packed
+ * batch's cu_seqlens must start at 0, end at T and never decrease (the
+ * layout rules at the top of this header). The call enqueues two small
+ * kernels on `stream`: the first stores 0 to *flags, the second ORs in
+ *   COMBA_CHECK_ALPHA_RANGE  an alpha outside (0, 1], or NaN;
+ *   COMBA_CHECK_CU_ORDER     cu_seqlens[n+1] < cu_seqlens[n] for some n;
+ *   COMBA_CHECK_CU_BOUNDS    cu_seqlens[0] != 0 or cu_seqlens[N] != T.
+ * *flags is 0 when every precondition holds; read it after the stream has
+ * run. Do not pass the gate logits of the fused entry points as alpha.
+ * alpha: device float32, n_alpha entries (B * T * H); cu_seqlens: device int32
+ * [num_seqs + 1], or NULL (then num_seqs and T are not read); flags: device,
+ * one uint32, owned by the caller. Calls that share a flags word race.
+ * Errors: COMBA_ERR_INVALID_ARG for NULL alpha or flags, n_alpha < 0, or
+ * with cu_seqlens num_seqs < 1 or T < 0.
+ */
+#define COMBA_CHECK_ALPHA_RANGE 1u
+#define COMBA_CHECK_CU_ORDER 2u
+#define COMBA_CHECK_CU_BOUNDS 4u
+int32_t comba_check_inputs(const float* alpha, int64_t n_alpha, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int32_t T, uint32_t* flags, void* stream);
+
+/*
  * Measurement aid, not part of the recurrence: the matrix-core ceiling of the
  * device it runs on, to set beside the published dense bf16 peak when the
  * chunk kernels are rated against it. Launches `blocks` workgroups of four

@@ -332,3 +332,23 @@ def test_lds_pattern_layouts_cover_each_tile_once():
             rows = sorted((lp.qk_row(K, p, j, spread), lp.qk_col(K, p, spread))
                           for p in range(256) for j in range(64 * kp // 256))
             assert rows == [(r, c) for r in range(64) for c in range(kp)]
+
+
+
+@pytest.mark.parametrize("alpha,n_alpha,cu,nseq,T,flags", [
+    (None, 16, None, 0, 0, FAKE),      # NULL alpha
+    (FAKE, 16, None, 0, 0, None),      # NULL flags
+    (FAKE, -1, None, 0, 0, FAKE),      # negative count
+    (FAKE, 16, FAKE, 0, 16, FAKE),     # cu_seqlens with no sequence
+    (FAKE, 16, FAKE, 2, -1, FAKE),     # cu_seqlens with T < 0
+])
+def test_check_inputs_rejects_bad_arguments(alpha, n_alpha, cu, nseq, T, flags):
+    assert comba.lib().comba_check_inputs(alpha, n_alpha, cu, nseq, T, flags, None) == api.COMBA_ERR_INVALID_ARG
+    assert api.last_error() != ""
+
+
+def test_check_flags_match_the_header():
+    text = open(os.path.join(ROOT, "include", "comba.h")).read()
+    for name in ("COMBA_CHECK_ALPHA_RANGE", "COMBA_CHECK_CU_ORDER", "COMBA_CHECK_CU_BOUNDS"):
+        m = re.search(rf"#define {name} (\d+)u", text)
+        assert m and int(m.group(1)) == getattr(api, name), name
