@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define COMBA_ABI_VERSION 5
+#define COMBA_ABI_VERSION 6
 
 /* Status codes returned by every entry point. */
 enum {

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_function():
 
 def test_version_and_status_strings():
     L = comba.lib()
-    assert L.comba_abi_version() == 5
+    assert L.comba_abi_version() == 6
     assert api.status_string(0) == "COMBA_OK"
     assert api.status_string(-1) == "COMBA_ERR_INVALID_ARG"
     assert api.status_string(-2) == "COMBA_ERR_UNSUPPORTED"
