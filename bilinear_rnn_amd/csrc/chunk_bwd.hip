@@ -29,8 +29,9 @@
 // Launches after a forward pass that stores every chunk's incoming state (the
 // chunk kernels' checkpoint option):
 //   chunk_bwd_prep_kernel  one workgroup per (chunk, head), all chunks at once:
-//                          Tinv, P, k_t.k_s and the decay gates of the chunk,
-//                          stored;
+//                          Tinv, P (their 16 x 16 blocks on or below the
+//                          diagonal), k_t.k_s (fp32 inputs) and the decay
+//                          gates of the chunk, stored;
 //   chunk_bwd_dh_kernel    reverse scan over chunks, one workgroup per
 //   (_bf16_kernel)         (sequence, head, 32 (fp32) or 64 (bf16) value
 //                          channels), next chunk prefetched into registers:
@@ -39,12 +40,14 @@
 //   chunk_bwd_grad_kernel  one workgroup per (chunk, head): every per-token
 //                          gradient and a partial of dd;
 //   dd_reduce_kernel       dd per head, summed over chunks in a fixed order.
-// The gradient kernel, and the scan for fp32 inputs, form their products on
-// the fp32 matrix cores (16 x 16 x 4 tiles, exact fp32 operands read from
+// For fp32 inputs the scan and the gradient kernel form their products on the
+// fp32 matrix cores (16 x 16 x 4 tiles, exact fp32 operands read from
 // row-major LDS buffers; a transposed operand only swaps the fragment's
-// indices). For bf16 inputs the scan runs on the bf16 matrix cores with every
-// fp32 operand split into hi + lo bf16, and the prep kernel forms its scores on
-// them; for fp32 inputs the prep kernel uses the vector units.
+// indices). For bf16 inputs both run on the bf16 matrix cores with every fp32
+// operand split into hi + lo bf16, and the prep kernel forms its scores on
+// them; for fp32 inputs the prep kernel's scores use the vector units. The
+// prep kernel's inverse takes its diagonal blocks by substitution on the
+// vector units and its off-diagonal blocks on the fp32 matrix cores.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
