@@ -204,7 +204,7 @@ BWD_SOURCES = ("chunk_bwd.hip", "chunk_fwd_bf16.hip", "chunk_common.h", "device_
                "launch.h")
 BWD_KERNELS = (("checkpointing forward", "chunk_fwd_bf16_kernel<128, 128, 64, unsigned short, false, true>"),
                ("prep", "chunk_bwd_prep_kernel<128, unsigned short>"),
-               ("reverse scan", "chunk_bwd_dh_bf16_kernel<128, 128>"),
+               ("reverse scan", "chunk_bwd_dh_pc_kernel<128, 128>"),
                ("gradient pass", "chunk_bwd_grad_bf16_kernel<128, 128>"),
                ("dd reduction", "dd_reduce_kernel"))
 

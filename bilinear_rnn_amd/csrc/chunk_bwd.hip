@@ -1113,37 +1113,40 @@ constexpr int kDhbVT = 64;  // value channels per workgroup of the bf16 reverse 
 // bf16: P and Tinv ([t'][t] as the prep kernel stores them), and the
 // right-hand operands dUbar, X = diag(e^G) dO, Z = -d X - diag(b1) dR and dh,
 // stored by channel with the reduction axis (tokens or keys) in perm32 order.
+// ---- reverse scan on bf16 matrix cores, producer / consumer form -------------------------
+
+// One chunk's shared operands of the reverse scan, double-buffered between
+// the producer and the consumer wavefronts: q and k rows ([token][key], keys
+// of each 32-block in perm32 order), Tinv and P split hi / lo ([t][s]), dO
+// ([token][channel]) and the three gate rows the consumers read, by token.
 template <int K>
-struct alignas(16) SmemDhB {
+struct alignas(16) DhChunkBuf {
   u16 Qc[64 * K], Kc[64 * K];
-  u16 Ph[64 * 64], Pl[64 * 64], Th[64 * 64], Tl[64 * 64];
+  u16 Th[64 * 64], Tl[64 * 64], Ph[64 * 64], Pl[64 * 64];
   u16 dO[64 * kDhbVT];
-  u16 dUh[kDhbVT * 64], dUl[kDhbVT * 64], Xh[kDhbVT * 64], Xl[kDhbVT * 64], Zh[kDhbVT * 64], Zl[kDhbVT * 64];
-  u16 dhh[kDhbVT * K], dhl[kDhbVT * K];
-  ChunkGates gt;
+  float b1[64], eg[64], en[64];  // beta e^Gx, e^G, e^(Gn - G): rows 3-5 of the stored gates
 };
 
-// Reverse scan of dh for bf16 inputs: the products of chunk_bwd_dh_kernel on
-// 16x16x32 bf16 matrix cores, every fp32 operand split into hi + lo bf16
-// (exact operands enter once), 64 value channels per workgroup. Wavefront w
-// owns the channel blocks cb = 2 (w / 4) + {0, 1}: the token block tb of their
-// dUbar and dR (tb = w % 4 for w < 4, 3 - w % 4 otherwise, so that the two
-// wavefronts of a SIMD hold triangle rows of complementary length) and the key
-// blocks NBW (w % 4) + c of their dh, kept in fp32 registers across the
-// chunks. Per chunk, three barriers after the staging one:
-//   dUbar = diag(e^(Gn - G)) K dh + P^T dO
+// Reverse scan of dh for bf16 inputs, 64 value channels per workgroup, in the
+// forward's two roles one chunk apart. Producers (wavefronts 4-7) stage chunk
+// c - 1 (q, k, Tinv, P, dO, gates; loads issued a chunk ahead) while the
+// consumers (wavefronts 0-3, 16 channels each) run chunk c; one barrier per
+// chunk hands a buffer over. A consumer keeps dh (keys x its 16 channels) in
+// fp32 registers for the whole sequence and needs no other wavefront's
+// results, so the chain of a chunk has no barrier inside:
+//   dUbar = diag(e^(Gn - G)) K dh + P^T dO   (K dh over its own channels)
 //   dR    = Tinv^T dUbar,  X = diag(e^G) dO,  Z = -d X - diag(b1) dR
-//   dh   <- e^Gn dh + q^T X + k^T Z          (q~^T X = q^T X - d k^T X)
+//   dh   <- e^Gn dh + q^T X + k^T Z
+// with every fp32 operand split into hi + lo bf16 as in the forward.
 template <int K, int V>
-__global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
+__global__ __launch_bounds__(512) void chunk_bwd_dh_pc_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const float* __restrict__ d, const u16* __restrict__ dO,
     const int32_t* __restrict__ cu_seqlens, int T, int H, int N, const float* __restrict__ Tg,
     const float* __restrict__ Pg, const float* __restrict__ Gg, const float* __restrict__ dsf,
     float* __restrict__ dhck, float* __restrict__ ds0) {
-  constexpr int NT = 512, VT = kDhbVT, NVT = V / VT, NBW = K / 64;  // dh key blocks per channel block
-  constexpr int MPT = 64 * 16 / NT;
-  static_assert(VT == 64 && 64 * VT / 8 == NT, "four 16-channel blocks, one 16-byte dO piece per thread");
-  __shared__ SmemDhB<K> sm;
+  constexpr int VT = kDhbVT, NVT = V / VT, NS = K / 32, KB = K / 16;
+  static_assert(VT == 64, "four consumer wavefronts of 16 channels");
+  __shared__ DhChunkBuf<K> buf[2];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int unit, vt;
@@ -1151,172 +1154,144 @@ __global__ __launch_bounds__(512) void chunk_bwd_dh_bf16_kernel(
   const int h = unit % H, n = unit / H;
   int b, t0, t1;
   sequence_range(cu_seqlens, n, T, b, t0, t1);
-  const float dd_ = d[h];
   const int nch = (t1 - t0 + 63) / 64;
   const bool packed = cu_seqlens != nullptr;
-  const int cb0 = 2 * (wave >> 2), tb = wave < 4 ? (wave & 3) : 3 - (wave & 3);
-  const int64_t crow0 = (static_cast<int64_t>(n) * H + h) * V + vt * VT + l16;  // state row of channel l16
 
-  // dh blocks (keys 16 kb + 4 g + i, channel 16 cb + l16), fp32, from dL/dS_final
-  f32x4 dhr[2][NBW];
+  if (wave >= 4) {
+    // ======================= producers: stage chunk nch - 1 - it in iteration it =======================
+    const int ptid = tid - 256;
+    constexpr int MPT = 64 * 16 / 256;  // 16-byte pieces of a 64 x 64 fp32 matrix per thread
+    RowPieces<K, 256, u16> rqk;
+    f32x4 rt[MPT], rp[MPT], rg{};
+    u32x4 ro[2];
+    const int orow = ptid / (VT / 8), ocol = 8 * (ptid % (VT / 8));  // dO pieces: rows orow, orow + 32
+    auto fetch = [&](int ci) {
+      const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
+      const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
+      const int64_t sl = chunk_slot(packed, t0, n, ci, T) * H + h;
+      rqk.load(q, k, tok0, H, nrows, ptid);
+      const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j) ro[j] = load16(orsrc, ((orow + 32 * j) * H * V + vt * VT + ocol) * 2);
 #pragma unroll
-    for (int c = 0; c < NBW; ++c) {
-      const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
-      dhr[j][c] = dsf ? ld4(dsf + (crow0 + 16 * (cb0 + j)) * K + key4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < MPT; ++j) {
+        const int e = ptid + j * 256, row = e >> 4, c4 = 4 * (e & 15);
+        rt[j] = ld4_lower(Tg + sl * 64 * 64, row, c4);
+        rp[j] = ld4_lower(Pg + sl * 64 * 64, row, c4);
+      }
+      if (ptid < 48) rg = ld4(Gg + sl * kGateWords + 3 * 64 + 4 * ptid);
+    };
+    if (nch > 0) fetch(nch - 1);
+    for (int it = 0; it <= nch; ++it) {
+      if (it < nch) {
+        DhChunkBuf<K>& bf = buf[it & 1];
+        rqk.store_bf16(bf.Qc, bf.Kc, ptid);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&bf.dO[swz<VT>(orow + 32 * j, ocol)]) = ro[j];
+#pragma unroll
+        for (int j = 0; j < MPT; ++j) {
+          const int e = ptid + j * 256, row = e >> 4, c4 = 4 * (e & 15);
+          put_split4(bf.Th, bf.Tl, swz<64>(row, c4), rt[j]);
+          put_split4(bf.Ph, bf.Pl, swz<64>(row, c4), rp[j]);
+        }
+        if (ptid < 48) {
+          const int r = ptid >> 4;
+          st4((r == 0 ? bf.b1 : r == 1 ? bf.eg : bf.en) + 4 * (ptid & 15), rg);
+        }
+        if (it + 1 < nch) fetch(nch - 2 - it);  // in flight during the next chunk's staging wait
+      }
+      __syncthreads();
     }
-
-  // next chunk's operands, one chunk ahead in registers, fetched in three
-  // parts over the chunk's three compute stages: issued together, the 16-byte
-  // loads of all eight wavefronts queue in the CU's memory unit and stall the
-  // wavefronts behind them for about 1,500 cycles (the state-gradient stores,
-  // moved out of the staging stage, do the same)
-  RowPieces<K, NT, u16> rqk;
-  u32x4 ro;
-  f32x4 rg{};
-  f32x4 rt[MPT], rp[MPT];
-  const int orow = tid / (VT / 8), ocol = 8 * (tid % (VT / 8));
-  auto fetch_qk = [&](int ci) {
-    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    rqk.load(q, k, (static_cast<int64_t>(b) * T + c0) * H + h, H, nrows, tid);
-  };
-  auto fetch_tp = [&](int ci) {
-    const int64_t sl = chunk_slot(packed, t0, n, ci, T) * H + h;
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) {
-      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-      rt[j] = ld4_lower(Tg + sl * 64 * 64, row, c4);
-      rp[j] = ld4_lower(Pg + sl * 64 * 64, row, c4);
-    }
-  };
-  auto fetch_og = [&](int ci) {
-    const int c0 = t0 + 64 * ci, nrows = min(64, t1 - c0);
-    const int64_t tok0 = (static_cast<int64_t>(b) * T + c0) * H + h;
-    const __amdgpu_buffer_rsrc_t orsrc = rows_rsrc(dO + tok0 * V, static_cast<int64_t>(nrows) * H * V * 2);
-    ro = load16(orsrc, (orow * H * V + vt * VT + ocol) * 2);
-    if (tid < kGateWords / 4) rg = ld4(Gg + (chunk_slot(packed, t0, n, ci, T) * H + h) * kGateWords + 4 * tid);
-  };
-
-  if (nch > 0) {
-    fetch_qk(nch - 1);
-    fetch_tp(nch - 1);
-    fetch_og(nch - 1);
+    return;
   }
-  for (int ci = nch - 1; ci >= 0; --ci) {
-    const int64_t slot = chunk_slot(packed, t0, n, ci, T);
-    __syncthreads();
-    rqk.store_bf16(sm.Qc, sm.Kc, tid);
-    *reinterpret_cast<u32x4*>(&sm.dO[swz<VT>(orow, ocol)]) = ro;
-#pragma unroll
-    for (int j = 0; j < MPT; ++j) {
-      const int e = tid + j * NT, row = e >> 4, c4 = 4 * (e & 15);
-      put_split4(sm.Th, sm.Tl, swz<64>(row, c4), rt[j]);
-      put_split4(sm.Ph, sm.Pl, swz<64>(row, c4), rp[j]);
-    }
-    if (tid < kGateWords / 4) st4(&sm.gt.G[0] + 4 * tid, rg);
-    // this chunk's outgoing-state gradient: hi / lo for the products, fp32 for
-    // the gradient kernel ([channel][key])
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int ch = 16 * (cb0 + j) + l16;
-      float* dst = dhck + ((slot * H + h) * V + vt * VT + ch) * K;
-#pragma unroll
-      for (int c = 0; c < NBW; ++c) {
-        const int key4 = 16 * (NBW * (wave & 3) + c) + 4 * g;
-        put_split4(sm.dhh, sm.dhl, swz<K>(ch, perm_col(key4)), dhr[j][c]);
-        st4(dst + key4, dhr[j][c]);
-      }
-    }
-    __syncthreads();
-    if (ci > 0) fetch_qk(ci - 1);  // in flight during this chunk's work
 
-    // dUbar of the blocks (tb, cb): diag(e^(Gn - G)) K dh, then + P^T dO
-    {
-      f32x4 kd[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // ======================= consumers: chunk nch - it in iteration it =======================
+  const int cw = wave;
+  const int cpos = 16 * cw + 4 * (l16 & 3);  // dO tile position of this lane's channel quad
+  const int64_t crow = (static_cast<int64_t>(n) * H + h) * V + vt * VT + 16 * cw + l16;  // state row
+  const float dd_ = d[h];
+  f32x4 dh[KB];  // dh[key 16 kb + 4 g + i][channel]
 #pragma unroll
-      for (int s_ = 0; s_ < K / 32; ++s_) {
-        const bf16x8 a = lds8(&sm.Kc[swz<K>(16 * tb + l16, 32 * s_ + 8 * g)]);
+  for (int kb = 0; kb < KB; ++kb)
+    dh[kb] = dsf ? ld4(dsf + crow * K + 16 * kb + 4 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it <= nch; ++it) {
+    if (it > 0) {
+      const int ci = nch - it;
+      const DhChunkBuf<K>& bf = buf[(it - 1) & 1];
+      // this chunk's outgoing-state gradient, fp32 [channel][key], for the gradient pass
+      float* dst = dhck + ((chunk_slot(packed, t0, n, ci, T) * H + h) * V + vt * VT + 16 * cw + l16) * K;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int off = swz<K>(16 * (cb0 + j) + l16, 32 * s_ + 8 * g);
-          kd[j] = mfma16x16x32(a, lds8(&sm.dhh[off]), kd[j]);
-          kd[j] = mfma16x16x32(a, lds8(&sm.dhl[off]), kd[j]);
+      for (int kb = 0; kb < KB; ++kb) st4(dst + 16 * kb + 4 * g, dh[kb]);
+      bf16x8 hb[NS], lb[NS];
+#pragma unroll
+      for (int s_ = 0; s_ < NS; ++s_) split_pair(dh[2 * s_], dh[2 * s_ + 1], hb[s_], lb[s_]);
+      // dUbar = diag(e^(Gn - G)) K dh + P^T dO (P[t'][t] = 0 for t' < t)
+      f32x4 du[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        f32x4 kd{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s_ = 0; s_ < NS; ++s_) {
+          const bf16x8 a = lds8(&bf.Kc[swz<K>(16 * r + l16, 32 * s_ + 8 * g)]);
+          kd = mfma16x16x32(a, hb[s_], kd);
+          kd = mfma16x16x32(a, lb[s_], kd);
+        }
+        du[r] = ld4(&bf.en[16 * r + 4 * g]) * kd;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (s2 == 0 && r >= 2) continue;
+          const bf16x8 o = tr_frag<VT>(bf.dO, 32 * s2, cpos, g, l16);
+          const int pos = 16 * r + 4 * (l16 & 3);
+          du[r] = mfma16x16x32(tr_frag<64>(bf.Ph, 32 * s2, pos, g, l16), o, du[r]);
+          du[r] = mfma16x16x32(tr_frag<64>(bf.Pl, 32 * s2, pos, g, l16), o, du[r]);
         }
       }
-      const f32x4 en = ld4(&sm.gt.EGnG[16 * tb + 4 * g]);
-      const int pos = 16 * tb + 4 * (l16 & 3);
+      // dR = Tinv^T dUbar (Tinv[t'][t] = 0 for t' < t); X = diag(e^G) dO; Z = -d X - diag(b1) dR
+      bf16x8 uh[2], ul[2];
+      split_pair(du[0], du[1], uh[0], ul[0]);
+      split_pair(du[2], du[3], uh[1], ul[1]);
+      f32x4 X[4], Z[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f32x4 du = en * kd[j];
-#pragma unroll
-        for (int s_ = 0; s_ < 2; ++s_) {
-          if (s_ == 0 && tb >= 2) continue;  // P[t'][t] = 0 for t' < t
-          const bf16x8 o = tr_frag<VT>(sm.dO, 32 * s_, 16 * (cb0 + j) + 4 * (l16 & 3), g, l16);
-          du = mfma16x16x32(tr_frag<64>(sm.Ph, 32 * s_, pos, g, l16), o, du);
-          du = mfma16x16x32(tr_frag<64>(sm.Pl, 32 * s_, pos, g, l16), o, du);
-        }
-        put_split4(sm.dUh, sm.dUl, swz<64>(16 * (cb0 + j) + l16, perm_col(16 * tb + 4 * g)), du);
-      }
-    }
-    __syncthreads();
-    if (ci > 0) fetch_tp(ci - 1);
-
-    // dR = Tinv^T dUbar, then X and Z of the blocks (tb, cb)
-    {
-      const int pos = 16 * tb + 4 * (l16 & 3);
-      const f32x4 eg = ld4(&sm.gt.EG[16 * tb + 4 * g]), b1 = ld4(&sm.gt.bEGx[16 * tb + 4 * g]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ch = 16 * (cb0 + j) + l16;
+      for (int r = 0; r < 4; ++r) {
         f32x4 dr{0.f, 0.f, 0.f, 0.f};
+        const int pos = 16 * r + 4 * (l16 & 3);
 #pragma unroll
-        for (int s_ = 0; s_ < 2; ++s_) {
-          if (s_ == 0 && tb >= 2) continue;  // Tinv[t'][t] = 0 for t' < t
-          const int bo = swz<64>(ch, 32 * s_ + 8 * g);
-          dr = mma3(tr_frag<64>(sm.Th, 32 * s_, pos, g, l16), tr_frag<64>(sm.Tl, 32 * s_, pos, g, l16),
-                    lds8(&sm.dUh[bo]), lds8(&sm.dUl[bo]), dr);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          if (s2 == 0 && r >= 2) continue;
+          dr = mma3(tr_frag<64>(bf.Th, 32 * s2, pos, g, l16), tr_frag<64>(bf.Tl, 32 * s2, pos, g, l16), uh[s2], ul[s2],
+                    dr);
         }
-        const f32x4 x = eg * tr4<VT>(sm.dO, 16 * tb, 16 * (cb0 + j) + 4 * (l16 & 3), g, l16);
-        const f32x4 z = -dd_ * x - b1 * dr;
-        const int off = swz<64>(ch, perm_col(16 * tb + 4 * g));
-        put_split4(sm.Xh, sm.Xl, off, x);
-        put_split4(sm.Zh, sm.Zl, off, z);
+        X[r] = ld4(&bf.eg[16 * r + 4 * g]) * tr4<VT>(bf.dO, 16 * r, cpos, g, l16);
+        Z[r] = -dd_ * X[r] - ld4(&bf.b1[16 * r + 4 * g]) * dr;
+      }
+      bf16x8 xh[2], xl[2], zh[2], zl[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        split_pair(X[2 * s2], X[2 * s2 + 1], xh[s2], xl[s2]);
+        split_pair(Z[2 * s2], Z[2 * s2 + 1], zh[s2], zl[s2]);
+      }
+      // dh <- e^Gn dh + q^T X + k^T Z
+      const float eGn = bf.eg[63];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x4 acc = eGn * dh[kb];
+        const int pos = perm_col(16 * kb + 4 * (l16 & 3));
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const bf16x8 aq = tr_frag<K>(bf.Qc, 32 * s2, pos, g, l16), ak = tr_frag<K>(bf.Kc, 32 * s2, pos, g, l16);
+          acc = mfma16x16x32(aq, xh[s2], acc);
+          acc = mfma16x16x32(aq, xl[s2], acc);
+          acc = mfma16x16x32(ak, zh[s2], acc);
+          acc = mfma16x16x32(ak, zl[s2], acc);
+        }
+        dh[kb] = acc;
       }
     }
     __syncthreads();
-    if (ci > 0) fetch_og(ci - 1);
-
-    // dh <- e^Gn dh + q^T X + k^T Z for the wavefront's blocks
-    const float eGn = sm.gt.EG[63];
-#pragma unroll
-    for (int c = 0; c < NBW; ++c) {
-      const int kb = NBW * (wave & 3) + c;
-      f32x4 acc[2] = {eGn * dhr[0][c], eGn * dhr[1][c]};
-#pragma unroll
-      for (int s_ = 0; s_ < 2; ++s_) {
-        const int pos = perm_col(16 * kb + 4 * (l16 & 3));
-        const bf16x8 aq = tr_frag<K>(sm.Qc, 32 * s_, pos, g, l16);
-        const bf16x8 ak = tr_frag<K>(sm.Kc, 32 * s_, pos, g, l16);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int off = swz<64>(16 * (cb0 + j) + l16, 32 * s_ + 8 * g);
-          acc[j] = mfma16x16x32(aq, lds8(&sm.Xh[off]), acc[j]);
-          acc[j] = mfma16x16x32(aq, lds8(&sm.Xl[off]), acc[j]);
-          acc[j] = mfma16x16x32(ak, lds8(&sm.Zh[off]), acc[j]);
-          acc[j] = mfma16x16x32(ak, lds8(&sm.Zl[off]), acc[j]);
-        }
-      }
-      dhr[0][c] = acc[0];
-      dhr[1][c] = acc[1];
-    }
   }
   if (ds0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int c = 0; c < NBW; ++c)
-        st4(ds0 + (crow0 + 16 * (cb0 + j)) * K + 16 * (NBW * (wave & 3) + c) + 4 * g, dhr[j][c]);
+    for (int kb = 0; kb < KB; ++kb) st4(ds0 + crow * K + 16 * kb + 4 * g, dh[kb]);
   }
 }
 
@@ -1778,7 +1753,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (sizeof(InT) == 2) {
-    chunk_bwd_dh_bf16_kernel<K, V><<<xcd_grid(a.N * a.H, V / kDhbVT), 512, 0, st>>>(
+    chunk_bwd_dh_pc_kernel<K, V><<<xcd_grid(a.N * a.H, V / kDhbVT), 512, 0, st>>>(
         static_cast<const u16*>(a.q), static_cast<const u16*>(a.k), a.d, static_cast<const u16*>(a.dO),
         a.cu_seqlens, a.T, a.H, a.N, a.Tg, a.Pg, a.Gg, a.dsf, a.dhck, a.ds0);
   } else {
