@@ -59,7 +59,7 @@ def expanded(inp):
     return out
 
 
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (64, 128)])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (64, 128), (128, 64)])
 @pytest.mark.parametrize("Hk", [1, 2])
 @pytest.mark.parametrize("T", [300, 64])
 def test_bf16_shared_qk_chunk(K, V, Hk, T):
